@@ -1,0 +1,155 @@
+"""Plain float64 definitions of what the fused attention path computes.
+
+TEST INFRASTRUCTURE: imported only by the tests, the smoke entry point and the
+benchmark's CPU-baseline leg; never by the product path.
+
+Sources (pages and their sections):
+  * "fmha sm120: beyond torch.sdpa" (WingEdge777), section 1 "flash attention":
+    multi-head attention is s = q.k^T * scale, p = softmax(s), o = p.v, with
+    q, k, v laid out [batch, seq, heads, head_dim]; section 2 "fmha
+    implementation": grouped-query heads use kv_head = q_head // (Hq / Hkv),
+    and the causal mask keeps key j for query i when i >= j (top-left).
+  * "CUDA Flash Decoding" (yunpan.plus), section 2.2 "chunk partial + global
+    LSE weighted reduce": per chunk c, S_c = q.K_c^T, m_c = max S_c,
+    P_c = exp(S_c - m_c), l_c = sum P_c, O_c = P_c.V_c / l_c,
+    lse_c = m_c + log l_c; then global_lse = log sum_c exp(lse_c),
+    w_c = exp(lse_c - global_lse), O = sum_c w_c O_c.
+  * "Tensor Core migration plan" (CuFlash-Attn design doc), cross-cutting
+    notes: the log-sum-exp row statistic is kept as fp32 output.
+
+Readings where the pages leave a step open (each is also listed in the design
+notes of the repository):
+  * lse is the natural logarithm of the row's softmax denominator including
+    the max: lse_i = m_i + ln(l_i) = ln sum_j exp(S_ij).
+  * The causal mask is top-left aligned and only defined here for N == M.
+  * A row with no allowed key has O = 0 and lse = -inf (unreachable with a
+    top-left causal mask and N == M, since key 0 is always allowed).
+  * Inputs are the already-rounded fp16/bf16 values upcast exactly to
+    float64; ``scale`` is the fp32 value handed to the GPU, upcast.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref"]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a torch tensor or numpy array to float64."""
+    if hasattr(x, "detach"):  # torch tensor (fp16/bf16/fp32 upcast is exact)
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _softmax_rows(S: np.ndarray):
+    """Row softmax of a score matrix whose disallowed entries are -inf.
+
+    Returns (P, lse) with P normalised along the last axis and
+    lse = m + ln(sum exp(S - m)), the natural-log row log-sum-exp.
+    Rows with no finite entry give P = 0 and lse = -inf.
+    """
+    m = np.max(S, axis=-1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    E = np.exp(S - m_safe)                 # exp(-inf) = 0 for masked keys
+    l = np.sum(E, axis=-1, keepdims=True)
+    P = np.where(empty, 0.0, E / np.where(empty, 1.0, l))
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return P, lse[..., 0]
+
+
+def attn_ref(q, k, v, scale: float, causal: bool = False, rows=None):
+    """Attention forward, materialising S and P per (batch, query head).
+
+    q [B, N, Hq, d]; k [B, M, Hkv, d]; v [B, M, Hkv, dv] (the "fmha sm120"
+    page's layout; the pages use dv = d).
+    Returns O [B, n, Hq, dv] and lse [B, Hq, n] in float64, where n = N, or
+    n = len(rows) when ``rows`` selects a subset of query positions (the
+    causal mask still uses each row's absolute position).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, Hq, d = q.shape
+    Bk, M, Hkv, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape[:3] != k.shape[:3]:
+        raise ValueError("shape mismatch between q, k, v")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if causal and N != M:
+        raise ValueError("causal attention is defined here only for N == M")
+    group = Hq // Hkv
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+
+    O = np.zeros((B, n, Hq, v.shape[3]))
+    lse = np.zeros((B, Hq, n))
+    keys = np.arange(M)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // group                       # contiguous query-head groups
+            Qbh = q[b, rows, h, :]                # [n, d]
+            Kbh = k[b, :, kh, :]                  # [M, d]
+            Vbh = v[b, :, kh, :]                  # [M, dv]
+            S = float(scale) * (Qbh @ Kbh.T)      # [n, M]
+            if causal:
+                S = np.where(keys[None, :] > rows[:, None], -np.inf, S)
+            P, lse_bh = _softmax_rows(S)
+            O[b, :, h, :] = P @ Vbh
+            lse[b, h, :] = lse_bh
+    return O, lse
+
+
+def decode_partials_ref(q, k, v, scale: float, chunk: int):
+    """Per-chunk partials of single-query attention (Flash Decoding step 1).
+
+    q [B, Hq, d]; k, v [B, Hkv, M, d] (the decode page's per-head KV layout).
+    Chunk c covers keys [c*chunk, min((c+1)*chunk, M)); the last chunk may be
+    shorter.  Returns o_part [B, Hq, C, d] (each chunk's *normalised* output)
+    and lse_part [B, Hq, C] (m_c + ln l_c), C = ceil(M / chunk).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, d = q.shape
+    Bk, Hkv, M, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k, v")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    C = -(-M // chunk)
+    o_part = np.zeros((B, Hq, C, d))
+    lse_part = np.zeros((B, Hq, C))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // group
+            for c in range(C):
+                lo, hi = c * chunk, min((c + 1) * chunk, M)
+                s = float(scale) * (k[b, kh, lo:hi, :] @ q[b, h, :])   # S_c [len]
+                m_c = np.max(s)
+                p = np.exp(s - m_c)                                   # P_c
+                l_c = np.sum(p)                                       # l_c
+                o_part[b, h, c, :] = (p @ v[b, kh, lo:hi, :]) / l_c   # O_c
+                lse_part[b, h, c] = m_c + np.log(l_c)                 # lse_c
+    return o_part, lse_part
+
+
+def lse_merge_ref(o_part, lse_part):
+    """Log-sum-exp weighted merge of chunk partials (Flash Decoding step 2).
+
+    o_part [..., C, d], lse_part [..., C] -> O [..., d], lse [...]:
+    g = max_c lse_c + ln sum_c exp(lse_c - max_c lse_c),
+    w_c = exp(lse_c - g), O = sum_c w_c O_c, lse = g.
+    """
+    o_part, lse_part = _f64(o_part), _f64(lse_part)
+    mx = np.max(lse_part, axis=-1, keepdims=True)
+    g = mx + np.log(np.sum(np.exp(lse_part - mx), axis=-1, keepdims=True))
+    w = np.exp(lse_part - g)                                  # [..., C]
+    O = np.sum(w[..., None] * o_part, axis=-2)
+    return O, g[..., 0]
+
+
+def decode_ref(q, k, v, scale: float, chunk: int):
+    """Split-KV decode end to end: partials, then merge.  Returns
+    (O [B, Hq, d], lse [B, Hq], o_part, lse_part)."""
+    o_part, lse_part = decode_partials_ref(q, k, v, scale, chunk)
+    O, lse = lse_merge_ref(o_part, lse_part)
+    return O, lse, o_part, lse_part

@@ -1,0 +1,291 @@
+"""Checks that pin the CPU oracle to something other than itself.
+
+Every check takes the oracle as a parameter (a module exposing ``attn_ref``,
+``decode_partials_ref``, ``lse_merge_ref`` and ``decode_ref``) and raises
+AssertionError when the oracle disagrees with:
+  * a pure-Python brute force (``tests/brute.py``) on tiny inputs and on the
+    whole of the two small workloads;
+  * torch's float64 CPU ``scaled_dot_product_attention`` (a library routine
+    that computes the same definition; its ``is_causal`` mask is top-left);
+  * closed forms and invariants that the mathematics fixes.
+
+The same checks run against the real oracle (all must pass) and against
+copies of the oracle with a planted mistake (each must fail at least one),
+which shows that the pins can see a dropped term, a wrong sign or index, or a
+swapped operand.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from tests.brute import brute_attention, brute_decode, brute_decode_partials
+
+TOL = 1e-11
+
+
+def _rand(shape, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape) * scale
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------------------
+# Brute force
+# ---------------------------------------------------------------------------
+
+PREFILL_TINY = [
+    # B, N, M, Hq, Hkv, d, causal, scale
+    (1, 5, 5, 2, 1, 3, False, 0.7),
+    (1, 6, 6, 2, 2, 4, True, 0.5),
+    (2, 7, 7, 4, 2, 5, True, 0.3),
+    (2, 3, 9, 3, 1, 4, False, 1.1),
+    (1, 1, 1, 1, 1, 2, True, 0.9),
+]
+
+
+def check_brute_prefill_tiny(ora):
+    for i, (B, N, M, Hq, Hkv, d, causal, sc) in enumerate(PREFILL_TINY):
+        q = _rand((B, N, Hq, d), 10 + i)
+        k = _rand((B, M, Hkv, d), 20 + i)
+        v = _rand((B, M, Hkv, d), 30 + i)
+        O, lse = ora.attn_ref(q, k, v, sc, causal)
+        Ob, Lb = brute_attention(q, k, v, sc, causal)
+        _close(O, Ob, what=f"O case {i}")
+        _close(lse, Lb, what=f"lse case {i}")
+
+
+def check_brute_decode_tiny(ora):
+    # a tail chunk (M not a multiple of chunk), GQA, chunk larger than M
+    for i, (B, Hq, Hkv, M, d, chunk) in enumerate([(1, 2, 1, 10, 3, 4), (2, 4, 2, 7, 5, 3),
+                                                   (1, 1, 1, 5, 4, 8)]):
+        q = _rand((B, Hq, d), 40 + i)
+        k = _rand((B, Hkv, M, d), 50 + i)
+        v = _rand((B, Hkv, M, d), 60 + i)
+        op, lp = ora.decode_partials_ref(q, k, v, 0.6, chunk)
+        opb, lpb = brute_decode_partials(q, k, v, 0.6, chunk)
+        _close(op, opb, what=f"o_part case {i}")
+        _close(lp, lpb, what=f"lse_part case {i}")
+        O, L, _, _ = ora.decode_ref(q, k, v, 0.6, chunk)
+        Ob, Lb = brute_decode(q, k, v, 0.6)
+        _close(O, Ob, what=f"merged O case {i}")
+        _close(L, Lb, what=f"merged lse case {i}")
+
+
+def check_brute_workload(ora, w, seed=0):
+    """The whole of a small workload against brute force (a few seconds)."""
+    from workloads import make_inputs
+    q, k, v = make_inputs(w, seed)
+    if w.kind == "prefill":
+        O, lse = ora.attn_ref(q, k, v, w.scale, w.causal)
+        Ob, Lb = brute_attention(q, k, v, w.scale, w.causal)
+        _close(O, Ob, 1e-12, "O")
+        _close(lse, Lb, 1e-12, "lse")
+    else:
+        O, L, op, lp = ora.decode_ref(q, k, v, w.scale, w.chunk)
+        opb, lpb = brute_decode_partials(q, k, v, w.scale, w.chunk)
+        Ob, Lb = brute_decode(q, k, v, w.scale)
+        _close(op, opb, 1e-12, "o_part")
+        _close(lp, lpb, 1e-12, "lse_part")
+        _close(O, Ob, 1e-12, "O")
+        _close(L, Lb, 1e-12, "lse")
+
+
+# ---------------------------------------------------------------------------
+# Library special case: torch float64 SDPA on the CPU
+# ---------------------------------------------------------------------------
+
+def _sdpa(q, k, v, scale, causal):
+    """q [B,N,Hq,d], k/v [B,M,Hkv,d] float64 numpy -> O [B,N,Hq,d]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(np.ascontiguousarray(k)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 2, 1, 3)
+    g = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(g, dim=1)
+    vt = vt.repeat_interleave(g, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal,
+                                                         scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def check_sdpa(ora):
+    for i, (B, N, Hq, Hkv, d, causal) in enumerate([(2, 33, 4, 2, 16, True), (1, 40, 6, 3, 8, False),
+                                                    (1, 64, 8, 1, 32, True)]):
+        q = _rand((B, N, Hq, d), 70 + i)
+        k = _rand((B, N, Hkv, d), 80 + i)
+        v = _rand((B, N, Hkv, d), 90 + i)
+        O, _ = ora.attn_ref(q, k, v, 0.25, causal)
+        _close(O, _sdpa(q, k, v, 0.25, causal), 1e-12, f"sdpa case {i}")
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants
+# ---------------------------------------------------------------------------
+
+def check_identity_v_rows_are_probabilities(ora):
+    """With V = identity (d = M), O is the probability matrix: entries >= 0,
+    rows sum to 1, causal rows vanish above the diagonal, and each row equals
+    exp(S_ij - lse_i)."""
+    for causal in (False, True):
+        B, N, H, d = 1, 12, 2, 5
+        q = _rand((B, N, H, d), 100)
+        k = _rand((B, N, H, d), 101)
+        v = np.broadcast_to(np.eye(N)[None, :, None, :], (B, N, H, N)).copy()
+        P, lse = ora.attn_ref(q, k, v, 0.8, causal)
+        assert np.all(P >= 0)
+        _close(P.sum(-1), np.ones((B, N, H)), what="row sums")
+        if causal:
+            iu = np.triu_indices(N, 1)
+            assert np.all(P[0][iu[0], :, iu[1]] == 0), "causal probabilities above diagonal"
+        S = 0.8 * np.einsum("bihd,bjhd->bhij", q, k)
+        expected = np.exp(S - lse[..., None])
+        if causal:
+            expected = np.where(np.triu(np.ones((N, N), bool), 1), 0.0, expected)
+        _close(P.transpose(0, 2, 1, 3), expected, what="P = exp(S - lse)")
+
+
+def check_constant_v(ora):
+    B, N, Hq, Hkv, d = 2, 9, 4, 2, 6
+    q, k = _rand((B, N, Hq, d), 110), _rand((B, N, Hkv, d), 111)
+    u = _rand((d,), 112)
+    v = np.broadcast_to(u, (B, N, Hkv, d)).copy()
+    for causal in (False, True):
+        O, _ = ora.attn_ref(q, k, v, 0.5, causal)
+        _close(O, np.broadcast_to(u, O.shape), what="constant V")
+
+
+def check_single_key(ora):
+    B, Hq, d = 2, 3, 7
+    q, k, v = _rand((B, 1, Hq, d), 120), _rand((B, 1, Hq, d), 121), _rand((B, 1, Hq, d), 122)
+    for causal in (False, True):
+        O, lse = ora.attn_ref(q, k, v, 0.4, causal)
+        _close(O, v, what="M=1 output")
+        _close(lse[:, :, 0], 0.4 * np.sum(q[:, 0] * k[:, 0], -1), what="M=1 lse")
+
+
+def check_causal_row0(ora):
+    B, N, Hq, Hkv, d = 2, 11, 4, 2, 5
+    q, k, v = _rand((B, N, Hq, d), 130), _rand((B, N, Hkv, d), 131), _rand((B, N, Hkv, d), 132)
+    O, lse = ora.attn_ref(q, k, v, 0.6, True)
+    kv = np.repeat(np.arange(Hkv), Hq // Hkv)
+    _close(O[:, 0], v[:, 0][:, kv], what="causal row 0 output")
+    _close(lse[:, :, 0], 0.6 * np.sum(q[:, 0] * k[:, 0][:, kv], -1), what="causal row 0 lse")
+
+
+def check_zero_scale(ora):
+    """scale = 0: uniform weights over the allowed keys."""
+    B, N, Hq, d = 1, 8, 2, 3
+    q, k, v = _rand((B, N, Hq, d), 140), _rand((B, N, Hq, d), 141), _rand((B, N, Hq, d), 142)
+    O, lse = ora.attn_ref(q, k, v, 0.0, False)
+    _close(O, np.broadcast_to(v.mean(1, keepdims=True), O.shape), what="scale 0 output")
+    _close(lse, np.full(lse.shape, math.log(N)), what="scale 0 lse")
+    O, lse = ora.attn_ref(q, k, v, 0.0, True)
+    cum = np.cumsum(v, axis=1) / np.arange(1, N + 1)[None, :, None, None]
+    _close(O, cum, what="causal scale 0 output")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, N + 1)), lse.shape), what="causal scale 0 lse")
+
+
+def check_key_shift(ora):
+    """Adding u to every key leaves O unchanged and shifts lse_i by scale*q_i.u."""
+    B, N, Hq, d = 1, 10, 2, 4
+    q, k, v = _rand((B, N, Hq, d), 150), _rand((B, N, Hq, d), 151), _rand((B, N, Hq, d), 152)
+    u = _rand((d,), 153)
+    for causal in (False, True):
+        O0, l0 = ora.attn_ref(q, k, v, 0.7, causal)
+        O1, l1 = ora.attn_ref(q, k + u, v, 0.7, causal)
+        _close(O1, O0, what="key shift output")
+        _close(l1 - l0, 0.7 * np.einsum("bihd,d->bhi", q, u), what="key shift lse")
+
+
+def check_permutation(ora):
+    B, N, M, Hq, d = 1, 6, 13, 2, 4
+    q, k, v = _rand((B, N, Hq, d), 160), _rand((B, M, Hq, d), 161), _rand((B, M, Hq, d), 162)
+    perm = np.random.default_rng(163).permutation(M)
+    O0, l0 = ora.attn_ref(q, k, v, 0.5, False)
+    O1, l1 = ora.attn_ref(q, k[:, perm], v[:, perm], 0.5, False)
+    _close(O1, O0, what="permutation output")
+    _close(l1, l0, what="permutation lse")
+
+
+def check_gqa_is_repeated_mha(ora):
+    B, N, Hq, Hkv, d = 2, 9, 6, 2, 4
+    q, k, v = _rand((B, N, Hq, d), 170), _rand((B, N, Hkv, d), 171), _rand((B, N, Hkv, d), 172)
+    g = Hq // Hkv
+    for causal in (False, True):
+        O0, l0 = ora.attn_ref(q, k, v, 0.5, causal)
+        O1, l1 = ora.attn_ref(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), 0.5, causal)
+        _close(O0, O1, what="GQA output")
+        _close(l0, l1, what="GQA lse")
+
+
+def check_decode_is_single_query_attention(ora):
+    B, Hq, Hkv, M, d = 2, 4, 2, 37, 6
+    q, k, v = _rand((B, Hq, d), 180), _rand((B, Hkv, M, d), 181), _rand((B, Hkv, M, d), 182)
+    O, L, _, _ = ora.decode_ref(q, k, v, 0.45, 8)
+    Of, Lf = ora.attn_ref(q[:, None], k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3), 0.45, False)
+    _close(O, Of[:, 0], what="decode vs forward output")
+    _close(L, Lf[:, :, 0], what="decode vs forward lse")
+
+
+def check_merge_identities(ora):
+    B, Hq, M, d = 1, 3, 29, 5
+    q, k, v = _rand((B, Hq, d), 190), _rand((B, Hq, M, d), 191), _rand((B, Hq, M, d), 192)
+    ref = None
+    for chunk in (1, 3, 7, 29, 64):          # any partition, uneven tail included
+        O, L, op, lp = ora.decode_ref(q, k, v, 0.5, chunk)
+        if ref is None:
+            ref = (O, L)
+        _close(O, ref[0], what=f"partition {chunk} output")
+        _close(L, ref[1], what=f"partition {chunk} lse")
+        rev = ora.lse_merge_ref(op[..., ::-1, :], lp[..., ::-1])   # order invariance
+        _close(rev[0], O, what="reversed chunk order")
+    op1, lp1 = ora.decode_partials_ref(q, k, v, 0.5, M)          # one chunk: identity merge
+    O1, L1 = ora.lse_merge_ref(op1, lp1)
+    _close(O1, op1[..., 0, :], what="single chunk output")
+    _close(L1, lp1[..., 0], what="single chunk lse")
+    # two chunks with equal lse average their outputs
+    o2 = _rand((2, 4), 193)
+    Om, Lm = ora.lse_merge_ref(o2[None], np.array([[0.3, 0.3]]))
+    _close(Om[0], o2.mean(0), what="equal-weight merge")
+    _close(Lm[0], 0.3 + math.log(2.0), what="equal-weight merge lse")
+
+
+def check_two_keys_closed_form(ora):
+    """Two keys: O = sigmoid-weighted mix, lse = log(e^s0 + e^s1)."""
+    q = np.array([[[[1.0, -2.0]]]])
+    k = np.array([[[[0.5, 0.25]], [[-1.0, 3.0]]]])
+    v = np.array([[[[2.0, 1.0]], [[-4.0, 0.5]]]])
+    s0, s1 = 0.9 * (0.5 - 0.5), 0.9 * (-1.0 - 6.0)
+    w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+    O, lse = ora.attn_ref(q, k, v, 0.9, False)
+    _close(O[0, 0, 0], [(1 - w1) * 2.0 + w1 * -4.0, (1 - w1) * 1.0 + w1 * 0.5], what="two-key O")
+    _close(lse[0, 0, 0], math.log(math.exp(s0) + math.exp(s1)), what="two-key lse")
+
+
+FAST_CHECKS = [
+    check_brute_prefill_tiny, check_brute_decode_tiny, check_sdpa,
+    check_identity_v_rows_are_probabilities, check_constant_v, check_single_key,
+    check_causal_row0, check_zero_scale, check_key_shift, check_permutation,
+    check_gqa_is_repeated_mha, check_decode_is_single_query_attention,
+    check_merge_identities, check_two_keys_closed_form,
+]
+
+
+def failing_checks(ora):
+    """Names of the fast checks that the given oracle fails (exceptions count)."""
+    bad = []
+    for chk in FAST_CHECKS:
+        try:
+            chk(ora)
+        except Exception as e:  # noqa: BLE001 - a crash is a failed pin too
+            bad.append(f"{chk.__name__}: {type(e).__name__}: {e}"[:200])
+    return bad

@@ -1,0 +1,50 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch every one of them (CPU only).  The mistakes are planted by editing the
+oracle's source text, so the real oracle is never touched."""
+import pathlib
+import types
+
+import numpy as np
+import pytest
+
+from tests import pins
+
+SRC = (pathlib.Path(__file__).resolve().parents[1] / "oracle" / "attention.py").read_text()
+
+MUTANTS = {
+    # name: (original text, planted mistake)
+    "gqa_interleaved_heads": ("kh = h // group", "kh = h % Hkv"),
+    "causal_off_by_one": ("keys[None, :] > rows[:, None]", "keys[None, :] >= rows[:, None]"),
+    "causal_upper_triangle": ("keys[None, :] > rows[:, None]", "keys[None, :] < rows[:, None]"),
+    "scale_dropped": ("S = float(scale) * (Qbh @ Kbh.T)", "S = (Qbh @ Kbh.T)"),
+    "scale_squared": ("S = float(scale) * (Qbh @ Kbh.T)", "S = float(scale) ** 2 * (Qbh @ Kbh.T)"),
+    "pv_uses_keys": ("O[b, :, h, :] = P @ Vbh", "O[b, :, h, :] = P @ Kbh[:, :Vbh.shape[1]]"),
+    "max_over_wrong_axis": ("m = np.max(S, axis=-1, keepdims=True)", "m = np.max(S, axis=0, keepdims=True)"),
+    "lse_without_max": ("m_safe + np.log(np.where(empty, 1.0, l))", "np.log(np.where(empty, 1.0, l))"),
+    "lse_log2": ("m_safe + np.log(np.where(empty, 1.0, l))", "m_safe + np.log2(np.where(empty, 1.0, l))"),
+    "softmax_unnormalised": ("E / np.where(empty, 1.0, l)", "E"),
+    "exp_sign_flipped": ("E = np.exp(S - m_safe)", "E = np.exp(m_safe - S)"),
+    "decode_tail_chunk_dropped": ("C = -(-M // chunk)", "C = M // chunk"),
+    "decode_partial_unnormalised": ("/ l_c   # O_c", "  # O_c"),
+    "decode_lse_without_max": ("m_c + np.log(l_c)", "np.log(l_c)"),
+    "decode_scale_dropped": ("s = float(scale) * (k[b, kh, lo:hi, :] @ q[b, h, :])",
+                             "s = (k[b, kh, lo:hi, :] @ q[b, h, :])"),
+    "merge_weights_unnormalised": ("w = np.exp(lse_part - g)", "w = np.exp(lse_part - mx)"),
+    "merge_lse_without_max": ("g = mx + np.log(", "g = np.log("),
+    "merge_plain_average": ("O = np.sum(w[..., None] * o_part, axis=-2)", "O = np.mean(o_part, axis=-2)"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found in the oracle"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__dict__["np"] = np
+    exec(compile(SRC.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    bad = pins.failing_checks(_mutant(name))
+    assert bad, f"no pin caught the planted mistake {name}"
