@@ -1,0 +1,122 @@
+"""MI355X (gfx950) fused attention forward and split-KV decode.
+
+Thin Python binding over the C ABI in ``include/attn.h``: it only marshals
+torch tensors (device memory and the current stream) into pointers and sizes;
+every step of the computation runs in the HIP kernels of ``csrc/``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
+    "attn_decode_workspace_bytes", "attn_status_string", "attn_decode",
+]
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+_DTYPES = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        super().__init__(f"{fn} failed with status {status}: {attn_status_string(status)}")
+        self.status = status
+
+
+def attn_status_string(status: int) -> str:
+    return _lib.load().attn_status_string(int(status)).decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _check(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,
+             return_lse: bool = True, stream=None):
+    """q [B,N,Hq,d], k/v [B,M,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N] fp32 or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n)
+    B, N, Hq, d = q.shape
+    M, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale),
+                              _dtype_code(q), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return o, lse
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, M: int, d: int, chunk_size: int = 128) -> int:
+    return int(_lib.load().attn_decode_workspace_bytes(B, Hq, M, d, chunk_size))
+
+
+def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = None,
+                        o_part=None, lse_part=None, stream=None):
+    """q [B,Hq,d], k/v [B,Hkv,M,d] -> (o_part [B,Hq,C,d] fp32, lse_part [B,Hq,C] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n)
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    C = -(-M // chunk_size)
+    if scale is None:
+        scale = d ** -0.5
+    if o_part is None:
+        o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                         lse_part.data_ptr(), B, Hq, Hkv, M, d, chunk_size,
+                                         float(scale), _dtype_code(q), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_splitkv")
+    return o_part, lse_part
+
+
+def lse_merge(o_part, lse_part, out_dtype=torch.float16, o=None, lse=None, return_lse: bool = True,
+              stream=None):
+    """o_part [B,Hq,C,d], lse_part [B,Hq,C] -> (o [B,Hq,d] out_dtype, lse [B,Hq] fp32 or None)."""
+    _check(o_part, "o_part")
+    _check(lse_part, "lse_part")
+    B, Hq, C, d = o_part.shape
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=out_dtype, device=o_part.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
+    st = _lib.load().lse_merge(o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, B, Hq, C, d,
+                               _DTYPES[o.dtype], _stream(stream))
+    if st != 0:
+        raise AttnError(st, "lse_merge")
+    return o, lse
+
+
+def attn_decode(q, k, v, chunk_size: int = 128, scale: float | None = None, stream=None):
+    """Split-KV decode end to end (two launches on one stream)."""
+    o_part, lse_part = attn_decode_splitkv(q, k, v, chunk_size, scale, stream=stream)
+    o, lse = lse_merge(o_part, lse_part, q.dtype, stream=stream)
+    return o, lse, o_part, lse_part

@@ -1,0 +1,114 @@
+// C ABI of the attention library: argument validation, status codes and
+// kernel dispatch.  Every entry point validates all arguments before touching
+// the GPU, launches asynchronously on the caller's stream, never allocates and
+// never synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "../../include/attn.h"
+
+namespace attn {
+hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int Hq, int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
+                            hipStream_t stream);
+hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                           int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream);
+hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq,
+                          int C, int d, bool bf16, hipStream_t stream);
+}  // namespace attn
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // 32-bit element offsets per dimension product
+constexpr int kDecodeChunk = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_head_dim(int d) { return d == 64 || d == 128; }
+bool valid_dtype(int dt) { return dt == ATTN_F16 || dt == ATTN_BF16; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_DIMENSION: return "a size argument is not positive";
+    case ATTN_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
+    case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N == M (top-left mask)";
+    case ATTN_ERR_CHUNK_SIZE: return "decode chunk size must be 128";
+    case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
+    case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
+    case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+             int M, int d, int causal, float scale, attn_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (causal && N != M) return ATTN_ERR_CAUSAL_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  if ((int64_t)B * N * Hq * d >= kMaxElems || (int64_t)B * M * Hkv * d >= kMaxElems ||
+      (int64_t)B * Hq * ((N + 127) / 128) >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(attn::prefill_dispatch(q, k, v, o, lse, B, Hq, Hkv, N, M, d, causal != 0,
+                                              dtype == ATTN_BF16, scale, stream));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size) {
+  if (B <= 0 || Hq <= 0 || M <= 0 || d <= 0 || chunk_size <= 0) return 0;
+  const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
+  return (size_t)((int64_t)B * Hq * C * (d + 1) * 4);
+}
+
+int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                        int Hq, int Hkv, int M, int d, int chunk_size, float scale, attn_dtype_t dtype,
+                        hipStream_t stream) {
+  if (!q || !k || !v || !o_part || !lse_part) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || chunk_size <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (chunk_size != kDecodeChunk) return ATTN_ERR_CHUNK_SIZE;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
+  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, dtype == ATTN_BF16,
+                                             scale, stream));
+}
+
+int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int num_chunks,
+              int d, attn_dtype_t out_dtype, hipStream_t stream) {
+  if (!o_part || !lse_part || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || num_chunks <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(out_dtype)) return ATTN_ERR_DTYPE;
+  if ((int64_t)B * Hq * num_chunks * d >= kMaxElems || (int64_t)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
+  if ((reinterpret_cast<uintptr_t>(o_part) & 3u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(o) & 1u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(
+      attn::merge_dispatch(o_part, lse_part, o, lse, B, Hq, num_chunks, d, out_dtype == ATTN_BF16, stream));
+}
+
+}  // extern "C"

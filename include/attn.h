@@ -1,0 +1,127 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * Operations (definitions from the pages, in their notation):
+ *   attn_fwd             fused attention forward, O = softmax(scale * Q K^T [+causal]) V,
+ *                        computed tile by tile with an online softmax so that the score
+ *                        and probability matrices never reach HBM ("fmha sm120: beyond
+ *                        torch.sdpa", section 1 "flash attention" and section 2 "fmha
+ *                        implementation").
+ *   attn_decode_splitkv  Flash-Decoding step 1: per-chunk partial outputs O_c and
+ *                        log-sum-exp lse_c of a single query ("CUDA Flash Decoding",
+ *                        section 2.2, step 1).
+ *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
+ *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
+ *                        section 2.2, step 2, and section 6 "reduce kernel").
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are device memory owned by the caller, contiguous in the
+ *     stated layout, and 16-byte aligned.  The library never allocates, frees,
+ *     synchronises or throws; work is enqueued on `stream` (NULL = the default
+ *     stream) and completes asynchronously.
+ *   - The return value is ATTN_OK (0) or a negative attn_status_t.  On any error
+ *     nothing is launched and no output is touched, except ATTN_ERR_LAUNCH, which
+ *     reports a failed kernel launch (outputs are then undefined).
+ *   - Outputs must not alias inputs.  fp16/bf16 outputs are rounded to nearest even
+ *     from fp32.  All accumulation is fp32.
+ *   - Inputs holding Inf/NaN propagate NaN to the affected outputs.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type, declared exactly as HIP declares it. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  ATTN_F16 = 0,  /* IEEE binary16 */
+  ATTN_BF16 = 1  /* bfloat16 */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_POINTER = -1,   /* a required pointer is NULL */
+  ATTN_ERR_BAD_DIMENSION = -2,  /* a size is <= 0 */
+  ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not in {64, 128} */
+  ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
+  ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
+  ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N != M */
+  ATTN_ERR_CHUNK_SIZE = -7,     /* decode chunk size other than 128 */
+  ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (hipGetLastError) */
+  ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
+  ATTN_ERR_ALIGNMENT = -10,     /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_SCALE = -11          /* scale is negative, infinite or NaN */
+} attn_status_t;
+
+/*
+ * attn_fwd - fused multi-head / grouped-query attention forward (prefill).
+ *
+ *   q   [B, N, Hq, d]   dtype, read        o   [B, N, Hq, d]  dtype, written
+ *   k   [B, M, Hkv, d]  dtype, read        lse [B, Hq, N]     fp32, written (may be NULL)
+ *   v   [B, M, Hkv, d]  dtype, read
+ *
+ * For batch b and query head h the key/value head is h / (Hq / Hkv) (contiguous
+ * groups, "fmha sm120", section 2).  S = scale * Q K^T; with causal != 0 key j is
+ * masked for query i when j > i (top-left mask, defined only for N == M);
+ * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
+ * including the row maximum).  Requires d in {64, 128}, Hq % Hkv == 0, a finite
+ * scale >= 0, and B*N*Hq*d, B*M*Hkv*d below 2^31.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
+             attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes - bytes of fp32 partials that one split-KV decode call
+ * writes: B*Hq*C*(d+1)*4 with C = ceil(M / chunk_size).  The caller may carve
+ * o_part (B*Hq*C*d floats) and lse_part (B*Hq*C floats) out of one buffer of this
+ * size.  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size);
+
+/*
+ * attn_decode_splitkv - per-chunk partials of single-query attention.
+ *
+ *   q   [B, Hq, d]        dtype, read     o_part   [B, Hq, C, d]  fp32, written
+ *   k   [B, Hkv, M, d]    dtype, read     lse_part [B, Hq, C]     fp32, written
+ *   v   [B, Hkv, M, d]    dtype, read
+ *
+ * Chunk c covers keys [c*chunk_size, min((c+1)*chunk_size, M)); the last chunk may
+ * be shorter.  For each chunk: s_j = scale * q.k_j, m_c = max_j s_j,
+ * p_j = exp(s_j - m_c), l_c = sum p_j, o_part = (sum_j p_j v_j) / l_c (normalised),
+ * lse_part = m_c + ln l_c ("CUDA Flash Decoding", section 2.2 step 1).  No mask.
+ * Requires chunk_size == 128, d in {64, 128}, Hq % Hkv == 0, a finite scale >= 0,
+ * B*Hq <= 65535, and B*Hkv*M*d, B*Hq*C*d below 2^31.
+ */
+int attn_decode_splitkv(const void* q, const void* k, const void* v,
+                        float* o_part, float* lse_part,
+                        int B, int Hq, int Hkv, int M, int d, int chunk_size, float scale,
+                        attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * lse_merge - combine chunk partials into the decode output.
+ *
+ *   o_part   [B, Hq, C, d] fp32, read     o   [B, Hq, d]  out_dtype, written
+ *   lse_part [B, Hq, C]    fp32, read     lse [B, Hq]     fp32, written (may be NULL)
+ *
+ * g = max_c lse_c + ln sum_c exp(lse_c - max_c lse_c), w_c = exp(lse_c - g),
+ * o = sum_c w_c o_part[c], lse = g ("CUDA Flash Decoding", section 2.2 step 2).
+ * Requires num_chunks >= 1 and d in {64, 128}.
+ */
+int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+              int B, int Hq, int num_chunks, int d, attn_dtype_t out_dtype,
+              hipStream_t stream);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,117 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/attn.h declares, and rejects every invalid argument with its
+documented status before touching the GPU.  No call here has a complete set
+of valid arguments, so nothing is ever launched."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+from attention_attn_fwd_06_amd import _lib
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "attn.h"
+FAKE = 4096  # a 16-byte-aligned non-null address; never dereferenced
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def status_codes():
+    text = HEADER.read_text()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(
+        ["attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "lse_merge", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(_lib.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SYMBOLS)
+
+
+def test_status_strings():
+    lib = _lib.load()
+    codes = status_codes()
+    seen = set()
+    for name, val in codes.items():
+        if name in ("ATTN_F16", "ATTN_BF16"):
+            continue
+        s = lib.attn_status_string(val).decode()
+        assert s and s != "unknown status", name
+        seen.add(s)
+    assert len(seen) == len([n for n in codes if n not in ("ATTN_F16", "ATTN_BF16")])
+    assert lib.attn_status_string(12345).decode() == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, N=128, M=128, d=64,
+             causal=0, scale=0.125, dtype=0, stream=None)
+    a.update(kw)
+    return _lib.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                a["N"], a["M"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(Hq=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(M=-5), -2), (dict(d=0), -2),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(d=32), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(Hq=6, Hkv=4), -5),
+    (dict(causal=1, N=128, M=256), -6),
+    (dict(scale=-0.5), -11), (dict(scale=float("inf")), -11), (dict(scale=float("nan")), -11),
+    (dict(B=1 << 12, N=1 << 12, Hq=1 << 4, d=128), -9),
+    (dict(q=FAKE + 8), -10), (dict(o=FAKE + 2), -10), (dict(lse=FAKE + 2), -10),
+])
+def test_attn_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, op=FAKE, lp=FAKE, B=1, Hq=8, Hkv=8, M=512, d=128, chunk=128,
+             scale=0.088, dtype=0, stream=None)
+    a.update(kw)
+    return _lib.load().attn_decode_splitkv(a["q"], a["k"], a["v"], a["op"], a["lp"], a["B"], a["Hq"],
+                                           a["Hkv"], a["M"], a["d"], a["chunk"], a["scale"], a["dtype"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1),
+    (dict(M=0), -2), (dict(chunk=0), -2), (dict(B=-1), -2),
+    (dict(d=80), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
+    (dict(chunk=64), -7), (dict(chunk=256), -7),
+    (dict(scale=-1.0), -11),
+    (dict(B=70000, Hq=1, Hkv=1, M=128), -9),
+    (dict(k=FAKE + 4), -10), (dict(op=FAKE + 1), -10),
+])
+def test_decode_rejects(kw, code):
+    assert dec(**kw) == code
+
+
+def mrg(**kw):
+    a = dict(op=FAKE, lp=FAKE, o=FAKE, lse=None, B=1, Hq=8, C=4, d=128, dtype=0, stream=None)
+    a.update(kw)
+    return _lib.load().lse_merge(a["op"], a["lp"], a["o"], a["lse"], a["B"], a["Hq"], a["C"], a["d"],
+                                 a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), -1), (dict(o=None), -1), (dict(C=0), -2), (dict(d=100), -3), (dict(dtype=3), -4),
+    (dict(o=FAKE + 1), -10), (dict(lse=FAKE + 1), -10),
+])
+def test_merge_rejects(kw, code):
+    assert mrg(**kw) == code
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    assert lib.attn_decode_workspace_bytes(2, 8, 65536, 128, 128) == 2 * 8 * 512 * 129 * 4
+    assert lib.attn_decode_workspace_bytes(1, 8, 513, 128, 128) == 1 * 8 * 5 * 129 * 4
+    assert lib.attn_decode_workspace_bytes(0, 8, 512, 128, 128) == 0

@@ -1,0 +1,276 @@
+"""GPU path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Tolerances (fixed for this method): max|dO| <= 2e-3 for fp16 and <= 8e-3 for
+bf16 outputs, |dlse| <= 1e-3, both against the unrounded float64 oracle on the
+same seeded, already-rounded inputs.  Decode partials (fp32) are held to the
+same bounds.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, decode_inputs, make_inputs, prefill_inputs, torch_dtype
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+TOL_O = {"f16": 2e-3, "bf16": 8e-3}
+TOL_LSE = 1e-3
+
+
+def attn():
+    import attention_attn_fwd_06_amd as a
+    return a
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def gpu_fwd(q, k, v, causal, scale):
+    o, lse = attn().attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return f64(o), f64(lse)
+
+
+def check_prefill(q, k, v, causal, scale, dtype, rows=None, bh=None, label=""):
+    """Run the GPU on the whole problem; compare all of it, or the given
+    (batch, head) pairs and query rows, with the oracle."""
+    Og, Lg = gpu_fwd(q, k, v, causal, scale)
+    assert np.all(np.isfinite(Og)) and np.all(np.isfinite(Lg)), "non-finite output"
+    if bh is None:
+        Or, Lr = oracle.attn_ref(q, k, v, scale, causal)
+        eo, el = maxerr(Og, Or), maxerr(Lg, Lr)
+    else:
+        Hq, Hkv = q.shape[2], k.shape[2]
+        eo = el = 0.0
+        for b, h in bh:
+            kh = h // (Hq // Hkv)
+            Or, Lr = oracle.attn_ref(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, kh:kh + 1],
+                                     v[b:b + 1, :, kh:kh + 1], scale, causal, rows=rows)
+            eo = max(eo, maxerr(Og[b:b + 1, rows, h:h + 1], Or))
+            el = max(el, maxerr(Lg[b:b + 1, h:h + 1, rows], Lr))
+    say(f"  {label}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O[dtype], f"{label}: max|dO| {eo:.3e} > {TOL_O[dtype]}"
+    assert el <= TOL_LSE, f"{label}: max|dlse| {el:.3e} > {TOL_LSE}"
+
+
+# --------------------------------------------------------------------------
+# prefill
+# --------------------------------------------------------------------------
+
+def test_prefill_tiny_workload_whole():
+    w = WORKLOADS["tiny_mha_fp16_d64"]
+    say(f"case {w.name}")
+    q, k, v = make_inputs(w, 0)
+    check_prefill(q, k, v, w.causal, w.scale, w.dtype, label=w.name)
+
+
+SHAPES = [
+    # B, N, M, Hq, Hkv, d, dtype, causal
+    (1, 1, 1, 1, 1, 64, "f16", False),
+    (1, 1, 1, 2, 1, 128, "bf16", True),
+    (1, 200, 333, 4, 4, 64, "f16", False),
+    (1, 130, 70, 2, 2, 64, "bf16", False),
+    (2, 256, 256, 4, 1, 128, "f16", True),
+    (1, 520, 520, 8, 2, 128, "bf16", True),
+    (3, 97, 97, 4, 4, 64, "bf16", True),
+    (1, 64, 4096, 8, 8, 128, "f16", False),
+    (2, 384, 384, 8, 4, 64, "f16", True),
+    (1, 300, 300, 16, 2, 128, "bf16", False),
+    (1, 129, 129, 8, 8, 128, "f16", True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_shapes_whole(shape):
+    B, N, M, Hq, Hkv, d, dt, causal = shape
+    say(f"case prefill {shape}")
+    g = torch.Generator("cpu").manual_seed(1234 + N + M)
+    q = torch.randn((B, N, Hq, d), generator=g).to(torch_dtype(dt))
+    k = torch.randn((B, M, Hkv, d), generator=g).to(torch_dtype(dt))
+    v = torch.randn((B, M, Hkv, d), generator=g).to(torch_dtype(dt))
+    check_prefill(q, k, v, causal, float(np.float32(d ** -0.5)), dt, label=str(shape))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefill_causal_gqa_bf16_reduced(seed):
+    """The causal GQA bf16 d=128 workload at reduced length (all rows, all
+    heads): includes the early causal rows where |O| is largest."""
+    say(f"case causal gqa bf16 reduced seed {seed}")
+    q, k, v = prefill_inputs(2, 8, 2, 1024, 1024, 128, "bf16", seed)
+    check_prefill(q, k, v, True, WORKLOADS["prefill_causal_gqa_bf16_d128"].scale, "bf16",
+                  label=f"B2 Hq8 Hkv2 N1024 seed{seed}")
+
+
+def _sample_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(0, 192), rng.choice(np.arange(192, N - 64), 256, replace=False),
+                           np.arange(N - 64, N)])
+    return np.sort(rows)
+
+
+def test_prefill_mha_fp16_d64_full_size_sampled():
+    w = WORKLOADS["prefill_mha_fp16_d64"]
+    say(f"case {w.name} (full size, sampled heads and rows)")
+    q, k, v = make_inputs(w, 0)
+    check_prefill(q, k, v, w.causal, w.scale, w.dtype, rows=_sample_rows(w.N, 1),
+                  bh=[(0, 0), (5, 7), (9, 12), (15, 15)], label=w.name)
+
+
+def test_prefill_causal_gqa_bf16_full_size_sampled():
+    w = WORKLOADS["prefill_causal_gqa_bf16_d128"]
+    say(f"case {w.name} (full size, sampled heads and rows)")
+    q, k, v = make_inputs(w, 0)
+    check_prefill(q, k, v, w.causal, w.scale, w.dtype, rows=_sample_rows(w.N, 2),
+                  bh=[(0, 0), (0, 3), (1, 13), (2, 22), (3, 31)], label=w.name)
+
+
+def test_prefill_deterministic():
+    say("case prefill determinism")
+    q, k, v = prefill_inputs(1, 8, 2, 520, 520, 128, "bf16", 5)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = attn().attn_fwd(qd, kd, vd, causal=True)
+    o2, l2 = attn().attn_fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_writes_every_output():
+    say("case prefill NaN-poisoned outputs")
+    q, k, v = prefill_inputs(2, 4, 2, 333, 333, 64, "f16", 6)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((2, 4, 333), float("nan"), device=DEV)
+    attn().attn_fwd(qd, kd, vd, causal=True, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+
+
+def test_prefill_invariants_black_box():
+    say("case prefill invariants")
+    B, N, Hq, Hkv, d = 1, 200, 8, 2, 128
+    q, k, v = prefill_inputs(B, Hq, Hkv, N, N, d, "bf16", 7)
+    scale = float(np.float32(d ** -0.5))
+    # constant V rows -> O equals that row
+    u = v[:, :1].expand_as(v).contiguous()
+    Og, _ = gpu_fwd(q, k, u, True, scale)
+    ref = np.broadcast_to(f64(u[:, :1]).repeat(Hq // Hkv, axis=2), Og.shape)
+    assert maxerr(Og, ref) <= TOL_O["bf16"]
+    # causal row 0 is exactly V[0] of its KV head
+    Og, Lg = gpu_fwd(q, k, v, True, scale)
+    v0 = f64(v[:, 0]).repeat(Hq // Hkv, axis=1)
+    assert maxerr(Og[:, 0], v0) == 0.0
+    # GQA == MHA with repeated KV heads (same kernel work per head: bitwise)
+    kr = k.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+    vr = v.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+    Og2, Lg2 = gpu_fwd(q, kr, vr, True, scale)
+    assert np.array_equal(Og, Og2) and np.array_equal(Lg, Lg2)
+    # scale = 0: uniform weights, lse = ln(#allowed keys)
+    Og, Lg = gpu_fwd(q, k, v, True, 0.0)
+    cnt = np.arange(1, N + 1)
+    assert maxerr(Lg, np.broadcast_to(np.log(cnt), Lg.shape)) <= TOL_LSE
+    vf = f64(v).repeat(Hq // Hkv, axis=2)
+    ref = np.cumsum(vf, axis=1) / cnt[None, :, None, None]
+    assert maxerr(Og, ref) <= TOL_O["bf16"]
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+
+def gpu_decode(q, k, v, chunk, scale):
+    o, lse, op, lp = attn().attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), chunk, scale)
+    torch.cuda.synchronize()
+    return f64(o), f64(lse), f64(op), f64(lp)
+
+
+def check_decode(q, k, v, chunk, scale, dtype, label):
+    Og, Lg, OPg, LPg = gpu_decode(q, k, v, chunk, scale)
+    Or, Lr, OPr, LPr = oracle.decode_ref(q, k, v, scale, chunk)
+    errs = dict(o=maxerr(Og, Or), lse=maxerr(Lg, Lr), o_part=maxerr(OPg, OPr), lse_part=maxerr(LPg, LPr))
+    say(f"  {label}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
+    assert errs["o"] <= TOL_O[dtype] and errs["o_part"] <= TOL_O[dtype], errs
+    assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
+
+
+@pytest.mark.parametrize("name", ["small_decode_fp16_d128", "long_decode_fp16_d128"])
+def test_decode_workload_whole(name):
+    w = WORKLOADS[name]
+    say(f"case {w.name}")
+    q, k, v = make_inputs(w, 0)
+    check_decode(q, k, v, w.chunk, w.scale, w.dtype, w.name)
+
+
+DEC_SHAPES = [
+    # B, Hq, Hkv, M, d, dtype
+    (1, 1, 1, 1, 128, "f16"),
+    (1, 2, 1, 127, 64, "f16"),
+    (2, 8, 2, 1000, 128, "bf16"),
+    (1, 4, 4, 129, 64, "bf16"),
+    (3, 16, 4, 4096, 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("shape", DEC_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_shapes(shape):
+    B, Hq, Hkv, M, d, dt = shape
+    say(f"case decode {shape}")
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=M)
+    check_decode(q, k, v, 128, float(np.float32(d ** -0.5)), dt, str(shape))
+
+
+@pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
+def test_lse_merge_standalone(C, d, dt):
+    say(f"case lse_merge C={C} d={d} {dt}")
+    g = torch.Generator("cpu").manual_seed(C)
+    op = torch.randn((2, 3, C, d), generator=g)
+    lp = torch.randn((2, 3, C), generator=g) * 4.0
+    o, lse = attn().lse_merge(op.to(DEV), lp.to(DEV), torch_dtype(dt))
+    torch.cuda.synchronize()
+    Or, Lr = oracle.lse_merge_ref(op, lp)
+    assert maxerr(f64(o), Or) <= TOL_O[dt]
+    assert maxerr(f64(lse), Lr) <= TOL_LSE
+
+
+def test_decode_matches_prefill_single_query():
+    say("case decode vs attn_fwd(N=1)")
+    B, Hq, Hkv, M, d = 2, 8, 2, 777, 128
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, "f16", seed=9)
+    scale = float(np.float32(d ** -0.5))
+    Od, Ld, _, _ = gpu_decode(q, k, v, 128, scale)
+    Of, Lf = gpu_fwd(q[:, None].contiguous(), k.transpose(1, 2).contiguous(), v.transpose(1, 2).contiguous(),
+                     False, scale)
+    assert maxerr(Od, Of[:, 0]) <= 2 * TOL_O["f16"]
+    assert maxerr(Ld, Lf[:, :, 0]) <= 2 * TOL_LSE
+
+
+def test_decode_deterministic_and_complete():
+    say("case decode determinism / NaN-poisoned outputs")
+    q, k, v = decode_inputs(1, 8, 8, 1000, 128, "f16", seed=3)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    C = math.ceil(1000 / 128)
+    op = torch.full((1, 8, C, 128), float("nan"), device=DEV)
+    lp = torch.full((1, 8, C), float("nan"), device=DEV)
+    attn().attn_decode_splitkv(qd, kd, vd, o_part=op, lse_part=lp)
+    o = torch.full((1, 8, 128), float("nan"), device=DEV, dtype=torch.float16)
+    lse = torch.full((1, 8), float("nan"), device=DEV)
+    attn().lse_merge(op, lp, o=o, lse=lse)
+    o2, l2, _, _ = attn().attn_decode(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert not torch.isnan(op).any() and not torch.isnan(o).any() and not torch.isnan(lse).any()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
