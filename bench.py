@@ -1,0 +1,218 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal GQA bf16 prefill forward (B=4, Hq=32, Hkv=8,
+N=M=4096, d=128) plus one split-KV decode (B=2, H=8, M=65536, d=128, fp16,
+chunk 128: partial kernel + LSE merge), all through the C ABI, with inputs
+already resident in HBM.  The decode rotates between two independent K/V sets
+(1.07 GB together) so the 256 MB last-level cache cannot serve repeats.
+
+Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
+(4*B*Hq*N*M*d, halved for the causal mask) over the prefill kernel's average
+duration, measured with HIP events on the launch stream; the decode result is
+reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import statistics
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
+PREFILL = "prefill_causal_gqa_bf16_d128"
+DECODE = "long_decode_fp16_d128"
+KERNEL_SOURCES = {
+    "prefill": ["attention_attn_fwd_06_amd/csrc/prefill_fwd.hip",
+                "attention_attn_fwd_06_amd/csrc/device_common.h"],
+    "decode": ["attention_attn_fwd_06_amd/csrc/decode.hip",
+               "attention_attn_fwd_06_amd/csrc/device_common.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on a different kernel source."""
+    p = ROOT / "profiles" / f"{kind}_{workload}_traffic.md"
+    if not p.exists():
+        return None
+    vals = {}
+    for line in p.read_text().splitlines():
+        if ":" in line and line.startswith("- "):
+            key, val = line[2:].split(":", 1)
+            vals[key.strip()] = val.strip().strip("`")
+    if vals.get("kernel_source_sha256") != source_hash(kind):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(budget_s: float = 15.0):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    whole (batch, head) problems of the causal GQA workload, timed on the host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import WORKLOADS, attn_flops, make_inputs
+    w = WORKLOADS[PREFILL]
+    q, k, v = make_inputs(w, 0)
+    g = w.Hq // w.Hkv
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(pairs)
+    done, t0 = 0, time.perf_counter()
+    for b, h in pairs:
+        kh = h // g
+        oracle.attn_ref(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, kh:kh + 1], v[b:b + 1, :, kh:kh + 1],
+                        w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = attn_flops(1, done, w.N, w.M, w.d, w.causal)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) problems of {w.name} "
+                      f"(full 4096x4096 S and P per problem, float64 numpy), {dt:.1f} s; "
+                      f"FLOPs credited with the causal-halved count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one part only (for counter collection)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes, not run", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_attn_fwd_06_amd as attn
+    from workloads import WORKLOADS, attn_flops, decode_bytes, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp, wd = WORKLOADS[PREFILL], WORKLOADS[DECODE]
+
+    if args.only == "copy":
+        # Reference copy of a known size for scaling the HBM byte counters.
+        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
+        a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
+        return
+
+    do_p = args.only in (None, "prefill")
+    do_d = args.only in (None, "decode")
+    if do_p:
+        q, k, v = (t.to(dev) for t in make_inputs(wp, args.seed))
+        o = torch.empty_like(q)
+        lse = torch.empty((wp.B, wp.Hq, wp.N), dtype=torch.float32, device=dev)
+    if do_d:
+        dq, dk0, dv0 = (t.to(dev) for t in make_inputs(wd, args.seed))
+        _, dk1, dv1 = (t.to(dev) for t in make_inputs(wd, args.seed + 1))
+        kv_sets = [(dk0, dv0), (dk1, dv1)]
+        C = wd.num_chunks
+        o_part = torch.empty((wd.B, wd.Hq, C, wd.d), dtype=torch.float32, device=dev)
+        lse_part = torch.empty((wd.B, wd.Hq, C), dtype=torch.float32, device=dev)
+        do_ = torch.empty((wd.B, wd.Hq, wd.d), dtype=torch.float16, device=dev)
+        dlse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if do_p:
+            if ev: ev[0].record(stream)
+            attn.attn_fwd(q, k, v, causal=True, scale=wp.scale, o=o, lse=lse, stream=stream)
+            if ev: ev[1].record(stream)
+        if do_d:
+            kk, vv = kv_sets[i % 2]
+            if ev: ev[2].record(stream)
+            attn.attn_decode_splitkv(dq, kk, vv, wd.chunk, wd.scale, o_part=o_part, lse_part=lse_part,
+                                     stream=stream)
+            if ev: ev[3].record(stream)
+            attn.lse_merge(o_part, lse_part, o=do_, lse=dlse, stream=stream)
+            if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    out = {
+        "metric": "attn fwd TFLOP/s & % MFMA peak (prefill); decode HBM GB/s & % peak",
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{PREFILL} + {DECODE}",
+                   "prefill": wp.desc, "decode": wd.desc, "parallelism": "single GPU"},
+    }
+    if do_p:
+        p_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
+        flops = attn_flops(wp.B, wp.Hq, wp.N, wp.M, wp.d, wp.causal)
+        tf = flops / (p_ms * 1e-3) / 1e12
+        traffic = read_traffic("prefill", PREFILL)
+        out["value"] = round(tf, 2)
+        out["prefill_ms"] = round(p_ms, 4)
+        out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic, "kernel": "prefill_fwd_kernel<128,bf16,causal>",
+                           "per_launch": f"{flops:.6g} FLOP (causal-halved)"}
+    if do_d:
+        c_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in events)
+        m_ms = statistics.mean(e[3].elapsed_time(e[4]) for e in events)
+        nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d)
+        chunk_bytes = nbytes - wd.B * wd.Hq * wd.d * 2  # K+V+q (O is written by the merge)
+        gbps = nbytes / ((c_ms + m_ms) * 1e-3) / 1e9
+        out["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "dtype": "f16", "chunk_ms": round(c_ms, 4), "merge_ms": round(m_ms, 4),
+                         "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
+                         "algorithmic_bytes": nbytes}
+        out["roofline_decode"] = {"bound": "hbm", "achieved": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(chunk_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                  "traffic": read_traffic("decode", DECODE),
+                                  "kernel": "decode_chunk_kernel<128,f16>",
+                                  "per_launch": f"{chunk_bytes:.6g} B (K+V+q)"}
+        if not do_p:
+            out["value"], out["unit"], out["dtype"] = out["decode"]["value"], "GB/s", "f16"
+    if args.only is None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
