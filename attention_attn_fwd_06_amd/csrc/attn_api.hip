@@ -61,7 +61,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (causal && N != M) return ATTN_ERR_CAUSAL_SHAPE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
-  if ((int64_t)B * N * Hq * d >= kMaxElems || (int64_t)B * M * Hkv * d >= kMaxElems ||
+  if ((int64_t)B * N * Hq * d >= kMaxElems || (int64_t)B * (M + 64) * Hkv * d >= kMaxElems ||
       (int64_t)B * Hq * ((N + 127) / 128) >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -104,7 +104,7 @@ int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
   if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(out_dtype)) return ATTN_ERR_DTYPE;
   if ((int64_t)B * Hq * num_chunks * d >= kMaxElems || (int64_t)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
-  if ((reinterpret_cast<uintptr_t>(o_part) & 3u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(o) & 1u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_ALIGNMENT;
   return launch_status(

@@ -4,17 +4,21 @@
 // flow; section 6: the reduce kernel).
 //
 // MI355X design (not the page's CUDA design):
-//  * chunk kernel: one 256-thread workgroup per (chunk of 128 keys, batch,
-//    query head).  Every K and V load of the chunk (64 KB at d = 128) is issued
-//    up front: V does not depend on the scores, so the whole chunk is in flight
+//  * chunk kernel: persistent grid of 256-thread workgroups (as many as fit
+//    on the chip at once), each taking (chunk of 128 keys, batch, query head)
+//    items in turn, so the grid drains evenly.  Every K and V load of a chunk
+//    (64 KB at d = 128) is issued up front, with a nontemporal hint: V does not depend on the scores, so the whole chunk is in flight
 //    at once and the kernel streams HBM.  A row of K/V (d * 2 bytes) is read by
 //    d/8 consecutive lanes, 16 bytes each (fully coalesced).
 //  * scores use fp32 accumulation (v_dot2_f32_{f16,bf16}) and a DPP sum over the
 //    lanes that share a key row; softmax statistics use exp2 with the scale
 //    folded into one multiply; partials are written in fp32, O_c normalised.
-//  * merge kernel: one workgroup per (batch, query head, 32-column slice of d),
-//    so the fp32 partials are read by many CUs at once; chunk weights are
-//    recomputed from lse_c (no staging limit on the number of chunks).
+//  * merge kernel: one workgroup per (batch, query head, 16-column slice of d),
+//    one pass over the partials with a running max (no separate pass for the
+//    global log-sum-exp, no limit on the number of chunks), 16-byte loads, and
+//    eight independent loads in flight per thread.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace attn {
@@ -44,183 +48,221 @@ __device__ __forceinline__ float row_sum(float x) {
   else return sum8(x);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load that streams past the caches (K/V are read exactly once).
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Persistent grid: workgroup w handles items w, w + gridDim.x, ... where item
+// = c + C * (b * Hq + h), so every workgroup ends at about the same time.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kDecThreads)
 void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, float* __restrict__ o_part,
                          float* __restrict__ lse_part, int Hq, int Hkv, int M, int C,
-                         float scale_log2) {
-  constexpr int kLanes = D / 8;                     // lanes per key row
+                         int n_items, float scale_log2) {
+  constexpr int kLanes = D / 8;                       // lanes per key row
   constexpr int kRowsPerPass = kDecThreads / kLanes;  // 16 (d=128) or 32 (d=64)
   constexpr int kPasses = kChunk / kRowsPerPass;      // rows per thread
   constexpr int kWaves = kDecThreads / 64;
-  __shared__ float red[kWaves];
+  __shared__ float red[2][kWaves];
   __shared__ float opart[kWaves][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int h = bh % Hq, b = bh / Hq;
-  const int kvh = h / (Hq / Hkv);
   const int col = tid % kLanes;  // 16-byte column chunk
   const int r0 = tid / kLanes;   // first row of this thread
-  const int key0 = c * kChunk;
-  const int len = min(kChunk, M - key0);
 
-  const uint16_t* kp = k + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
-  const uint16_t* vp = v + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
-  const uint4 qv = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h) * D + col * 8);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int c = item % C;
+    const int bh = item / C;
+    const int h = bh % Hq, b = bh / Hq;
+    const int kvh = h / (Hq / Hkv);
+    const int key0 = c * kChunk;
+    const int len = min(kChunk, M - key0);
 
-  // issue the whole chunk: K then V
-  uint4 kr[kPasses], vr[kPasses];
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = r0 + p * kRowsPerPass;
-    kr[p] = row < len ? *reinterpret_cast<const uint4*>(kp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = r0 + p * kRowsPerPass;
-    vr[p] = row < len ? *reinterpret_cast<const uint4*>(vp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
-  }
+    const uint16_t* kp = k + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
+    const uint16_t* vp = v + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
+    const uint4 qv = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h) * D + col * 8);
 
-  // scores in log2 units: x_j = scale * log2(e) * q.k_j
-  float x[kPasses];
-  float mx = -INFINITY;
+    // issue the whole chunk: K then V
+    uint4 kr[kPasses], vr[kPasses];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = r0 + p * kRowsPerPass;
-    float sdot = row_sum<kLanes>(dot8<BF16>(qv, kr[p], 0.f));
-    x[p] = row < len ? sdot * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, x[p]);
-  }
-  // chunk max: over the rows of this wave, then over the waves
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, max_xor32(mx));
-  if (kLanes == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = r0 + p * kRowsPerPass;
-    const float e = row < len ? __builtin_amdgcn_exp2f(x[p] - m) : 0.f;
-    l += e;
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[p]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x2 vv = unpack2<BF16>(vw[t]);
-      acc[2 * t] = fmaf(e, vv[0], acc[2 * t]);
-      acc[2 * t + 1] = fmaf(e, vv[1], acc[2 * t + 1]);
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = r0 + p * kRowsPerPass;
+      kr[p] = row < len ? load_stream(kp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
     }
-  }
-  // l: every lane of a row group holds the same e, so sum one lane per row group
-  // over the rows of the wave, then across waves.
-  l += __shfl_xor(l, 16);
-  l = sum_xor32(l);
-  if (kLanes == 8) l += __shfl_xor(l, 8);
-  // column partials: reduce lanes with the same column chunk within the wave
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    float a = acc[t];
-    if (kLanes == 8) a += __shfl_xor(a, 8);
-    a += __shfl_xor(a, 16);
-    a = sum_xor32(a);
-    acc[t] = a;
-  }
-  __syncthreads();  // red[] reused below
-  if (lane < kLanes) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) opart[wave][lane * 8 + t] = acc[t];
-  }
-  if (lane == 0) red[wave] = l;
-  __syncthreads();
-  if (tid < D) {
-    float lt = 0.f, ot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      lt += red[w];
-      ot += opart[w][tid];
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = r0 + p * kRowsPerPass;
+      vr[p] = row < len ? load_stream(vp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
     }
-    const int64_t base = ((int64_t)b * Hq + h) * C + c;
-    o_part[base * D + tid] = ot / lt;
-    if (tid == 0) lse_part[base] = (m + log2f(lt)) * kLn2;
+
+    // scores in log2 units: x_j = scale * log2(e) * q.k_j
+    float x[kPasses];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = r0 + p * kRowsPerPass;
+      const float sdot = row_sum<kLanes>(dot8<BF16>(qv, kr[p], 0.f));
+      x[p] = row < len ? sdot * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[p]);
+    }
+    // chunk max: over the rows of this wave, then over the waves
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = max_xor32(mx);
+    if (kLanes == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
+    if (lane == 0) red[0][wave] = mx;
+    __syncthreads();
+    float m = red[0][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[0][w]);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = r0 + p * kRowsPerPass;
+      const float e = row < len ? __builtin_amdgcn_exp2f(x[p] - m) : 0.f;
+      l += e;
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[p]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x2 vv = unpack2<BF16>(vw[t]);
+        acc[2 * t] = fmaf(e, vv[0], acc[2 * t]);
+        acc[2 * t + 1] = fmaf(e, vv[1], acc[2 * t + 1]);
+      }
+    }
+    // l: the lanes of a row group hold the same e; sum over the row groups of
+    // the wave, then across waves.
+    l += __shfl_xor(l, 16);
+    l = sum_xor32(l);
+    if (kLanes == 8) l += __shfl_xor(l, 8);
+    // column partials: reduce the lanes that share a column chunk
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float a = acc[t];
+      if (kLanes == 8) a += __shfl_xor(a, 8);
+      a += __shfl_xor(a, 16);
+      a = sum_xor32(a);
+      acc[t] = a;
+    }
+    if (lane < kLanes) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) opart[wave][lane * 8 + t] = acc[t];
+    }
+    if (lane == 0) red[1][wave] = l;
+    __syncthreads();
+    if (tid < D) {
+      float lt = 0.f, ot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        lt += red[1][w];
+        ot += opart[w][tid];
+      }
+      const int64_t base = (int64_t)bh * C + c;
+      o_part[base * D + tid] = ot / lt;
+      if (tid == 0) lse_part[base] = (m + log2f(lt)) * kLn2;
+    }
+    __syncthreads();  // opart / red reused by the next item
   }
 }
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeCols = 32;
+constexpr int kMergeCols = 16;                          // d columns per workgroup
+constexpr int kMergeGroups = kMergeThreads / (kMergeCols / 4);  // chunk groups (64)
 
+// One pass over the partials: each thread walks chunks grp, grp + 64, ... of one
+// (batch, head) and 4 consecutive columns, keeping a running max of lse_c (log2
+// units) with the matching rescaled weight sum and weighted output; the 64
+// groups are then combined with the same rule.  O = sum_c 2^(l_c - M) O_c /
+// sum_c 2^(l_c - M) for any reference M equals sum_c w_c O_c.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kMergeThreads)
 void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                       uint16_t* __restrict__ o, float* __restrict__ lse, int C) {
-  constexpr int kGroups = kMergeThreads / kMergeCols;  // chunk groups
-  constexpr int kWaves = kMergeThreads / 64;
-  __shared__ float red[kWaves];
-  __shared__ float part[kGroups][kMergeCols];
+  __shared__ float sm[kMergeGroups], ss[kMergeGroups];
+  __shared__ float sacc[kMergeGroups][kMergeCols + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const int cq = tid & 3, grp = tid >> 2;
   const int bh = blockIdx.x;
-  const int slice = blockIdx.y;
+  const int col0 = blockIdx.y * kMergeCols + cq * 4;
   const float* lp = lse_part + (int64_t)bh * C;
+  const float* op = o_part + (int64_t)bh * C * D + col0;
 
-  // g2 = log2 sum_c exp(lse_c), computed as max + log2 sum 2^(lse2_c - max)
-  float mx = -INFINITY;
-  for (int c = tid; c < C; c += kMergeThreads) mx = fmaxf(mx, lp[c] * kLog2e);
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float gmax = red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) gmax = fmaxf(gmax, red[w]);
-  __syncthreads();
-  float se = 0.f;
-  for (int c = tid; c < C; c += kMergeThreads) se += __builtin_amdgcn_exp2f(lp[c] * kLog2e - gmax);
-  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off);
-  if (lane == 0) red[wave] = se;
-  __syncthreads();
-  float sum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) sum += red[w];
-  const float g2 = gmax + log2f(sum);
-
-  // O[col] = sum_c 2^(lse2_c - g2) * O_c[col]
-  const int col = tid % kMergeCols, grp = tid / kMergeCols;
-  const int dcol = slice * kMergeCols + col;
-  const float* op = o_part + (int64_t)bh * C * D + dcol;
-  float acc = 0.f;
-  for (int c = grp; c < C; c += kGroups)
-    acc = fmaf(__builtin_amdgcn_exp2f(lp[c] * kLog2e - g2), op[(int64_t)c * D], acc);
-  part[grp][col] = acc;
+  float m = -INFINITY, s = 0.f;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 8
+  for (int c = grp; c < C; c += kMergeGroups) {
+    const float l2 = lp[c] * kLog2e;
+    const float4 ov = *reinterpret_cast<const float4*>(op + (int64_t)c * D);
+    const float mn = fmaxf(m, l2);
+    const float r = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first chunk (m = -inf)
+    const float w = __builtin_amdgcn_exp2f(l2 - mn);
+    s = fmaf(s, r, w);
+    a0 = fmaf(a0, r, w * ov.x);
+    a1 = fmaf(a1, r, w * ov.y);
+    a2 = fmaf(a2, r, w * ov.z);
+    a3 = fmaf(a3, r, w * ov.w);
+    m = mn;
+  }
+  if (cq == 0) {
+    sm[grp] = m;
+    ss[grp] = s;
+  }
+  sacc[grp][cq * 4 + 0] = a0;
+  sacc[grp][cq * 4 + 1] = a1;
+  sacc[grp][cq * 4 + 2] = a2;
+  sacc[grp][cq * 4 + 3] = a3;
   __syncthreads();
   if (tid < kMergeCols) {
-    float t = 0.f;
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) t += part[gi][tid];
-    const int d = slice * kMergeCols + tid;
-    uint32_t packed = pack2<BF16>(t, 0.f);
-    o[(int64_t)bh * D + d] = (uint16_t)(packed & 0xffffu);
-    if (slice == 0 && tid == 0 && lse != nullptr) lse[bh] = g2 * kLn2;
+    float M = -INFINITY;
+    for (int gi = 0; gi < kMergeGroups; ++gi) M = fmaxf(M, sm[gi]);
+    float S = 0.f, A = 0.f;
+    for (int gi = 0; gi < kMergeGroups; ++gi) {
+      const float r = (sm[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[gi] - M);
+      S = fmaf(ss[gi], r, S);
+      A = fmaf(sacc[gi][tid], r, A);
+    }
+    const int d = blockIdx.y * kMergeCols + tid;
+    o[(int64_t)bh * D + d] = (uint16_t)(pack2<BF16>(A / S, 0.f) & 0xffffu);
+    if (blockIdx.y == 0 && tid == 0 && lse != nullptr) lse[bh] = (M + log2f(S)) * kLn2;
   }
+}
+
+// Resident workgroups per CU for a kernel, times the CU count (cached per device).
+template <typename K>
+static int resident_grid(K kernel, int threads) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < kMaxDev && cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const int g = cus * per_cu;
+  if (dev < kMaxDev) cache[dev] = g;
+  return g;
 }
 
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                            int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream) {
   const int C = (M + kChunk - 1) / kChunk;
-  const dim3 grid(C, B * Hq);
+  const int n_items = B * Hq * C;
   const float sl2 = scale * kLog2e;
-#define ATTN_DEC_CASE(DD, BB)                                                                         \
-  if (d == DD && bf16 == BB) {                                                                        \
-    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), grid, dim3(kDecThreads), 0, stream,             \
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,  \
-                       Hq, Hkv, M, C, sl2);                                                           \
-    return hipGetLastError();                                                                         \
+#define ATTN_DEC_CASE(DD, BB)                                                                          \
+  if (d == DD && bf16 == BB) {                                                                         \
+    static_assert(DD % 8 == 0, "");                                                                    \
+    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB>, kDecThreads));       \
+    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,        \
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
+                       Hq, Hkv, M, C, n_items, sl2);                                                   \
+    return hipGetLastError();                                                                          \
   }
   ATTN_DEC_CASE(64, false)
   ATTN_DEC_CASE(64, true)

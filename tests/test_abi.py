@@ -104,7 +104,7 @@ def mrg(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=None), -1), (dict(o=None), -1), (dict(C=0), -2), (dict(d=100), -3), (dict(dtype=3), -4),
-    (dict(o=FAKE + 1), -10), (dict(lse=FAKE + 1), -10),
+    (dict(o=FAKE + 1), -10), (dict(lse=FAKE + 1), -10), (dict(op=FAKE + 4), -10),
 ])
 def test_merge_rejects(kw, code):
     assert mrg(**kw) == code
