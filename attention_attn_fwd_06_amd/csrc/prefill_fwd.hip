@@ -208,152 +208,193 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   qk_tile<D, BF16>(s_a, kbuf, qreg, l32, g);
   __syncthreads();  // K buffer 0 is refilled at the end of iteration 0
 
-  // One pipelined step: S(j+1) -> s_next while tile j (s_cur) goes through the
-  // softmax and O += V(j)^T P(j).  Called twice per loop trip with the two S
-  // buffers swapped, so no register copies are needed between tiles.
-  auto step = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
-    const int n0 = j * kBN;
-    const bool load_k = j + 2 < n_tiles;
-    const bool load_v = j + 1 < n_tiles;
-    if (load_k) load_tile_lds<D>(kbuf + (j & 1) * kTE, krs, n0 + 2 * kBN, kv_row_bytes, wave, lane);
-    if (load_v) load_tile_lds<D>(vbuf + ((j + 1) & 1) * kTE, vrs, n0 + kBN, kv_row_bytes, wave, lane);
-
-    // ---- S(j+1): independent of this tile's softmax ----
-    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_next, kbuf + ((j + 1) & 1) * kTE, qreg, l32, g);
-
-    if (j < wave_tiles) {
-      // diagonal tiles and the key tail need a mask; all other tiles take the
-      // select-free path
-      const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
-      if (need_mask) {
+  // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks.
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
+  // the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of group G
+  // addresses V[K0 + s/4][D0 + 4*(s%4)] with D0 = 32*db + 16*(G&1) and K0 =
+  // the first key of the slot run, so lane i gets 4 consecutive keys of column
+  // D0 + i%16 = 32*db + l%32.
+  auto pv_kstep = [&](const uint16_t* Vt, int kb, int st, const s16x8 (&pbq)[kQB], const s16x8* plq) {
+    const int r0 = 32 * kb + 16 * st + 4 * (G >> 1) + (sl >> 2);  // slots 0..3
+    const int r1 = r0 + 8;                                         // slots 4..7
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          const int qi = qw + 32 * qb + l32;
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-              const bool ok = key < M && (!CAUSAL || key <= qi);
-              s_cur[qb][kb][i] = ok ? s_cur[qb][kb][i] : -INFINITY;
-            }
-        }
-      }
-
-      // ---- online softmax (exp2 domain, one query per lane and block) ----
-      float m_tile[kQB];
-      bool grow = false;
+    for (int db = 0; db < kDB; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
+      const int off0 = r0 * D + (((col >> 3) ^ swz<D>(r0)) << 3) + (col & 7);
+      const int off1 = r1 * D + (((col >> 3) ^ swz<D>(r1)) << 3) + (col & 7);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off1));
+      const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[qb][kb][i]);
-        mx = max_xor32(mx);
-        m_tile[qb] = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
-        grow |= m_tile[qb] > m_run[qb] + 8.0f;
+        acc_o[qb][db] = mfma32x32x16<BF16>(a, pbq[qb], acc_o[qb][db]);
+        if (plq != nullptr) acc_o[qb][db] = mfma32x32x16<BF16>(a, plq[qb], acc_o[qb][db]);
       }
-      // Move the reference max only when it grows by more than 2^8; otherwise
-      // p may reach 2^8, which fp32 accumulation and 16-bit P represent fine.
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], m_tile[qb]);
-          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < kDB; ++i) acc_o[qb][i] *= alpha;
-          m_run[qb] = m_new;
-        }
-      }
+    }
+  };
 
-      // ---- P^T operands straight from the accumulator layout ----
-      // k-step (kb, st) uses accumulator elements 8*st .. 8*st+7, i.e. keys
-      // 32*kb + 16*st + 8*(jj/4) + 4*g + jj%4 for slot jj.
-      float p[kQB][kKB][16];
+  // Row max of tile j and the rare move of the reference max (see below).
+  auto row_max_update = [&](f32x16 (&s_cur)[kQB][kKB]) {
+    float m_tile[kQB];
+    bool grow = false;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        float lsum = 0.f;
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float sv = s_cur[qb][kb][i];
-              // masked keys give an exact zero, also when scale == 0
-              const float x = (sv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fmaf(sv, scale_log2, -m_use));
-              p[qb][kb][i] = x;
-              lsum += x;
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float x = __builtin_amdgcn_exp2f(fmaf(s_cur[qb][kb][i], scale_log2, -m_use));
-              p[qb][kb][i] = x;
-              lsum += x;
-            }
-        }
-        l_run[qb] += lsum;
-      }
-      s16x8 pb[kQB][kKB][2];
-      s16x8 pl[kQB][kKB][2];  // bf16, first tile: p - bf16(p), rounded to bf16
-      const bool split_p = BF16 && j == 0;
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const float* pp = &p[qb][kb][8 * st];
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack2<BF16>(pp[2 * e], pp[2 * e + 1]);
-            pb[qb][kb][st] = __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
-            if (split_p) {
-              uint32_t wl[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const f32x2 hv = unpack2<BF16>(w[e]);
-                wl[e] = pack2<BF16>(pp[2 * e] - hv[0], pp[2 * e + 1] - hv[1]);
-              }
-              pl[qb][kb][st] = __builtin_bit_cast(s16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
-            }
-          }
-
-      // ---- O^T += V^T P^T ----
-      // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
-      // of the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of
-      // group G addresses V[K0 + s/4][D0 + 4*(s%4)] with D0 = 32*db + 16*(G&1)
-      // and K0 = first key of the slot run, so lane i gets 4 consecutive keys
-      // of column D0 + i%16 = 32*db + l%32.
-      const uint16_t* Vt = vbuf + (j & 1) * kTE;
+    for (int qb = 0; qb < kQB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = 32 * kb + 16 * st + 4 * (G >> 1) + (sl >> 2);  // slots 0..3
-          const int r1 = r0 + 8;                                         // slots 4..7
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const int col = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
-            const int off0 = r0 * D + (((col >> 3) ^ swz<D>(r0)) << 3) + (col & 7);
-            const int off1 = r1 * D + (((col >> 3) ^ swz<D>(r1)) << 3) + (col & 7);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off0));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off1));
-            const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-              acc_o[qb][db] = mfma32x32x16<BF16>(a, pb[qb][kb][st], acc_o[qb][db]);
-              if (split_p) acc_o[qb][db] = mfma32x32x16<BF16>(a, pl[qb][kb][st], acc_o[qb][db]);
-            }
-          }
-        }
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[qb][kb][i]);
+      mx = max_xor32(mx);
+      m_tile[qb] = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+      grow |= m_tile[qb] > m_run[qb] + 8.0f;
     }
+    // Move the reference max only when it grows by more than 2^8; otherwise
+    // p may reach 2^8, which fp32 accumulation and 16-bit P represent fine.
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], m_tile[qb]);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) acc_o[qb][i] *= alpha;
+        m_run[qb] = m_new;
+      }
+    }
+  };
 
+  // p = 2^(s*scale*log2e - m) for 8 accumulator elements, packed to the PV B
+  // operand; k-step (kb, st) uses accumulator elements 8*st .. 8*st+7, i.e.
+  // keys 32*kb + 16*st + 8*(jj/4) + 4*g + jj%4 for slot jj.  The row sum l is
+  // accumulated from the unrounded fp32 p (a sum of 16-bit-rounded weights
+  // can be off by 2^-9 relative when a few keys dominate, too much for lse).
+  auto exp_pack = [&](const f32x16& sv, int st, float m_use, float& lsum, bool masked, s16x8& pb, s16x8* pl) {
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = sv[8 * st + e];
+      float y = __builtin_amdgcn_exp2f(fmaf(x, scale_log2, -m_use));
+      if (masked) y = (x == -INFINITY) ? 0.f : y;  // exact zero also for scale == 0
+      pv[e] = y;
+      lsum += y;
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
+    pb = __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    if (pl != nullptr) {
+      uint32_t wl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 hv = unpack2<BF16>(w[e]);
+        wl[e] = pack2<BF16>(pv[2 * e] - hv[0], pv[2 * e + 1] - hv[1]);
+      }
+      *pl = __builtin_bit_cast(s16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+    }
+  };
+
+  // General step (first tile, diagonal and tail tiles, last tile of a wave):
+  // S(j+1) -> s_next if this wave needs it, then mask, softmax and PV of tile j.
+  auto step_general = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
+    const int n0 = j * kBN;
+    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_next, kbuf + ((j + 1) & 1) * kTE, qreg, l32, g);
+    if (j >= wave_tiles) return;
+    const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int qi = qw + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool ok = key < M && (!CAUSAL || key <= qi);
+            s_cur[qb][kb][i] = ok ? s_cur[qb][kb][i] : -INFINITY;
+          }
+      }
+    }
+    row_max_update(s_cur);
+    const bool split_p = BF16 && j == 0;  // bf16: hi/lo split of P on the first tile
+    const uint16_t* Vt = vbuf + (j & 1) * kTE;
+    float lsum[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) lsum[qb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s16x8 pb[kQB], pl[kQB];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+          exp_pack(s_cur[qb][kb], st, m_use, lsum[qb], need_mask, pb[qb], split_p ? &pl[qb] : nullptr);
+        }
+        pv_kstep(Vt, kb, st, pb, split_p ? pl : nullptr);
+      }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += lsum[qb];
+  };
+
+  // Steady-state step (no mask, reference max already finite, S(j+1) needed):
+  // after the row max, the QK MFMAs of tile j+1, the exp/pack VALU work of
+  // tile j and its PV MFMAs form one basic block, and the scheduler is asked
+  // to interleave them (each MFMA followed by the next LDS read, 2-4 VALU and,
+  // during the QK half, 2 exp2) so that the matrix core and the VALU run at the
+  // same time and every LDS read is issued one MFMA ahead of its use.
+  auto step_fast = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
+    row_max_update(s_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_tile<D, BF16>(s_next, kbuf + ((j + 1) & 1) * kTE, qreg, l32, g);
+    const uint16_t* Vt = vbuf + (j & 1) * kTE;
+    float lsum[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) lsum[qb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s16x8 pb[kQB];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) exp_pack(s_cur[qb][kb], st, m_run[qb], lsum[qb], false, pb[qb], nullptr);
+        pv_kstep(Vt, kb, st, pb, nullptr);
+      }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += lsum[qb];
+    // QK: kDT*kKB LDS reads, kDT*kKB*kQB MFMAs; PV: 2*kDB*2*kKB tr reads,
+    // kDB*2*kKB*kQB MFMAs; about 4 VALU per MFMA overall.
+    constexpr int kMfmaQK = kDT * kKB * kQB, kMfmaPV = kDB * 2 * kKB * kQB;
+    // Per MFMA: the QK half also takes one K-fragment read (kLead reads ahead),
+    // kQkValu VALU and kQkTrans exp2; the PV half takes its two transposed V
+    // reads and kPvValu VALU.  d = 64 has twice the softmax work per MFMA.
+    constexpr int kLead = 6;
+    constexpr int kQkValu = D == 128 ? 2 : 6, kQkTrans = D == 128 ? 1 : 2, kPvValu = D == 128 ? 4 : 6;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS reads ahead
+#pragma unroll
+    for (int i = 0; i < kMfmaQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, kQkValu, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x400, kQkTrans, 0);  // exp2
+    }
+#pragma unroll
+    for (int i = 0; i < kMfmaPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, kPvValu, 0);   // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto step = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
+    const int n0 = j * kBN;
+    if (j + 2 < n_tiles) load_tile_lds<D>(kbuf + (j & 1) * kTE, krs, n0 + 2 * kBN, kv_row_bytes, wave, lane);
+    if (j + 1 < n_tiles) load_tile_lds<D>(vbuf + ((j + 1) & 1) * kTE, vrs, n0 + kBN, kv_row_bytes, wave, lane);
+    const bool fast = j >= 1 && j + 1 < wave_tiles && !(CAUSAL && n0 + kBN - 1 > qw) && n0 + kBN <= M;
+    if (fast)
+      step_fast(j, s_cur, s_next);
+    else
+      step_general(j, s_cur, s_next);
     wait_tile_loads();
     __syncthreads();
   };

@@ -11,7 +11,7 @@ Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 duration, measured with HIP events on the launch stream; the decode result is
 reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--prewarm-s 1.5] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -100,7 +100,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-s", type=float, default=1.5,
+                    help="seconds of untimed steps before the counted warm-up (clock ramp)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
@@ -162,6 +164,14 @@ def main():
             attn.lse_merge(o_part, lse_part, o=do_, lse=dlse, stream=stream)
             if ev: ev[4].record(stream)
 
+    # The GPU reaches its sustained clock only after about a second of load:
+    # run untimed steps for --prewarm-s seconds, then the counted warm-up.
+    t_pre = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        step(i)
+        torch.cuda.synchronize()
+        i += 1
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
