@@ -6,10 +6,9 @@
 // section 2: GQA head map and top-left causal tile skipping).
 //
 // MI355X design (not the page's CUDA design):
-//  * one workgroup = 4 waves, one wave per SIMD (up to 512 VGPRs incl. AGPRs);
-//    each wave owns 64 queries (two 32-query blocks) of one (batch, query
-//    head) for the whole KV loop, so BM = 256 queries per workgroup and every
-//    K/V fragment read from LDS feeds two MFMAs.
+//  * one workgroup = 8 waves, two per SIMD (256 VGPRs each); each wave owns
+//    32 queries of one (batch, query head) for the whole KV loop, so BM = 256
+//    queries share every K/V tile fetched into LDS (one workgroup per CU).
 //  * both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 //    accumulators, transposed so that one lane owns one query per block:
 //      S^T[key][query] = K Q^T   (A = K rows from LDS, B = Q^T kept in VGPRs)
@@ -45,10 +44,11 @@ namespace attn {
 constexpr int kQB = 1;             // 32-query blocks per wave
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr int kWavesPerEU = 2;     // waves per SIMD
+constexpr int kWaves = 8;          // waves per workgroup
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
-constexpr int kThreads = 256;      // 4 waves of 64
+constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32 * kQB;      // queries per wave
-constexpr int kBM = 4 * kQW;       // queries per workgroup
+constexpr int kBM = kWaves * kQW;  // queries per workgroup
 
 // 16-byte chunk swizzle: physical chunk = logical chunk ^ swz<D>(row).  The
 // LDS serves 256 bytes (64 banks) per cycle: 16 lanes of a ds_read_b128 or 32
@@ -97,9 +97,10 @@ __device__ __forceinline__ void load_tile_lds(uint16_t* lds_tile, __amdgpu_buffe
                                               int row_stride_bytes, int wave, int lane) {
   constexpr int kU = D / 8;                     // 16-byte units per row
   constexpr int kInst = kBN * kU / kThreads;    // instructions per thread
+  static_assert(kBN * kU % kThreads == 0, "tile must split evenly over the workgroup");
 #pragma unroll
   for (int i = 0; i < kInst; ++i) {
-    const int base = (i * 4 + wave) * 64;        // first unit written by this instruction
+    const int base = (i * kWaves + wave) * 64;   // first unit written by this instruction
     const int P = base + lane;
     const int row = P / kU, pc = P % kU;
     const int c = pc ^ swz<D>(row);
@@ -367,7 +368,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // Per MFMA: the QK half also takes one K-fragment read (kLead reads ahead),
     // kQkValu VALU and kQkTrans exp2; the PV half takes its two transposed V
     // reads and kPvValu VALU.  d = 64 has twice the softmax work per MFMA.
-    constexpr int kLead = 6;
+    constexpr int kLead = 4;
     constexpr int kQkValu = D == 128 ? 2 : 6, kQkTrans = D == 128 ? 1 : 2, kPvValu = D == 128 ? 4 : 6;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS reads ahead
 #pragma unroll
