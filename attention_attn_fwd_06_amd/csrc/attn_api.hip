@@ -61,7 +61,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (causal && N != M) return ATTN_ERR_CAUSAL_SHAPE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
-  if ((int64_t)B * N * Hq * d >= kMaxElems || (int64_t)B * (M + 64) * Hkv * d >= kMaxElems ||
+  if ((int64_t)B * (N + 256) * Hq * d >= kMaxElems || (int64_t)B * (M + 64) * Hkv * d >= kMaxElems ||
       (int64_t)B * Hq * ((N + 127) / 128) >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||

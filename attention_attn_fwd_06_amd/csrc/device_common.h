@@ -58,6 +58,14 @@ __device__ __forceinline__ f32x2 unpack2(uint32_t u) {
   }
 }
 
+// x, hidden from the optimiser: values computed from the result inside a loop
+// cannot be hoisted out of it, so a loop-invariant per-lane base plus several
+// per-iteration offsets costs one register instead of one per offset.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Value held by lane l ^ 32 (one v_permlane32_swap).
 __device__ __forceinline__ float xor32(float x) {
   int xi = __float_as_int(x);

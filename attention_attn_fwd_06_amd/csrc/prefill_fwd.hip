@@ -22,7 +22,9 @@
 //    MFMAs of S(j+1) = K(j+1) Q^T, which do not depend on the softmax of tile
 //    j, so the in-order issue interleaves them with the softmax VALU work;
 //    then O += V(j)^T P(j).  K(j+2) and V(j+1) are fetched straight into LDS
-//    (buffer_load ... lds, no staging registers) during the iteration.
+//    (buffer_load ... lds, no staging registers) during the iteration; in the
+//    steady state the fetch instructions are spread over the QK MFMAs rather
+//    than issued back to back, so no wave stalls on a full load queue.
 //  * K and V tiles (BN = 64 keys) are double-buffered in LDS, row-major with a
 //    16-byte-chunk XOR swizzle that keeps both the K row reads and the
 //    transposed V reads free of bank conflicts; tile rows past M come back as
@@ -37,18 +39,18 @@
 //    queries all precede a tile skips its math; only diagonal tiles are
 //    masked.  Grid: longest causal q-tiles first, heads of one GQA group
 //    adjacent, and an XCD-aware remap so heads sharing K/V share an L2.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace attn {
 
-constexpr int kQB = 1;             // 32-query blocks per wave
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr int kWavesPerEU = 2;     // waves per SIMD
 constexpr int kWaves = 8;          // waves per workgroup
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQW = 32 * kQB;      // queries per wave
-constexpr int kBM = kWaves * kQW;  // queries per workgroup
+constexpr int kBM = kWaves * 32;   // queries per workgroup (32 per wave)
 
 // 16-byte chunk swizzle: physical chunk = logical chunk ^ swz<D>(row).  The
 // LDS serves 256 bytes (64 banks) per cycle: 16 lanes of a ds_read_b128 or 32
@@ -68,67 +70,125 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <int D>
-struct TileCfg {
-  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
-  static constexpr int kTileElems = kBN * D;              // one K or V tile
-  static constexpr int kLoads = kBN * kChunks / kThreads;  // 16-byte loads per thread per tile
-};
-
-// Buffer resource over one (batch, kv head) slice of K or V: rows past M read
-// as zero.  gfx9 descriptor word 3.  The host guarantees (M + 64) rows of the
-// slice stay below 2^32 bytes, so offsets of rows past M never wrap around.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t row_stride, int M,
-                                                            int D) {
+// Buffer descriptor over one (batch, kv head) slice of K or V: base address,
+// stride 0 (raw buffer), size in bytes, gfx9 word 3.  Offsets at or past the
+// size read as zero, so rows past M come back as zeros.  The host guarantees
+// (M + 64) rows of the slice stay below 2^32 bytes, so the per-lane offsets of
+// rows past M never wrap around.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_desc(const uint16_t* base, int64_t row_stride, int M, int D) {
   const int64_t bytes = ((int64_t)(M - 1) * row_stride + D) * 2;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  return (i32x4){(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// One buffer_load_dwordx4 ... lds: lane L's 16 bytes at byte offset voff of the
+// buffer go to LDS byte address lds + 16 * L (M0 holds lds).  Inline asm, so
+// that the compiler does not see an LDS write: it would otherwise wait for
+// every outstanding tile fetch (vmcnt(0)) before the next LDS read.  Each tile
+// is instead waited for explicitly (vmcnt) by the fetching wave before the
+// barrier that publishes it.  s_nop: one wait state between the M0 write and
+// its use.  M0 is listed as clobbered (nothing else in these kernels keeps a
+// value in M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-// Global -> LDS without registers: each buffer_load_dwordx4 ... lds writes the
-// 16 bytes of lane L at M0 + 16 * L, so a wave fills 64 consecutive 16-byte
-// units of the swizzled tile per instruction and picks, per lane, the global
-// chunk that belongs at that unit (physical chunk pc of row r holds logical
-// chunk pc ^ swz<D>(r)).  Rows past M come back as zeros.  Completion is tracked
-// by vmcnt; the caller waits before the barrier that publishes the tile.
+// Global -> LDS without registers: each fetch instruction writes 64
+// consecutive 16-byte units of the swizzled tile, lane L picking the global
+// chunk that belongs at unit L (physical chunk pc of row r holds logical chunk
+// pc ^ swz<D>(r)).  Instruction i of wave w covers units (i*kWaves + w)*64 ..
+// +63, i.e. rows kRowsPerInst*i + (w*64 + L)/kU; the row-in-instruction part
+// and the chunk are per-lane constants (voff_lane below), since kRowsPerInst
+// is a multiple of the swizzle period (16 rows).
 template <int D>
-__device__ __forceinline__ void load_tile_lds(uint16_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc, int n0,
-                                              int row_stride_bytes, int wave, int lane) {
-  constexpr int kU = D / 8;                     // 16-byte units per row
-  constexpr int kInst = kBN * kU / kThreads;    // instructions per thread
+struct Fetch {
+  static constexpr int kU = D / 8;                          // 16-byte units per row
+  static constexpr int kInst = kBN * kU / kThreads;         // instructions per wave per tile
+  static constexpr int kRowsPerInst = kWaves * 64 / kU;     // rows covered by one instruction index
+  static constexpr uint32_t kInstBytes = 64 * 16;           // LDS bytes written per instruction
   static_assert(kBN * kU % kThreads == 0, "tile must split evenly over the workgroup");
-#pragma unroll
-  for (int i = 0; i < kInst; ++i) {
-    const int base = (i * kWaves + wave) * 64;   // first unit written by this instruction
-    const int P = base + lane;
-    const int row = P / kU, pc = P % kU;
-    const int c = pc ^ swz<D>(row);
-    const uint32_t off = (uint32_t)(n0 + row) * (uint32_t)row_stride_bytes + (uint32_t)(c * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + base * 8), 16, (int)off, 0, 0, 0);
+  static_assert(kInst == 1 || kRowsPerInst % 16 == 0, "swizzle must repeat across instructions");
+  // per-lane byte offset of instruction 0 relative to the tile's first row
+  static __device__ __forceinline__ uint32_t voff_lane(int wave, int lane, int row_stride_bytes) {
+    const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
+    return (uint32_t)rl * (uint32_t)row_stride_bytes + (uint32_t)((pc ^ swz<D>(rl)) * 16);
   }
-}
+  // instruction i of the tile starting at key row n0, into the LDS tile at lds_tile
+  static __device__ __forceinline__ void issue(i32x4 desc, uint32_t lds_tile, int n0, int i, int wave,
+                                               uint32_t voff, int row_stride_bytes) {
+    dma16(desc, lds_tile + (uint32_t)(i * kWaves + wave) * kInstBytes,
+          voff + (uint32_t)(n0 + kRowsPerInst * i) * (uint32_t)row_stride_bytes);
+  }
+  static __device__ __forceinline__ void tile(i32x4 desc, uint32_t lds_tile, int n0, int wave, uint32_t voff,
+                                              int row_stride_bytes) {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) issue(desc, lds_tile, n0, i, wave, voff, row_stride_bytes);
+  }
+};
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// S^T[qb][kb] = K(tile) Q^T for the wave's two query blocks.
+// Workgroup barrier: this wave's LDS reads are complete (lgkmcnt(0)) so the
+// buffers they read can be refilled after it.  The asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void kv_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS access through 32-bit byte addresses; constant parts of an address
+// (tile, 32-key block, k-step) become the instruction's offset field.
+typedef __attribute__((address_space(3))) s16x8 lds_s16x8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ s16x8 lds_read_b128(uint32_t addr) { return *(const lds_s16x8*)(uintptr_t)addr; }
+__device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+}
+
+// Per-lane LDS addressing of the two MFMA operands that come from LDS.
+//  K (A operand of S^T = K Q^T): lane l reads row 32*kb + l%32, logical chunk
+//    2t + l/32 of contraction step t.  swz of that row equals swz(l%32), and
+//    (2t + g) ^ s = 2t ^ (g ^ s), so the byte offset within the row is
+//    32t ^ kx with kx = 16 * (g ^ swz(l%32)).
+//  V (A operand of O^T += V^T P^T, ds_read_b64_tr_b16): see pv_kstep.  For
+//    k-step (kb, st) the rows are 32*kb + 16*st + rb (+ 8), and swz only sees
+//    the low four row bits, so kb and st are constant offsets and each lane
+//    needs one address per (32-column block of O^T, row half).
+template <int D>
+struct LdsAddr {
+  uint32_t k_row;       // lds base + (l%32) * row bytes
+  uint32_t kx;          // 16 * (g ^ swz(l%32))
+  uint32_t v[D / 32][2];  // lds base + V row/chunk offset for (d block, row half)
+};
+
+// S^T[kb] = K(tile) Q^T for the wave's 32 queries (first tile, diagonal and
+// tail tiles).  The Q^T operand of contraction step t is lane l's 16 bytes at
+// q_lane + 1024 t (see the Q^T layout in the kernel).
 template <int D, bool BF16>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[kQB][kKB], const uint16_t* Kt, const s16x8 (&qreg)[kQB][D / 16],
-                                        int l32, int g) {
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint32_t k_row, uint32_t kx,
+                                        uint32_t q_lane) {
   constexpr int kDT = D / 16;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
+  for (int kb = 0; kb < kKB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) s[qb][kb] = (f32x16){};
-#pragma unroll
-  for (int t = 0; t < kDT; ++t)
+  for (int t = 0; t < kDT; ++t) {
+    // k_row + (32t ^ kx): k_row is a multiple of 128 and 32t ^ kx < 128 * D / 64
+    const uint32_t row_t = k_row + ((uint32_t)(32 * t) ^ kx);
+    const s16x8 bq = lds_read_b128(q_lane + (uint32_t)(1024 * t));
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
-      const int row = 32 * kb + l32;
-      const s16x8 a = *reinterpret_cast<const s16x8*>(Kt + row * D + (((2 * t + g) ^ swz<D>(row)) << 3));
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[qb][kb] = mfma32x32x16<BF16>(a, qreg[qb][t], s[qb][kb]);
+      const s16x8 a = lds_read_b128(row_t + k_tile + (uint32_t)(kb * 32 * D * 2));
+      s[kb] = mfma32x32x16<BF16>(a, bq, s[kb]);
     }
+  }
 }
 
 template <int D, bool BF16, bool CAUSAL>
@@ -139,11 +199,18 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                         int n_qtiles, int total, float scale_log2) {
   constexpr int kDT = D / 16;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
-  constexpr int kTE = TileCfg<D>::kTileElems;
-  // LDS: K buffers 0, 1 then V buffers 0, 1
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTE];
+  constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
+  using F = Fetch<D>;
+  // LDS: K buffers 0, 1, V buffers 0, 1, then the Q^T operands of the 8 waves
+  // (kDT KB each: contraction step t of wave w holds lane l's 16 bytes at
+  // 1024 (w kDT + t) + 16 l, so every Q^T read is one conflict-free
+  // ds_read_b128 and Q takes no registers during the KV loop).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * kBN * D + kWaves * kDT * 512];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u16*)smem;
+  const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTB, qbuf0 = lds0 + 4 * kTB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int G = lane >> 4, sl = lane & 15;
 
@@ -158,109 +225,103 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int h = kvh * group + hg;
 
   const int q_start = qt * kBM;
-  const int qw = q_start + wave * kQW;  // first query of this wave
-  const int qlast = qw + kQW - 1;       // last query of this wave
+  const int qw = q_start + wave * 32;  // first query of this wave
+  const int qlast = qw + 31;           // last query of this wave
+  const int qi = qw + l32;             // this lane's query
 
   const int64_t q_row_stride = (int64_t)Hq * D;
   const int64_t kv_row_stride = (int64_t)Hkv * D;
   const int kv_row_bytes = (int)(kv_row_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
+  const i32x4 kdesc = make_desc(k + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
+  const i32x4 vdesc = make_desc(v + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
+  const uint32_t voff = F::voff_lane(wave, lane, kv_row_bytes);
 
-  // ---- Q^T operands: 16 bytes per contraction step and query block ----
-  s16x8 qreg[kQB][kDT];
+  // ---- per-lane LDS operand addresses ----
+  LdsAddr<D> la;
+  la.k_row = lds0 + (uint32_t)l32 * D * 2;
+  la.kx = (uint32_t)((g ^ swz<D>(l32)) << 4);
+  {
+    // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
+    // of the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of
+    // group G addresses V[K0 + s/4][D0 + 4*(s%4)] with D0 = 32*db + 16*(G&1)
+    // and K0 the first key of the slot run, so lane i gets 4 consecutive keys
+    // of column D0 + i%16 = 32*db + l%32.  Rows: rb = 4*(G/2) + s/4 for slots
+    // 0..3 and rb + 8 for slots 4..7.
+    const int rb = 4 * (G >> 1) + (sl >> 2);
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qi = qw + 32 * qb + l32;
-    const uint16_t* qp = q + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D + 8 * g;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = rb + 8 * hh;
 #pragma unroll
-    for (int t = 0; t < kDT; ++t) {
-      uint4 u = (qi < N) ? *reinterpret_cast<const uint4*>(qp + 16 * t) : make_uint4(0, 0, 0, 0);
-      qreg[qb][t] = __builtin_bit_cast(s16x8, u);
+      for (int db = 0; db < kDB; ++db) {
+        const int col = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
+        la.v[db][hh] = vbuf0 + (uint32_t)(row * D * 2 + ((((col >> 3) ^ swz<D>(row)) << 4) | ((col & 7) * 2)));
+      }
     }
   }
 
-  f32x16 acc_o[kQB][kDB];
-  float m_run[kQB];  // running max of scale*log2e*s
-  float l_run[kQB];  // running sum over this lane's keys
+  // ---- Q^T operand: lane l of step t needs Q[qw + l%32][16t + 8g .. +7] ----
+  const uint32_t q_lane = qbuf0 + (uint32_t)(wave * kDT) * 1024u + (uint32_t)lane * 16u;
+
+  f32x16 acc_o[kDB];
+  float m_run = -INFINITY;  // running max of scale*log2e*s (the reference max)
+  float l_run = 0.f;        // running sum over this lane's keys
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kDB; ++i) acc_o[qb][i] = (f32x16){};
-  }
+  for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
 
   const int kv_end = CAUSAL ? min(M, q_start + kBM) : M;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // last tile that holds a key <= some query of this wave
   const int wave_tiles = CAUSAL ? min(n_tiles, qlast / kBN + 1) : n_tiles;
 
-  uint16_t* const kbuf = smem;
-  uint16_t* const vbuf = smem + 2 * kTE;
-
-  // ---- prologue: K(0), V(0), K(1) to LDS; S(0) ----
-  load_tile_lds<D>(kbuf, krs, 0, kv_row_bytes, wave, lane);
-  load_tile_lds<D>(vbuf, vrs, 0, kv_row_bytes, wave, lane);
-  if (n_tiles > 1) load_tile_lds<D>(kbuf + kTE, krs, kBN, kv_row_bytes, wave, lane);
+  // ---- prologue: Q^T, K(0), V(0), K(1) to LDS; S(0) ----
+  {
+    // rows past N read as zero; the host keeps (N + kBM) rows below 2^32 bytes
+    const i32x4 qdesc = make_desc(q + ((int64_t)b * N * Hq + h) * D, q_row_stride, N, D);
+    const uint32_t qv = (uint32_t)qi * (uint32_t)(q_row_stride * 2) + 16u * (uint32_t)g;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t) dma16(qdesc, qbuf0 + (uint32_t)(wave * kDT + t) * 1024u, qv + 32u * t);
+  }
+  F::tile(kdesc, kbuf0, 0, wave, voff, kv_row_bytes);
+  F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
+  if (n_tiles > 1) F::tile(kdesc, kbuf0 + kTB, kBN, wave, voff, kv_row_bytes);
   wait_tile_loads();
-  __syncthreads();
-  f32x16 s_a[kQB][kKB], s_b[kQB][kKB];
-  qk_tile<D, BF16>(s_a, kbuf, qreg, l32, g);
-  __syncthreads();  // K buffer 0 is refilled at the end of iteration 0
+  kv_barrier();
+  f32x16 s_a[kKB], s_b[kKB];  // S of the current tile is always in s_a between steps
+  qk_tile<D, BF16>(s_a, 0, la.k_row, la.kx, q_lane);
+  kv_barrier();  // K buffer 0 is refilled in iteration 0
 
-  // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks.
-  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
-  // the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of group G
-  // addresses V[K0 + s/4][D0 + 4*(s%4)] with D0 = 32*db + 16*(G&1) and K0 =
-  // the first key of the slot run, so lane i gets 4 consecutive keys of column
-  // D0 + i%16 = 32*db + l%32.
-  auto pv_kstep = [&](const uint16_t* Vt, int kb, int st, const s16x8 (&pbq)[kQB], const s16x8* plq) {
-    const int r0 = 32 * kb + 16 * st + 4 * (G >> 1) + (sl >> 2);  // slots 0..3
-    const int r1 = r0 + 8;                                         // slots 4..7
+  // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks; v_tile
+  // is the V buffer's offset from V buffer 0.
+  auto pv_kstep = [&](uint32_t v_tile, int kb, int st, const s16x8& pb, const s16x8* pl) {
+    const uint32_t koff = v_tile + (uint32_t)((32 * kb + 16 * st) * D * 2);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      const int col = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
-      const int off0 = r0 * D + (((col >> 3) ^ swz<D>(r0)) << 3) + (col & 7);
-      const int off1 = r1 * D + (((col >> 3) ^ swz<D>(r1)) << 3) + (col & 7);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off1));
+      const s16x4 lo = lds_read_tr16_b64(la.v[db][0] + koff);
+      const s16x4 hi = lds_read_tr16_b64(la.v[db][1] + koff);
       const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        acc_o[qb][db] = mfma32x32x16<BF16>(a, pbq[qb], acc_o[qb][db]);
-        if (plq != nullptr) acc_o[qb][db] = mfma32x32x16<BF16>(a, plq[qb], acc_o[qb][db]);
-      }
+      acc_o[db] = mfma32x32x16<BF16>(a, pb, acc_o[db]);
+      if (pl != nullptr) acc_o[db] = mfma32x32x16<BF16>(a, *pl, acc_o[db]);
     }
   };
 
   // Row max of tile j and the rare move of the reference max (see below).
-  auto row_max_update = [&](f32x16 (&s_cur)[kQB][kKB]) {
-    float m_tile[kQB];
-    bool grow = false;
+  auto row_max_update = [&](f32x16 (&s_cur)[kKB]) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[qb][kb][i]);
-      mx = max_xor32(mx);
-      m_tile[qb] = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
-      grow |= m_tile[qb] > m_run[qb] + 8.0f;
-    }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+    mx = max_xor32(mx);
+    const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
     // Move the reference max only when it grows by more than 2^8; otherwise
     // p may reach 2^8, which fp32 accumulation and 16-bit P represent fine.
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], m_tile[qb]);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) acc_o[qb][i] *= alpha;
-        m_run[qb] = m_new;
-      }
+      for (int i = 0; i < kDB; ++i) acc_o[i] *= alpha;
+      m_run = m_new;
     }
   };
 
@@ -295,136 +356,217 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   };
 
   // General step (first tile, diagonal and tail tiles, last tile of a wave):
-  // S(j+1) -> s_next if this wave needs it, then mask, softmax and PV of tile j.
-  auto step_general = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
+  // fetches K(j+2) and V(j+1), computes S(j+1) into s_b if this wave needs it,
+  // then mask, softmax and PV of tile j from s_a; ends with S(j+1) in s_a.  The
+  // buffer parity is a run-time value here (these steps are few).
+  auto step_general = [&](const int j, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
+    // bf16: P is split into hi + lo parts on the first tile
+    constexpr bool kSplit = BF16 && kFirst;
+    const uint32_t par = (uint32_t)(j & 1);
+    const uint32_t k_next = (1 - par) * kTB, v_cur = par * kTB;
     const int n0 = j * kBN;
-    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_next, kbuf + ((j + 1) & 1) * kTE, qreg, l32, g);
-    if (j >= wave_tiles) return;
-    const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = qw + 32 * qb + l32;
+    if (j + 2 < n_tiles) F::tile(kdesc, kbuf0 + par * kTB, n0 + 2 * kBN, wave, voff, kv_row_bytes);
+    if (j + 1 < n_tiles) F::tile(vdesc, vbuf0 + (1 - par) * kTB, n0 + kBN, wave, voff, kv_row_bytes);
+    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_b, k_next, la.k_row, opaque(la.kx), q_lane);
+    if (j < wave_tiles) {
+      const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
             const bool ok = key < M && (!CAUSAL || key <= qi);
-            s_cur[qb][kb][i] = ok ? s_cur[qb][kb][i] : -INFINITY;
+            s_a[kb][i] = ok ? s_a[kb][i] : -INFINITY;
           }
       }
-    }
-    row_max_update(s_cur);
-    const bool split_p = BF16 && j == 0;  // bf16: hi/lo split of P on the first tile
-    const uint16_t* Vt = vbuf + (j & 1) * kTE;
-    float lsum[kQB];
+      row_max_update(s_a);
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float lsum = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) lsum[qb] = 0.f;
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s16x8 pb[kQB], pl[kQB];
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-          exp_pack(s_cur[qb][kb], st, m_use, lsum[qb], need_mask, pb[qb], split_p ? &pl[qb] : nullptr);
+        for (int st = 0; st < 2; ++st) {
+          s16x8 pb, pl;
+          exp_pack(s_a[kb], st, m_use, lsum, need_mask, pb, kSplit ? &pl : nullptr);
+          pv_kstep(v_cur, kb, st, pb, kSplit ? &pl : nullptr);
         }
-        pv_kstep(Vt, kb, st, pb, split_p ? pl : nullptr);
-      }
+      l_run += lsum;
+    }
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += lsum[qb];
+    for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+    wait_tile_loads();
+    kv_barrier();
   };
 
-  // Steady-state step (no mask, reference max already finite, S(j+1) needed):
-  // after the row max, the QK MFMAs of tile j+1, the exp/pack VALU work of
-  // tile j and its PV MFMAs form one basic block, and the scheduler is asked
-  // to interleave them (each MFMA followed by the next LDS read, 2-4 VALU and,
-  // during the QK half, 2 exp2) so that the matrix core and the VALU run at the
-  // same time and every LDS read is issued one MFMA ahead of its use.
-  auto step_fast = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
-    row_max_update(s_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    qk_tile<D, BF16>(s_next, kbuf + ((j + 1) & 1) * kTE, qreg, l32, g);
-    const uint16_t* Vt = vbuf + (j & 1) * kTE;
-    float lsum[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) lsum[qb] = 0.f;
+  // Raw row max of a tile's S (unscaled, over this lane and lane ^ 32).
+  auto tile_max = [&](const f32x16 (&sv)[kKB]) {
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s16x8 pb[kQB];
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+    return max_xor32(mx);
+  };
+
+  // Steady-state step (no mask, reference max finite, S(j+1) needed), written
+  // as an explicit software pipeline of kN slots, one MFMA each: the 2 kDT QK
+  // MFMAs of S(j+1) = K(j+1) Q^T, then the 4 kDB PV MFMAs of O^T += V(j)^T P(j)
+  // (k-step ks = 2 kb + st, d block db).  Slot i issues MFMA i, the LDS reads
+  // of MFMA i + kL, a share of the exp/pack work of tile j (each P k-step is
+  // complete before its first PV MFMA), in its first odd slots one of the
+  // step's tile fetches, and in the last slots the row max of S(j+1) (whose
+  // MFMAs have finished by then), which the next step uses.  The slots are
+  // separated by scheduling fences, so the order is the one written here.
+  // mx: row max of tile j on entry, of tile j+1 on return.
+  auto step_fast = [&](const uint32_t k_next, const uint32_t v_cur, f32x16 (&s_cur)[kKB],
+                       f32x16 (&s_next)[kKB], float& mx, auto&& fetch) {
+    {
+      const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) exp_pack(s_cur[qb][kb], st, m_run[qb], lsum[qb], false, pb[qb], nullptr);
-        pv_kstep(Vt, kb, st, pb, nullptr);
+        for (int i = 0; i < kDB; ++i) acc_o[i] *= alpha;
+        m_run = m_new;
       }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += lsum[qb];
-    // QK: kDT*kKB LDS reads, kDT*kKB*kQB MFMAs; PV: 2*kDB*2*kKB tr reads,
-    // kDB*2*kKB*kQB MFMAs; about 4 VALU per MFMA overall.
-    constexpr int kMfmaQK = kDT * kKB * kQB, kMfmaPV = kDB * 2 * kKB * kQB;
-    // Per MFMA: the QK half also takes one K-fragment read (kLead reads ahead),
-    // kQkValu VALU and kQkTrans exp2; the PV half takes its two transposed V
-    // reads and kPvValu VALU.  d = 64 has twice the softmax work per MFMA.
-    constexpr int kLead = 4;
-    constexpr int kQkValu = D == 128 ? 2 : 6, kQkTrans = D == 128 ? 1 : 2, kPvValu = D == 128 ? 4 : 6;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS reads ahead
-#pragma unroll
-    for (int i = 0; i < kMfmaQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, kQkValu, 0);   // VALU
-      __builtin_amdgcn_sched_group_barrier(0x400, kQkTrans, 0);  // exp2
     }
+    // a fresh copy per step keeps the per-step K addresses from being hoisted
+    // out of the KV loop as kDT live registers
+    const uint32_t kx = opaque(la.kx);
+    constexpr int kNQ = 2 * kDT, kNP = 4 * kDB, kN = kNQ + kNP;
+    constexpr int kL = 4;                  // MFMAs whose operands are read ahead
+    constexpr int kNF = 2 * F::kInst;      // tile fetch instructions per step
+    constexpr int kExpEnd = kNQ + 3 * kDB;  // first PV MFMA of the last k-step
+    static_assert(kNQ >= 2 * kNF, "fetch slots");
+    s16x8 qv[kDT], ka[kNQ], va[kNP], pb[4];
+    float pe[4][8];
+    float lsum = 0.f, mxn = -INFINITY;
+    const float neg_m = -m_run;
+
+    auto reads = [&](const int i) {
+      if (i < kNQ) {
+        const int t = i >> 1, kb = i & 1;
+        if (kb == 0) qv[t] = lds_read_b128(q_lane + 1024u * (uint32_t)t);
+        const uint32_t row_t = la.k_row + ((uint32_t)(32 * t) ^ kx);
+        ka[i] = lds_read_b128(row_t + k_next + (uint32_t)(kb * 32 * D * 2));
+      } else if (i < kN) {
+        const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
+        const uint32_t koff = v_cur + (uint32_t)(16 * ks * D * 2);  // keys 16 ks .. 16 ks + 15
+        const s16x4 lo = lds_read_tr16_b64(la.v[db][0] + koff);
+        const s16x4 hi = lds_read_tr16_b64(la.v[db][1] + koff);
+        va[pi] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    // element e of P k-step ks (see exp_pack for the key order)
+    auto exp_elem = [&](const int k) {
+      const int ks = k >> 3, e = k & 7;
+      const float y = __builtin_amdgcn_exp2f(fmaf(s_cur[ks >> 1][8 * (ks & 1) + e], scale_log2, neg_m));
+      pe[ks][e] = y;
+      lsum += y;
+      if (e == 7) {
+        uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < kMfmaPV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, kPvValu, 0);   // VALU
+        for (int u = 0; u < 4; ++u) w[u] = pack2<BF16>(pe[ks][2 * u], pe[ks][2 * u + 1]);
+        pb[ks] = __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    };
+
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kL; ++i) reads(i);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < kNQ) {
+        const int t = i >> 1, kb = i & 1;
+        s_next[kb] = mfma32x32x16<BF16>(ka[i], qv[t], t == 0 ? (f32x16){} : s_next[kb]);
+      } else {
+        const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
+        acc_o[db] = mfma32x32x16<BF16>(va[pi], pb[ks], acc_o[db]);
+      }
+      reads(i + kL);
+      if ((i & 1) && (i >> 1) < kNF) fetch(i >> 1);
+      // elements k with floor(k * kExpEnd / 32) == i
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        if (k * kExpEnd / 32 == i) exp_elem(k);
+      if (i >= kExpEnd) {
+        // row max of S(j+1), spread over the slots after the exp work
+        constexpr int kMaxSlots = kN - kExpEnd;
+        const int r = i - kExpEnd;
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if (k * kMaxSlots / 32 == r) mxn = fmaxf(mxn, s_next[k >> 4][k & 15]);
+        if (i == kN - 1) mx = max_xor32(mxn);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
+    l_run += lsum;
   };
 
-  auto step = [&](const int j, f32x16 (&s_cur)[kQB][kKB], f32x16 (&s_next)[kQB][kKB]) {
+  // One steady-state iteration; P is the parity of j (buffers alternate
+  // between tiles): S(j+1) reads K buffer 1-P, PV(j) reads V buffer P, and the
+  // iteration fetches K(j+2) into K buffer P and V(j+1) into V buffer 1-P.
+  auto step_fast_p = [&](const int j, f32x16 (&s_cur)[kKB], f32x16 (&s_next)[kKB], float& mx, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const uint32_t k_fill = kbuf0 + P * kTB, v_fill = vbuf0 + (1 - P) * kTB;
     const int n0 = j * kBN;
-    if (j + 2 < n_tiles) load_tile_lds<D>(kbuf + (j & 1) * kTE, krs, n0 + 2 * kBN, kv_row_bytes, wave, lane);
-    if (j + 1 < n_tiles) load_tile_lds<D>(vbuf + ((j + 1) & 1) * kTE, vrs, n0 + kBN, kv_row_bytes, wave, lane);
-    const bool fast = j >= 1 && j + 1 < wave_tiles && !(CAUSAL && n0 + kBN - 1 > qw) && n0 + kBN <= M;
-    if (fast)
-      step_fast(j, s_cur, s_next);
-    else
-      step_general(j, s_cur, s_next);
+    // j + 1 < wave_tiles <= n_tiles, so V(j+1) exists; without a K(j+2) the K
+    // slots repeat the V(j+1) fetches (same bytes to the same place)
+    const bool has_k = j + 2 < n_tiles;
+    const i32x4 d2 = has_k ? kdesc : vdesc;
+    const uint32_t l2 = has_k ? k_fill : v_fill;
+    const int r2 = has_k ? n0 + 2 * kBN : n0 + kBN;
+    auto fetch = [&](int i) {
+      if (i < F::kInst)
+        F::issue(vdesc, v_fill, n0 + kBN, i, wave, voff, kv_row_bytes);
+      else
+        F::issue(d2, l2, r2, i - F::kInst, wave, voff, kv_row_bytes);
+    };
+    step_fast((1 - P) * kTB, P * kTB, s_cur, s_next, mx, fetch);
     wait_tile_loads();
-    __syncthreads();
+    kv_barrier();
   };
 
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(j, s_a, s_b);
-    if (j + 1 < n_tiles) step(j + 1, s_b, s_a);
+  // Steps 1 .. fast_end-1 take the steady-state path: no key of the tile is
+  // masked, S(j+1) is needed and the reference max is finite (tile 0 is
+  // general).  Every wave runs n_tiles steps, each ending in one barrier.
+  const int fast_end =
+      min(min(wave_tiles - 1, M / kBN), CAUSAL ? (qw + 1) / kBN : wave_tiles);  // first non-fast step >= 1
+  step_general(0, std::true_type{});
+  int j = 1;
+  float mx = tile_max(s_a);  // row max of the tile in s_a, carried by the fast steps
+  for (; j + 1 < fast_end; j += 2) {
+    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{});
+    step_fast_p(j + 1, s_b, s_a, mx, std::integral_constant<int, 0>{});
   }
+  if (j < fast_end) {
+    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{});
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+    ++j;
+  }
+  for (; j < n_tiles; ++j) step_general(j, std::false_type{});
 
   // ---- epilogue: O / l -> 16-bit, lse = ln2 * (m + log2 l) ----
+  const float l_tot = sum_xor32(l_run);
+  const float inv = 1.f / l_tot;
+  if (qi < N) {
+    uint16_t* op = o + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qi = qw + 32 * qb + l32;
-    const float l_tot = sum_xor32(l_run[qb]);
-    const float inv = 1.f / l_tot;
-    if (qi < N) {
-      uint16_t* op = o + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D;
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d0 = 32 * db + 8 * r + 4 * g;
-          uint2 w;
-          w.x = pack2<BF16>(acc_o[qb][db][4 * r + 0] * inv, acc_o[qb][db][4 * r + 1] * inv);
-          w.y = pack2<BF16>(acc_o[qb][db][4 * r + 2] * inv, acc_o[qb][db][4 * r + 3] * inv);
-          *reinterpret_cast<uint2*>(op + d0) = w;
-        }
-      if (lse != nullptr && g == 0) lse[((int64_t)b * Hq + h) * N + qi] = (m_run[qb] + log2f(l_tot)) * kLn2;
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * db + 8 * r + 4 * g;
+        uint2 w;
+        w.x = pack2<BF16>(acc_o[db][4 * r + 0] * inv, acc_o[db][4 * r + 1] * inv);
+        w.y = pack2<BF16>(acc_o[db][4 * r + 2] * inv, acc_o[db][4 * r + 3] * inv);
+        *reinterpret_cast<uint2*>(op + d0) = w;
+      }
+    if (lse != nullptr && g == 0) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 

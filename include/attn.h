@@ -70,7 +70,7 @@ typedef enum {
  * masked for query i when j > i (top-left mask, defined only for N == M);
  * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
  * including the row maximum).  Requires d in {64, 128}, Hq % Hkv == 0, a finite
- * scale >= 0, and B*N*Hq*d, B*(M+64)*Hkv*d below 2^31.
+ * scale >= 0, and B*(N+256)*Hq*d, B*(M+64)*Hkv*d below 2^31.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
