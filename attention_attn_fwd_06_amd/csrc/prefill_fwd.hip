@@ -152,6 +152,9 @@ __device__ __forceinline__ s16x8 lds_read_b128(uint32_t addr) { return *(const l
 __device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, u32x2 v) { *(lds_u32x2*)(uintptr_t)addr = v; }
 
 // Per-lane LDS addressing of the two MFMA operands that come from LDS.
 //  K (A operand of S^T = K Q^T): lane l reads row 32*kb + l%32, logical chunk
@@ -552,22 +555,43 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   for (; j < n_tiles; ++j) step_general(j, std::false_type{});
 
   // ---- epilogue: O / l -> 16-bit, lse = ln2 * (m + log2 l) ----
+  // Lane (l32, g) holds d = 32 db + 8 r + 4 g + (0..3) of its query row: half g
+  // of 16-byte chunk 4 db + r.  The rows go through this wave's Q^T region of
+  // LDS (free now: 32 rows of D 16-bit values), row-major with the chunk index
+  // XOR-swizzled by the row, and come back as whole rows, so every global
+  // store writes complete 128-byte lines instead of 16 bytes of 32 rows.
   const float l_tot = sum_xor32(l_run);
   const float inv = 1.f / l_tot;
-  if (qi < N) {
-    uint16_t* op = o + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D;
+  {
+    constexpr int kRowB = D * 2;              // bytes per O row
+    constexpr int kCh = D / 8;                // 16-byte chunks per row
+    constexpr int kRowsPerRead = 64 / kCh;    // rows covered by one wave-wide 16-byte read
+    const uint32_t ob = q_lane - (uint32_t)lane * 16u;  // this wave's region
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * db + 8 * r + 4 * g;
-        uint2 w;
-        w.x = pack2<BF16>(acc_o[db][4 * r + 0] * inv, acc_o[db][4 * r + 1] * inv);
-        w.y = pack2<BF16>(acc_o[db][4 * r + 2] * inv, acc_o[db][4 * r + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d0) = w;
+        const u32x2 w = {pack2<BF16>(acc_o[db][4 * r + 0] * inv, acc_o[db][4 * r + 1] * inv),
+                         pack2<BF16>(acc_o[db][4 * r + 2] * inv, acc_o[db][4 * r + 3] * inv)};
+        const int chunk = (4 * db + r) ^ (l32 % kCh);
+        lds_write_b64(ob + (uint32_t)(l32 * kRowB + chunk * 16 + g * 8), w);
       }
-    if (lse != nullptr && g == 0) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+    const int c = lane % kCh;
+    constexpr int kReads = 32 / kRowsPerRead;
+    s16x8 val[kReads];
+#pragma unroll
+    for (int k = 0; k < kReads; ++k) {
+      const int row = k * kRowsPerRead + lane / kCh;
+      val[k] = lds_read_b128(ob + (uint32_t)(row * kRowB + ((c ^ (row % kCh)) * 16)));
+    }
+#pragma unroll
+    for (int k = 0; k < kReads; ++k) {
+      const int qrow = qw + k * kRowsPerRead + lane / kCh;
+      if (qrow < N)
+        *reinterpret_cast<s16x8*>(o + ((int64_t)b * N + qrow) * q_row_stride + (int64_t)h * D + 8 * c) = val[k];
+    }
   }
+  if (lse != nullptr && g == 0 && qi < N) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // Host-side launcher (one instance per head dim, dtype and mask).
