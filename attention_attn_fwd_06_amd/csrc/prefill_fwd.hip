@@ -6,12 +6,18 @@
 // section 2: GQA head map and top-left causal tile skipping).
 //
 // MI355X design (not the page's CUDA design):
-//  * one workgroup = 8 waves, two per SIMD (256 VGPRs each); each wave owns
-//    32 queries of one (batch, query head) for the whole KV loop, so BM = 256
-//    queries share every K/V tile fetched into LDS (one workgroup per CU).
+//  * one workgroup = 4 waves (one per SIMD), 64 KB of LDS at d = 128, and two
+//    workgroups per CU (256 VGPRs per wave): the two run independently, so
+//    while one waits at a barrier, fetches its first tiles or writes O, the
+//    other's wave keeps the SIMD busy.  Each wave owns 32 queries of one
+//    (batch, query head) for the whole KV loop; with GQA a workgroup takes two
+//    query heads of a group x 64 rows (one head x 128 rows without GQA), so 128
+//    query rows share every K/V tile fetched into LDS while the causal
+//    diagonal stays one 64-key tile per head and no wave idles past it.
 //  * both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 //    accumulators, transposed so that one lane owns one query per block:
-//      S^T[key][query] = K Q^T   (A = K rows from LDS, B = Q^T kept in VGPRs)
+//      S^T[key][query] = K Q^T   (A = K rows from LDS, B = Q^T kept in VGPRs
+//                                 for the whole KV loop)
 //      O^T[d][query]  += V^T P^T (A = V^T via ds_read_b64_tr_b16, B = P^T
 //                                 taken straight from the S^T accumulator)
 //    so the row max / row sum are in-lane plus one v_permlane32_swap, and the
@@ -35,10 +41,12 @@
 //  * bf16 only: on the first KV tile P is split into hi + lo bf16 parts (two
 //    PV MFMAs), so rows with very few keys (early causal rows, where |O| is
 //    large) keep fp32-level accuracy in P.
-//  * causal: tiles beyond the diagonal are never loaded; a wave whose 64
+//  * causal: tiles beyond the diagonal are never loaded; a wave whose 32
 //    queries all precede a tile skips its math; only diagonal tiles are
 //    masked.  Grid: longest causal q-tiles first, heads of one GQA group
 //    adjacent, and an XCD-aware remap so heads sharing K/V share an L2.
+//  * epilogue: O rows go through LDS (the K/V buffers, free by then) so that
+//    every store writes whole 128-byte lines.
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,7 +55,7 @@ namespace attn {
 
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr int kWavesPerEU = 2;     // waves per SIMD
-constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = kWaves * 32;   // queries per workgroup (32 per wave)
@@ -155,6 +163,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 __device__ __forceinline__ void lds_write_b64(uint32_t addr, u32x2 v) { *(lds_u32x2*)(uintptr_t)addr = v; }
+// Orders this wave's LDS accesses when lanes exchange data through LDS: the
+// wait completes the writes, and the memory clobber stops the compiler from
+// reusing values read before it (to the compiler, lanes are separate threads,
+// so without it another lane's write is invisible).
+__device__ __forceinline__ void lds_lane_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Per-lane LDS addressing of the two MFMA operands that come from LDS.
 //  K (A operand of S^T = K Q^T): lane l reads row 32*kb + l%32, logical chunk
@@ -173,11 +186,10 @@ struct LdsAddr {
 };
 
 // S^T[kb] = K(tile) Q^T for the wave's 32 queries (first tile, diagonal and
-// tail tiles).  The Q^T operand of contraction step t is lane l's 16 bytes at
-// q_lane + 1024 t (see the Q^T layout in the kernel).
+// tail tiles).  qreg[t]: this lane's Q^T operand of contraction step t.
 template <int D, bool BF16>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint32_t k_row, uint32_t kx,
-                                        uint32_t q_lane) {
+                                        const s16x8 (&qreg)[D / 16]) {
   constexpr int kDT = D / 16;
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb) s[kb] = (f32x16){};
@@ -185,7 +197,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint3
   for (int t = 0; t < kDT; ++t) {
     // k_row + (32t ^ kx): k_row is a multiple of 128 and 32t ^ kx < 128 * D / 64
     const uint32_t row_t = k_row + ((uint32_t)(32 * t) ^ kx);
-    const s16x8 bq = lds_read_b128(q_lane + (uint32_t)(1024 * t));
+    const s16x8 bq = qreg[t];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       const s16x8 a = lds_read_b128(row_t + k_tile + (uint32_t)(kb * 32 * D * 2));
@@ -199,36 +211,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
-                        int n_qtiles, int total, float scale_log2) {
+                        int n_qtiles, int total, int pack, float scale_log2) {
   constexpr int kDT = D / 16;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
   constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
   using F = Fetch<D>;
-  // LDS: K buffers 0, 1, V buffers 0, 1, then the Q^T operands of the 8 waves
-  // (kDT KB each: contraction step t of wave w holds lane l's 16 bytes at
-  // 1024 (w kDT + t) + 16 l, so every Q^T read is one conflict-free
-  // ds_read_b128 and Q takes no registers during the KV loop).
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * kBN * D + kWaves * kDT * 512];
+  // LDS: K buffers 0, 1, V buffers 0, 1 (64 KB at d = 128).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * kBN * D];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u16*)smem;
-  const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTB, qbuf0 = lds0 + 4 * kTB;
+  const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTB;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int G = lane >> 4, sl = lane & 15;
 
-  // ---- tile id -> (b, h, q-tile) ----
+  // ---- tile id -> (b, kv head, heads, q-tile) ----
+  // A workgroup takes `pack` query heads of one GQA group (they share K/V) and
+  // kBM / pack query rows of each: wave w works on head pack-slot
+  // w / (kWaves / pack), rows 32 (w % (kWaves / pack)) .. +31 of the tile.  With causal masking
+  // a shorter row span per head means a smaller masked diagonal and fewer
+  // waves idle past their diagonal, at the same K/V reuse per tile.
   const int lid = xcd_remap(blockIdx.x, total);
   const int group = Hq / Hkv;
-  const int hg = lid % group;
-  const int rest = lid / group;
+  const int packs = group / pack;      // head packs per GQA group
+  const int rows = kBM / pack;         // query rows per head in this tile
+  const int wph = kWaves / pack;       // waves per head
+  const int hp = lid % packs;
+  const int rest = lid / packs;
   const int qt = n_qtiles - 1 - rest % n_qtiles;  // longest (causal) first
   const int bkv = rest / n_qtiles;
   const int kvh = bkv % Hkv, b = bkv / Hkv;
-  const int h = kvh * group + hg;
+  const int h = kvh * group + hp * pack + wave / wph;  // this wave's query head
 
-  const int q_start = qt * kBM;
-  const int qw = q_start + wave * 32;  // first query of this wave
+  const int q_start = qt * rows;
+  const int qw = q_start + (wave % wph) * 32;  // first query of this wave
   const int qlast = qw + 31;           // last query of this wave
   const int qi = qw + l32;             // this lane's query
 
@@ -262,8 +279,8 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
   }
 
-  // ---- Q^T operand: lane l of step t needs Q[qw + l%32][16t + 8g .. +7] ----
-  const uint32_t q_lane = qbuf0 + (uint32_t)(wave * kDT) * 1024u + (uint32_t)lane * 16u;
+  // ---- Q^T operand: lane l of step t holds Q[qw + l%32][16t + 8g .. +7] ----
+  s16x8 qreg[kDT];
 
   f32x16 acc_o[kDB];
   float m_run = -INFINITY;  // running max of scale*log2e*s (the reference max)
@@ -271,18 +288,18 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
 
-  const int kv_end = CAUSAL ? min(M, q_start + kBM) : M;
+  const int kv_end = CAUSAL ? min(M, q_start + rows) : M;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // last tile that holds a key <= some query of this wave
   const int wave_tiles = CAUSAL ? min(n_tiles, qlast / kBN + 1) : n_tiles;
 
-  // ---- prologue: Q^T, K(0), V(0), K(1) to LDS; S(0) ----
+  // ---- prologue: Q^T to registers, K(0), V(0), K(1) to LDS; S(0) ----
   {
     // rows past N read as zero; the host keeps (N + kBM) rows below 2^32 bytes
-    const i32x4 qdesc = make_desc(q + ((int64_t)b * N * Hq + h) * D, q_row_stride, N, D);
-    const uint32_t qv = (uint32_t)qi * (uint32_t)(q_row_stride * 2) + 16u * (uint32_t)g;
+    const uint16_t* qp = q + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D + 8 * g;
 #pragma unroll
-    for (int t = 0; t < kDT; ++t) dma16(qdesc, qbuf0 + (uint32_t)(wave * kDT + t) * 1024u, qv + 32u * t);
+    for (int t = 0; t < kDT; ++t)
+      qreg[t] = (qi < N) ? *reinterpret_cast<const s16x8*>(qp + 16 * t) : (s16x8){};
   }
   F::tile(kdesc, kbuf0, 0, wave, voff, kv_row_bytes);
   F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
@@ -290,7 +307,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   wait_tile_loads();
   kv_barrier();
   f32x16 s_a[kKB], s_b[kKB];  // S of the current tile is always in s_a between steps
-  qk_tile<D, BF16>(s_a, 0, la.k_row, la.kx, q_lane);
+  qk_tile<D, BF16>(s_a, 0, la.k_row, la.kx, qreg);
   kv_barrier();  // K buffer 0 is refilled in iteration 0
 
   // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks; v_tile
@@ -371,7 +388,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const int n0 = j * kBN;
     if (j + 2 < n_tiles) F::tile(kdesc, kbuf0 + par * kTB, n0 + 2 * kBN, wave, voff, kv_row_bytes);
     if (j + 1 < n_tiles) F::tile(vdesc, vbuf0 + (1 - par) * kTB, n0 + kBN, wave, voff, kv_row_bytes);
-    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_b, k_next, la.k_row, opaque(la.kx), q_lane);
+    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
     if (j < wave_tiles) {
       const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
       if (need_mask) {
@@ -452,7 +469,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     auto reads = [&](const int i) {
       if (i < kNQ) {
         const int t = i >> 1, kb = i & 1;
-        if (kb == 0) qv[t] = lds_read_b128(q_lane + 1024u * (uint32_t)t);
+        if (kb == 0) qv[t] = qreg[t];
         const uint32_t row_t = la.k_row + ((uint32_t)(32 * t) ^ kx);
         ka[i] = lds_read_b128(row_t + k_next + (uint32_t)(kb * 32 * D * 2));
       } else if (i < kN) {
@@ -556,17 +573,18 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
   // ---- epilogue: O / l -> 16-bit, lse = ln2 * (m + log2 l) ----
   // Lane (l32, g) holds d = 32 db + 8 r + 4 g + (0..3) of its query row: half g
-  // of 16-byte chunk 4 db + r.  The rows go through this wave's Q^T region of
-  // LDS (free now: 32 rows of D 16-bit values), row-major with the chunk index
-  // XOR-swizzled by the row, and come back as whole rows, so every global
-  // store writes complete 128-byte lines instead of 16 bytes of 32 rows.
+  // of 16-byte chunk 4 db + r.  The rows go through LDS (this wave's share of
+  // the K/V buffers, free after the last step's barrier: 32 rows of D 16-bit
+  // values), row-major with the chunk index XOR-swizzled by the row, and come
+  // back as whole rows, so every global store writes complete 128-byte lines
+  // instead of 16 bytes of 32 rows.
   const float l_tot = sum_xor32(l_run);
   const float inv = 1.f / l_tot;
   {
     constexpr int kRowB = D * 2;              // bytes per O row
     constexpr int kCh = D / 8;                // 16-byte chunks per row
     constexpr int kRowsPerRead = 64 / kCh;    // rows covered by one wave-wide 16-byte read
-    const uint32_t ob = q_lane - (uint32_t)lane * 16u;  // this wave's region
+    const uint32_t ob = kbuf0 + (uint32_t)wave * (uint32_t)(32 * D * 2);  // K/V buffers are free now
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -576,6 +594,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         const int chunk = (4 * db + r) ^ (l32 % kCh);
         lds_write_b64(ob + (uint32_t)(l32 * kRowB + chunk * 16 + g * 8), w);
       }
+    lds_lane_fence();
     const int c = lane % kCh;
     constexpr int kReads = 32 / kRowsPerRead;
     s16x8 val[kReads];
@@ -598,11 +617,17 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                           int Hkv, int N, int M, float scale, hipStream_t stream) {
-  const int n_qtiles = (N + kBM - 1) / kBM;
-  const int total = B * Hq * n_qtiles;
+  // query heads per workgroup: the largest power of two that divides the GQA
+  // group and leaves at least 64 rows (one K/V tile) per head
+  const int group = Hq / Hkv;
+  int pack = 1;
+  while (pack * 2 * 64 <= kBM && group % (pack * 2) == 0) pack *= 2;
+  const int rows = kBM / pack;
+  const int n_qtiles = (N + rows - 1) / rows;
+  const int total = B * (Hq / pack) * n_qtiles;
   hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, M, Hq,
-                     Hkv, n_qtiles, total, scale * kLog2e);
+                     Hkv, n_qtiles, total, pack, scale * kLog2e);
   return hipGetLastError();
 }
 
