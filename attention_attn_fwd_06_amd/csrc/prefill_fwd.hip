@@ -38,9 +38,11 @@
 //  * exp2 domain with scale*log2(e) folded into one FMA; the O / l rescale is
 //    skipped unless some row's max grew by more than 2^8 (exact: O and l
 //    always share the same reference max).
-//  * bf16 only: on the first KV tile P is split into hi + lo bf16 parts (two
-//    PV MFMAs), so rows with very few keys (early causal rows, where |O| is
-//    large) keep fp32-level accuracy in P.
+//  * bf16 only: where a wave's first KV tile is masked or is its only tile
+//    (rows with at most 64 keys: early causal rows, where |O| is large), P of
+//    that tile is split into hi + lo bf16 parts (two PV MFMAs), so those rows
+//    keep fp32-level accuracy in P.  Any other wave runs the steady-state
+//    step from tile 0 on.
 //  * causal: tiles beyond the diagonal are never loaded; a wave whose 32
 //    queries all precede a tile skips its math; only diagonal tiles are
 //    masked.  Grid: longest causal q-tiles first, heads of one GQA group
@@ -375,7 +377,8 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
   };
 
-  // General step (first tile, diagonal and tail tiles, last tile of a wave):
+  // General step (a masked or only first tile, diagonal and tail tiles, last
+  // tile of a wave):
   // fetches K(j+2) and V(j+1), computes S(j+1) into s_b if this wave needs it,
   // then mask, softmax and PV of tile j from s_a; ends with S(j+1) in s_a.  The
   // buffer parity is a run-time value here (these steps are few).
@@ -439,10 +442,14 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // step's tile fetches, and in the last slots the row max of S(j+1) (whose
   // MFMAs have finished by then), which the next step uses.  The slots are
   // separated by scheduling fences, so the order is the one written here.
-  // mx: row max of tile j on entry, of tile j+1 on return.
+  // mx: row max of tile j on entry, of tile j+1 on return.  first: j == 0.
   auto step_fast = [&](const uint32_t k_next, const uint32_t v_cur, f32x16 (&s_cur)[kKB],
-                       f32x16 (&s_next)[kKB], float& mx, auto&& fetch) {
-    {
+                       f32x16 (&s_next)[kKB], float& mx, auto&& fetch, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
+    if constexpr (kFirst) {
+      // O and l are still zero: the reference max is simply set
+      m_run = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+    } else {
       const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
         const float m_new = fmaxf(m_run, m_tile);
@@ -464,7 +471,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     s16x8 qv[kDT], ka[kNQ], va[kNP], pb[4];
     float pe[4][8];
     float lsum = 0.f, mxn = -INFINITY;
-    const float neg_m = -m_run;
+    const float neg_m = (kFirst && m_run == -INFINITY) ? 0.f : -m_run;
 
     auto reads = [&](const int i) {
       if (i < kNQ) {
@@ -530,7 +537,8 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // One steady-state iteration; P is the parity of j (buffers alternate
   // between tiles): S(j+1) reads K buffer 1-P, PV(j) reads V buffer P, and the
   // iteration fetches K(j+2) into K buffer P and V(j+1) into V buffer 1-P.
-  auto step_fast_p = [&](const int j, f32x16 (&s_cur)[kKB], f32x16 (&s_next)[kKB], float& mx, auto parity) {
+  auto step_fast_p = [&](const int j, f32x16 (&s_cur)[kKB], f32x16 (&s_next)[kKB], float& mx, auto parity,
+                         auto first) {
     constexpr int P = decltype(parity)::value;
     const uint32_t k_fill = kbuf0 + P * kTB, v_fill = vbuf0 + (1 - P) * kTB;
     const int n0 = j * kBN;
@@ -546,25 +554,35 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       else
         F::issue(d2, l2, r2, i - F::kInst, wave, voff, kv_row_bytes);
     };
-    step_fast((1 - P) * kTB, P * kTB, s_cur, s_next, mx, fetch);
+    step_fast((1 - P) * kTB, P * kTB, s_cur, s_next, mx, fetch, first);
     wait_tile_loads();
     kv_barrier();
   };
 
-  // Steps 1 .. fast_end-1 take the steady-state path: no key of the tile is
-  // masked, S(j+1) is needed and the reference max is finite (tile 0 is
-  // general).  Every wave runs n_tiles steps, each ending in one barrier.
+  // Steps 0 .. fast_end-1 take the steady-state path: no key of the tile is
+  // masked and S(j+1) is needed (if fast_end is 0, tile 0 is a general step).
+  // Every wave runs n_tiles steps, each ending in one barrier.
   const int fast_end =
       min(min(wave_tiles - 1, M / kBN), CAUSAL ? (qw + 1) / kBN : wave_tiles);  // first non-fast step >= 1
-  step_general(0, std::true_type{});
+  // tile 0 takes the steady-state path too when it has no masked key and S(1)
+  // is needed (fast_end >= 1); O and l start at zero there
+  float mx;  // row max of the tile in s_a, carried by the fast steps
+  if (fast_end >= 1) {
+    mx = tile_max(s_a);
+    step_fast_p(0, s_a, s_b, mx, std::integral_constant<int, 0>{}, std::true_type{});
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+  } else {
+    step_general(0, std::true_type{});
+    mx = tile_max(s_a);
+  }
   int j = 1;
-  float mx = tile_max(s_a);  // row max of the tile in s_a, carried by the fast steps
   for (; j + 1 < fast_end; j += 2) {
-    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{});
-    step_fast_p(j + 1, s_b, s_a, mx, std::integral_constant<int, 0>{});
+    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{});
+    step_fast_p(j + 1, s_b, s_a, mx, std::integral_constant<int, 0>{}, std::false_type{});
   }
   if (j < fast_end) {
-    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{});
+    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{});
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
     ++j;
