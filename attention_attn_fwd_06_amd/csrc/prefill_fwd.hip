@@ -171,6 +171,15 @@ __device__ __forceinline__ void lds_write_b64(uint32_t addr, u32x2 v) { *(lds_u3
 // so without it another lane's write is invisible).
 __device__ __forceinline__ void lds_lane_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// (a ^ b) + c in one instruction, opaque to the compiler, so constant offsets
+// added to the result become instruction offsets instead of being
+// reassociated into extra live base registers.
+__device__ __forceinline__ uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+}
+
 // Per-lane LDS addressing of the two MFMA operands that come from LDS.
 //  K (A operand of S^T = K Q^T): lane l reads row 32*kb + l%32, logical chunk
 //    2t + l/32 of contraction step t.  swz of that row equals swz(l%32), and
@@ -460,9 +469,12 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         m_run = m_new;
       }
     }
-    // a fresh copy per step keeps the per-step K addresses from being hoisted
-    // out of the KV loop as kDT live registers
+    // fresh copies per step keep the per-step K addresses from being hoisted
+    // out of the KV loop as kDT live registers; the address of contraction
+    // step t is then one v_xad_u32, and the second 32-key block is an
+    // instruction offset
     const uint32_t kx = opaque(la.kx);
+    const uint32_t kbase = opaque(la.k_row + k_next);
     constexpr int kNQ = 2 * kDT, kNP = 4 * kDB, kN = kNQ + kNP;
     constexpr int kL = 4;                  // MFMAs whose operands are read ahead
     constexpr int kNF = 2 * F::kInst;      // tile fetch instructions per step
@@ -477,8 +489,8 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       if (i < kNQ) {
         const int t = i >> 1, kb = i & 1;
         if (kb == 0) qv[t] = qreg[t];
-        const uint32_t row_t = la.k_row + ((uint32_t)(32 * t) ^ kx);
-        ka[i] = lds_read_b128(row_t + k_next + (uint32_t)(kb * 32 * D * 2));
+        const uint32_t row_t = xor_add(kx, (uint32_t)(32 * t), kbase);
+        ka[i] = lds_read_b128(row_t + (uint32_t)(kb * 32 * D * 2));
       } else if (i < kN) {
         const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
         const uint32_t koff = v_cur + (uint32_t)(16 * ks * D * 2);  // keys 16 ks .. 16 ks + 15
