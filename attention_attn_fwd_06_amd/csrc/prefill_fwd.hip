@@ -217,12 +217,29 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint3
   }
 }
 
+// Division of a non-negative int below 2^31 by a fixed divisor d >= 1 with a
+// multiplier and a shift worked out on the host (round-up method of
+// Granlund and Montgomery): q = (mulhi(n, mul) + n) >> shift, with
+// shift = ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1.  Exact for
+// every n < 2^31; scalar instructions only.
+struct FastDiv {
+  uint32_t mul, shift, d;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.mul) + n) >> f.shift; }
+
+// Grid decomposition constants of one launch (see the tile-id decode in the kernel).
+struct TileDecode {
+  FastDiv packs, qtiles, hkv;  // divisors: head packs per GQA group, q-tiles, KV heads
+  int group;                   // query heads per KV head
+  int pack_shift;              // log2 of the query heads per workgroup
+};
+
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
-                        int n_qtiles, int total, int pack, float scale_log2) {
+                        int n_qtiles, int total, TileDecode td, float scale_log2) {
   constexpr int kDT = D / 16;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
   constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
@@ -244,19 +261,20 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // a shorter row span per head means a smaller masked diagonal and fewer
   // waves idle past their diagonal, at the same K/V reuse per tile.
   const int lid = xcd_remap(blockIdx.x, total);
-  const int group = Hq / Hkv;
-  const int packs = group / pack;      // head packs per GQA group
-  const int rows = kBM / pack;         // query rows per head in this tile
-  const int wph = kWaves / pack;       // waves per head
-  const int hp = lid % packs;
-  const int rest = lid / packs;
-  const int qt = n_qtiles - 1 - rest % n_qtiles;  // longest (causal) first
-  const int bkv = rest / n_qtiles;
-  const int kvh = bkv % Hkv, b = bkv / Hkv;
-  const int h = kvh * group + hp * pack + wave / wph;  // this wave's query head
+  const int group = td.group;
+  const int rows = kBM >> td.pack_shift;          // query rows per head in this tile
+  static_assert(kWaves == 4, "log2(kWaves) below");
+  const int wshift = 2 - td.pack_shift;           // log2 of the waves per head
+  const uint32_t rest = fdiv((uint32_t)lid, td.packs);
+  const int hp = lid - (int)(rest * td.packs.d);  // head pack within the GQA group
+  const uint32_t bkv = fdiv(rest, td.qtiles);
+  const int qt = n_qtiles - 1 - (int)(rest - bkv * (uint32_t)n_qtiles);  // longest (causal) first
+  const uint32_t bq = fdiv(bkv, td.hkv);
+  const int kvh = (int)(bkv - bq * (uint32_t)Hkv), b = (int)bq;
+  const int h = kvh * group + (hp << td.pack_shift) + (wave >> wshift);  // this wave's query head
 
   const int q_start = qt * rows;
-  const int qw = q_start + (wave % wph) * 32;  // first query of this wave
+  const int qw = q_start + (wave & ((1 << wshift) - 1)) * 32;  // first query of this wave
   const int qlast = qw + 31;           // last query of this wave
   const int qi = qw + l32;             // this lane's query
 
@@ -655,9 +673,19 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   const int rows = kBM / pack;
   const int n_qtiles = (N + rows - 1) / rows;
   const int total = B * (Hq / pack) * n_qtiles;
+  auto fast_div = [](uint32_t d) {
+    uint32_t l = 0;
+    while ((1u << l) < d) ++l;
+    const uint64_t mul = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)mul, l, d};
+  };
+  int pack_shift = 0;
+  while ((1 << pack_shift) < pack) ++pack_shift;
+  const TileDecode td{fast_div((uint32_t)(group / pack)), fast_div((uint32_t)n_qtiles), fast_div((uint32_t)Hkv),
+                      group, pack_shift};
   hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, M, Hq,
-                     Hkv, n_qtiles, total, pack, scale * kLog2e);
+                     Hkv, n_qtiles, total, td, scale * kLog2e);
   return hipGetLastError();
 }
 

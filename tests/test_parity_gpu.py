@@ -93,6 +93,9 @@ SHAPES = [
     (2, 384, 384, 8, 4, 64, "f16", True),
     (1, 300, 300, 16, 2, 128, "bf16", False),
     (1, 129, 129, 8, 8, 128, "f16", True),
+    # GQA groups and KV-head counts that are not powers of two (grid decode)
+    (2, 300, 300, 6, 3, 128, "bf16", True),
+    (1, 257, 257, 6, 2, 64, "f16", True),
 ]
 
 
