@@ -42,7 +42,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
     case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
-    case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N == M (top-left mask)";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N <= M (bottom-right mask)";
     case ATTN_ERR_CHUNK_SIZE: return "decode chunk size must be 128";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
@@ -59,7 +59,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
-  if (causal && N != M) return ATTN_ERR_CAUSAL_SHAPE;
+  if (causal && N > M) return ATTN_ERR_CAUSAL_SHAPE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
   if ((int64_t)B * (N + 256) * Hq * d >= kMaxElems || (int64_t)B * (M + 64) * Hkv * d >= kMaxElems ||
       (int64_t)B * Hq * ((N + 127) / 128) >= kMaxElems)

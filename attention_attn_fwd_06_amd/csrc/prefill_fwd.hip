@@ -3,7 +3,10 @@
 // Computes O = softmax(scale * Q K^T [+ causal mask]) V with an online softmax
 // ("fmha sm120: beyond torch.sdpa", section 1 "flash attention": load a Q tile,
 // loop over K/V tiles, rescale the running row max m and sum l, write O once;
-// section 2: GQA head map and top-left causal tile skipping).
+// section 2: GQA head map and causal tile skipping).  With fewer queries than
+// keys the causal mask is aligned bottom-right: the N queries are the last N
+// positions of the key sequence, so query i sees keys 0 .. i + M - N (for
+// N == M the pages' top-left mask).
 //
 // MI355X design (not the page's CUDA design):
 //  * one workgroup = 4 waves (one per SIMD), 64 KB of LDS at d = 128, and two
@@ -180,6 +183,17 @@ __device__ __forceinline__ uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) 
   return r;
 }
 
+// Row max over this lane and lane ^ 32.  A plain v_max_f32: its inputs are
+// MFMA results or -inf, never signalling NaNs, so the quieting that fmaxf
+// adds to each operand is not needed.
+__device__ __forceinline__ float row_max_xor32(float x) {
+  const int xi = __float_as_int(x);
+  const auto pr = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(__int_as_float(pr[0])), "v"(__int_as_float(pr[1])));
+  return r;
+}
+
 // Per-lane LDS addressing of the two MFMA operands that come from LDS.
 //  K (A operand of S^T = K Q^T): lane l reads row 32*kb + l%32, logical chunk
 //    2t + l/32 of contraction step t.  swz of that row equals swz(l%32), and
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
-                        int n_qtiles, int total, TileDecode td, float scale_log2) {
+                        int n_qtiles, int total, TileDecode td, int causal_off, float scale_log2) {
   constexpr int kDT = D / 16;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
   constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
@@ -317,10 +331,11 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
 
-  const int kv_end = CAUSAL ? min(M, q_start + rows) : M;
+  // causal: query i sees keys 0 .. i + causal_off (causal_off = M - N >= 0)
+  const int kv_end = CAUSAL ? min(M, q_start + rows + causal_off) : M;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // last tile that holds a key <= some query of this wave
-  const int wave_tiles = CAUSAL ? min(n_tiles, qlast / kBN + 1) : n_tiles;
+  const int wave_tiles = CAUSAL ? min(n_tiles, (qlast + causal_off) / kBN + 1) : n_tiles;
 
   // ---- prologue: Q^T to registers, K(0), V(0), K(1) to LDS; S(0) ----
   {
@@ -420,14 +435,14 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     if (j + 1 < n_tiles) F::tile(vdesc, vbuf0 + (1 - par) * kTB, n0 + kBN, wave, voff, kv_row_bytes);
     if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
     if (j < wave_tiles) {
-      const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw) || (n0 + kBN > M);
+      const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw + causal_off) || (n0 + kBN > M);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool ok = key < M && (!CAUSAL || key <= qi);
+            const bool ok = key < M && (!CAUSAL || key <= qi + causal_off);
             s_a[kb][i] = ok ? s_a[kb][i] : -INFINITY;
           }
       }
@@ -477,7 +492,9 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       // O and l are still zero: the reference max is simply set
       m_run = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
     } else {
-      const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+      // mx is finite here: the tile has no masked key (inputs holding Inf or
+      // NaN give NaN outputs either way)
+      const float m_tile = mx * scale_log2;
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
         const float m_new = fmaxf(m_run, m_tile);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -557,7 +574,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 #pragma unroll
         for (int k = 0; k < 32; ++k)
           if (k * kMaxSlots / 32 == r) mxn = fmaxf(mxn, s_next[k >> 4][k & 15]);
-        if (i == kN - 1) mx = max_xor32(mxn);
+        if (i == kN - 1) mx = row_max_xor32(mxn);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -593,7 +610,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // masked and S(j+1) is needed (if fast_end is 0, tile 0 is a general step).
   // Every wave runs n_tiles steps, each ending in one barrier.
   const int fast_end =
-      min(min(wave_tiles - 1, M / kBN), CAUSAL ? (qw + 1) / kBN : wave_tiles);  // first non-fast step >= 1
+      min(min(wave_tiles - 1, M / kBN), CAUSAL ? (qw + causal_off + 1) / kBN : wave_tiles);
   // tile 0 takes the steady-state path too when it has no masked key and S(1)
   // is needed (fast_end >= 1); O and l start at zero there
   float mx;  // row max of the tile in s_a, carried by the fast steps
@@ -685,7 +702,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
                       group, pack_shift};
   hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, M, Hq,
-                     Hkv, n_qtiles, total, td, scale * kLog2e);
+                     Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, scale * kLog2e);
   return hipGetLastError();
 }
 

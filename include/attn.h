@@ -50,7 +50,7 @@ typedef enum {
   ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not in {64, 128} */
   ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
-  ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N != M */
+  ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
   ATTN_ERR_CHUNK_SIZE = -7,     /* decode chunk size other than 128 */
   ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (hipGetLastError) */
   ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
@@ -67,7 +67,9 @@ typedef enum {
  *
  * For batch b and query head h the key/value head is h / (Hq / Hkv) (contiguous
  * groups, "fmha sm120", section 2).  S = scale * Q K^T; with causal != 0 key j is
- * masked for query i when j > i (top-left mask, defined only for N == M);
+ * masked for query i when j > i + (M - N): the N queries are the last N positions
+ * of the key sequence (a chunk of a longer prefill), so the last query sees every
+ * key; for N == M this is the page's top-left mask.  Causal requires N <= M;
  * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
  * including the row maximum).  Requires d in {64, 128}, Hq % Hkv == 0, a finite
  * scale >= 0, and B*(N+256)*Hq*d, B*(M+64)*Hkv*d below 2^31.

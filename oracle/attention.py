@@ -21,9 +21,13 @@ Readings where the pages leave a step open (each is also listed in the design
 notes of the repository):
   * lse is the natural logarithm of the row's softmax denominator including
     the max: lse_i = m_i + ln(l_i) = ln sum_j exp(S_ij).
-  * The causal mask is top-left aligned and only defined here for N == M.
-  * A row with no allowed key has O = 0 and lse = -inf (unreachable with a
-    top-left causal mask and N == M, since key 0 is always allowed).
+  * The causal mask for N <= M keys key j for query i when j <= i + (M - N):
+    the queries are the last N positions of the key sequence (a chunk of a
+    longer prefill), so the last query sees every key.  For N == M this is
+    the pages' top-left mask; N > M is not defined here.  The reading makes a
+    chunk's rows equal the same rows of the full-length causal attention.
+  * A row with no allowed key has O = 0 and lse = -inf (unreachable with
+    this mask and N <= M, since key 0 is always allowed).
   * Inputs are the already-rounded fp16/bf16 values upcast exactly to
     float64; ``scale`` is the fp32 value handed to the GPU, upcast.
 """
@@ -66,7 +70,8 @@ def attn_ref(q, k, v, scale: float, causal: bool = False, rows=None):
     page's layout; the pages use dv = d).
     Returns O [B, n, Hq, dv] and lse [B, Hq, n] in float64, where n = N, or
     n = len(rows) when ``rows`` selects a subset of query positions (the
-    causal mask still uses each row's absolute position).
+    causal mask still uses each row's absolute position; with causal, query
+    i may see keys 0 .. i + M - N).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, Hq, d = q.shape
@@ -75,8 +80,9 @@ def attn_ref(q, k, v, scale: float, causal: bool = False, rows=None):
         raise ValueError("shape mismatch between q, k, v")
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
-    if causal and N != M:
-        raise ValueError("causal attention is defined here only for N == M")
+    if causal and N > M:
+        raise ValueError("causal attention is defined here only for N <= M")
+    off = M - N if causal else 0                  # query i sees keys j <= i + off
     group = Hq // Hkv
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     n = rows.shape[0]
@@ -92,7 +98,7 @@ def attn_ref(q, k, v, scale: float, causal: bool = False, rows=None):
             Vbh = v[b, :, kh, :]                  # [M, dv]
             S = float(scale) * (Qbh @ Kbh.T)      # [n, M]
             if causal:
-                S = np.where(keys[None, :] > rows[:, None], -np.inf, S)
+                S = np.where(keys[None, :] > rows[:, None] + off, -np.inf, S)
             P, lse_bh = _softmax_rows(S)
             O[b, :, h, :] = P @ Vbh
             lse[b, h, :] = lse_bh

@@ -31,7 +31,8 @@ def brute_attention(q, k, v, scale, causal):
         for h in range(Hq):
             kh = h // g
             for i in range(N):
-                allowed = [j for j in range(M) if (not causal) or j <= i]
+                # causal: query i is position i + M - N of the key sequence
+                allowed = [j for j in range(M) if (not causal) or j <= i + M - N]
                 s = {j: scale * math.fsum(q[b][i][h][t] * k[b][j][kh][t] for t in range(d))
                      for j in allowed}
                 mx = max(s.values())

@@ -50,6 +50,9 @@ PREFILL_TINY = [
     (2, 7, 7, 4, 2, 5, True, 0.3),
     (2, 3, 9, 3, 1, 4, False, 1.1),
     (1, 1, 1, 1, 1, 2, True, 0.9),
+    # causal with fewer queries than keys (the last N positions of the sequence)
+    (1, 3, 8, 2, 1, 3, True, 0.8),
+    (2, 1, 6, 2, 2, 4, True, 0.6),
 ]
 
 
@@ -125,6 +128,33 @@ def check_sdpa(ora):
         v = _rand((B, N, Hkv, d), 90 + i)
         O, _ = ora.attn_ref(q, k, v, 0.25, causal)
         _close(O, _sdpa(q, k, v, 0.25, causal), 1e-12, f"sdpa case {i}")
+    # causal with N < M: SDPA with an explicit boolean mask (key j allowed for
+    # query i when j <= i + M - N), since its is_causal flag is top-left only
+    B, N, M, Hq, Hkv, d = 2, 7, 19, 4, 2, 8
+    q, k, v = _rand((B, N, Hq, d), 75), _rand((B, M, Hkv, d), 85), _rand((B, M, Hkv, d), 95)
+    O, _ = ora.attn_ref(q, k, v, 0.3, True)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    allow = torch.arange(M)[None, :] <= torch.arange(N)[:, None] + (M - N)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allow, scale=0.3)
+    _close(O, o.permute(0, 2, 1, 3).numpy(), 1e-12, "sdpa bottom-right mask")
+
+
+def check_causal_chunk_is_tail_of_full(ora):
+    """Causal attention of the last N query positions against all M keys
+    equals the same rows of the full-length (N = M) causal attention, and the
+    last query sees every key (its row equals non-causal attention)."""
+    B, M, Hq, Hkv, d = 2, 13, 4, 2, 6
+    qf, k, v = _rand((B, M, Hq, d), 160), _rand((B, M, Hkv, d), 161), _rand((B, M, Hkv, d), 162)
+    Of, Lf = ora.attn_ref(qf, k, v, 0.45, True)
+    for N in (1, 4, M):
+        O, L = ora.attn_ref(qf[:, M - N:], k, v, 0.45, True)
+        _close(O, Of[:, M - N:], what=f"chunk of {N} rows: O")
+        _close(L, Lf[:, :, M - N:], what=f"chunk of {N} rows: lse")
+    On, Ln = ora.attn_ref(qf[:, M - 1:], k, v, 0.45, False)
+    _close(Of[:, M - 1:], On, what="last row sees every key: O")
+    _close(Lf[:, :, M - 1:], Ln, what="last row sees every key: lse")
 
 
 # ---------------------------------------------------------------------------
@@ -276,7 +306,7 @@ FAST_CHECKS = [
     check_identity_v_rows_are_probabilities, check_constant_v, check_single_key,
     check_causal_row0, check_zero_scale, check_key_shift, check_permutation,
     check_gqa_is_repeated_mha, check_decode_is_single_query_attention,
-    check_merge_identities, check_two_keys_closed_form,
+    check_merge_identities, check_two_keys_closed_form, check_causal_chunk_is_tail_of_full,
 ]
 
 

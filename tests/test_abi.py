@@ -64,7 +64,7 @@ def fwd(**kw):
     (dict(d=96), -3), (dict(d=256), -3), (dict(d=32), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4),
     (dict(Hq=6, Hkv=4), -5),
-    (dict(causal=1, N=128, M=256), -6),
+    (dict(causal=1, N=256, M=128), -6),
     (dict(scale=-0.5), -11), (dict(scale=float("inf")), -11), (dict(scale=float("nan")), -11),
     (dict(B=1 << 12, N=1 << 12, Hq=1 << 4, d=128), -9),
     (dict(q=FAKE + 8), -10), (dict(o=FAKE + 2), -10), (dict(lse=FAKE + 2), -10),

@@ -14,8 +14,10 @@ SRC = (pathlib.Path(__file__).resolve().parents[1] / "oracle" / "attention.py").
 MUTANTS = {
     # name: (original text, planted mistake)
     "gqa_interleaved_heads": ("kh = h // group", "kh = h % Hkv"),
-    "causal_off_by_one": ("keys[None, :] > rows[:, None]", "keys[None, :] >= rows[:, None]"),
-    "causal_upper_triangle": ("keys[None, :] > rows[:, None]", "keys[None, :] < rows[:, None]"),
+    "causal_off_by_one": ("keys[None, :] > rows[:, None] + off", "keys[None, :] >= rows[:, None] + off"),
+    "causal_upper_triangle": ("keys[None, :] > rows[:, None] + off", "keys[None, :] < rows[:, None] + off"),
+    "causal_chunk_top_left": ("keys[None, :] > rows[:, None] + off", "keys[None, :] > rows[:, None]"),
+    "causal_chunk_offset_sign": ("off = M - N if causal else 0", "off = N - M if causal else 0"),
     "scale_dropped": ("S = float(scale) * (Qbh @ Kbh.T)", "S = (Qbh @ Kbh.T)"),
     "scale_squared": ("S = float(scale) * (Qbh @ Kbh.T)", "S = float(scale) ** 2 * (Qbh @ Kbh.T)"),
     "pv_uses_keys": ("O[b, :, h, :] = P @ Vbh", "O[b, :, h, :] = P @ Kbh[:, :Vbh.shape[1]]"),

@@ -96,6 +96,11 @@ SHAPES = [
     # GQA groups and KV-head counts that are not powers of two (grid decode)
     (2, 300, 300, 6, 3, 128, "bf16", True),
     (1, 257, 257, 6, 2, 64, "f16", True),
+    # causal with N < M: the queries are the last N positions (bottom-right mask)
+    (1, 1, 333, 4, 2, 128, "bf16", True),
+    (2, 64, 200, 8, 2, 128, "bf16", True),
+    (1, 100, 1000, 4, 1, 64, "f16", True),
+    (1, 130, 515, 8, 8, 128, "f16", True),
 ]
 
 
@@ -141,6 +146,20 @@ def test_prefill_causal_gqa_bf16_full_size_sampled():
     q, k, v = make_inputs(w, 0)
     check_prefill(q, k, v, w.causal, w.scale, w.dtype, rows=_sample_rows(w.N, 2),
                   bh=[(0, 0), (0, 3), (1, 13), (2, 22), (3, 31)], label=w.name)
+
+
+def test_prefill_causal_chunk_matches_full_rows():
+    """A causal chunk of the last N queries against all M keys gives the same
+    rows as the full-length causal call, to the parity bound (the two calls
+    tile the rows differently, so bitwise equality is not expected)."""
+    say("case causal chunk vs full rows")
+    q, k, v = prefill_inputs(1, 8, 2, 700, 700, 128, "bf16", 8)
+    scale = float(np.float32(128 ** -0.5))
+    Of, Lf = gpu_fwd(q, k, v, True, scale)
+    for n in (1, 77, 300):
+        Oc, Lc = gpu_fwd(q[:, 700 - n:].contiguous(), k, v, True, scale)
+        assert maxerr(Oc, Of[:, 700 - n:]) <= 2 * TOL_O["bf16"], n
+        assert maxerr(Lc, Lf[:, :, 700 - n:]) <= 2 * TOL_LSE, n
 
 
 def test_prefill_deterministic():
