@@ -6,6 +6,8 @@ every step of the computation runs in the HIP kernels of ``csrc/``.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -51,23 +53,44 @@ def _check(t: torch.Tensor, name: str):
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,
              return_lse: bool = True, stream=None):
-    """q [B,N,Hq,d], k/v [B,M,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N] fp32 or None)."""
+    """q [B,N,Hq,d], k/v [B,M,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N] fp32 or None).
+
+    q, k, v (and a given o) may be strided views (e.g. slices of a fused QKV
+    projection, or head-major tensors transposed to [B,N,H,d]) as long as the
+    last dimension is contiguous; they then go through attn_fwd_strided."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n)
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be 4-D with a contiguous last dimension")
     B, N, Hq, d = q.shape
     M, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = d ** -0.5
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device)
+    elif not o.is_cuda or o.dim() != 4 or o.stride(-1) != 1:
+        raise ValueError("o must be a 4-D GPU tensor with a contiguous last dimension")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = _lib.load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              lse.data_ptr() if lse is not None else None,
-                              B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale),
-                              _dtype_code(q), _stream(stream))
+    if lse is not None:
+        _check(lse, "lse")
+    lib = _lib.load()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale), _dtype_code(q))
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        st = lib.attn_fwd(*args, _stream(stream))
+        name = "attn_fwd"
+    else:
+        strides = _lib.Strides()
+        for field, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+            # the stride of a dimension of size 1 is never used: pass 0
+            getattr(strides, field)[:] = [t.stride(i) if t.shape[i] > 1 else 0 for i in range(3)]
+        st = lib.attn_fwd_strided(*args, ctypes.byref(strides), _stream(stream))
+        name = "attn_fwd_strided"
     if st != 0:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, name)
     return o, lse
 
 

@@ -10,10 +10,19 @@ import pathlib
 
 LIB_PATH = pathlib.Path(__file__).resolve().parent / "libattn_mi355x.so"
 
+
+class Strides(ctypes.Structure):
+    """attn_strides_t: element strides {batch, token, head} of q, k, v, o."""
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3),
+                ("v", ctypes.c_int64 * 3), ("o", ctypes.c_int64 * 3)]
+
+
 SYMBOLS = {
     # name: (restype, argtypes)
     "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 7
                  + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_fwd_strided": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 7
+                         + [ctypes.c_float, ctypes.c_int, ctypes.POINTER(Strides), ctypes.c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
                             + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),

@@ -12,7 +12,7 @@
 namespace attn {
 hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                             int Hq, int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
-                            hipStream_t stream);
+                            const attn_strides_t& st, hipStream_t stream);
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                            int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream);
 hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq,
@@ -48,12 +48,14 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    case ATTN_ERR_LAYOUT: return "strides must be >= 0 and multiples of 8 elements; k and v need one token stride >= d";
     default: return "unknown status";
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
-             int M, int d, int causal, float scale, attn_dtype_t dtype, hipStream_t stream) {
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int N, int M, int d, int causal, float scale, attn_dtype_t dtype,
+                     const attn_strides_t* strides, hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
   if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
@@ -61,14 +63,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (causal && N > M) return ATTN_ERR_CAUSAL_SHAPE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
-  if ((int64_t)B * (N + 256) * Hq * d >= kMaxElems || (int64_t)B * (M + 64) * Hkv * d >= kMaxElems ||
-      (int64_t)B * Hq * ((N + 127) / 128) >= kMaxElems)
+  attn_strides_t st;
+  if (strides) {
+    st = *strides;
+  } else {
+    const int64_t qn = (int64_t)Hq * d, kn = (int64_t)Hkv * d;
+    st = attn_strides_t{{N * qn, qn, d}, {M * kn, kn, d}, {M * kn, kn, d}, {N * qn, qn, d}};
+  }
+  const int64_t* all[4] = {st.q, st.k, st.v, st.o};
+  for (const int64_t* t : all)
+    for (int i = 0; i < 3; ++i)
+      if (t[i] < 0 || t[i] % 8 != 0) return ATTN_ERR_LAYOUT;
+  // k and v share one token stride of at least d (key rows past M must lie
+  // beyond the last key row, where the bounds-checked tile loads return zeros)
+  if (st.k[1] != st.v[1] || st.k[1] < d) return ATTN_ERR_LAYOUT;
+  // largest element offset of each tensor (+ d), and the K/V buffer range
+  // ((M + 64) token rows, so that offsets of the rows past M never wrap)
+  auto extent = [&](const int64_t* t, int rows, int heads) {
+    return (int64_t)(B - 1) * t[0] + (int64_t)(rows - 1) * t[1] + (int64_t)(heads - 1) * t[2] + d;
+  };
+  if (extent(st.q, N, Hq) >= kMaxElems || extent(st.o, N, Hq) >= kMaxElems ||
+      extent(st.k, M, Hkv) >= kMaxElems || extent(st.v, M, Hkv) >= kMaxElems ||
+      (int64_t)(M + 64) * st.k[1] + d >= kMaxElems || (int64_t)B * Hq * ((N + 63) / 64) >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_ALIGNMENT;
   return launch_status(attn::prefill_dispatch(q, k, v, o, lse, B, Hq, Hkv, N, M, d, causal != 0,
-                                              dtype == ATTN_BF16, scale, stream));
+                                              dtype == ATTN_BF16, scale, st, stream));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+             int M, int d, int causal, float scale, attn_dtype_t dtype, hipStream_t stream) {
+  return attn_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, N, M, d, causal, scale, dtype, nullptr, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size) {

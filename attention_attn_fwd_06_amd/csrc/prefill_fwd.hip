@@ -54,6 +54,7 @@
 //    every store writes whole 128-byte lines.
 #include <type_traits>
 
+#include "../../include/attn.h"
 #include "device_common.h"
 
 namespace attn {
@@ -253,7 +254,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
-                        int n_qtiles, int total, TileDecode td, int causal_off, float scale_log2) {
+                        int n_qtiles, int total, TileDecode td, int causal_off, attn_strides_t st,
+                        float scale_log2) {
   constexpr int kDT = D / 16;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
   constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
@@ -292,11 +294,11 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int qlast = qw + 31;           // last query of this wave
   const int qi = qw + l32;             // this lane's query
 
-  const int64_t q_row_stride = (int64_t)Hq * D;
-  const int64_t kv_row_stride = (int64_t)Hkv * D;
+  // element strides {batch, token, head}; k and v share their token stride
+  const int64_t kv_row_stride = st.k[1];
   const int kv_row_bytes = (int)(kv_row_stride * 2);
-  const i32x4 kdesc = make_desc(k + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
-  const i32x4 vdesc = make_desc(v + ((int64_t)b * M * Hkv + kvh) * D, kv_row_stride, M, D);
+  const i32x4 kdesc = make_desc(k + b * st.k[0] + kvh * st.k[2], kv_row_stride, M, D);
+  const i32x4 vdesc = make_desc(v + b * st.v[0] + kvh * st.v[2], kv_row_stride, M, D);
   const uint32_t voff = F::voff_lane(wave, lane, kv_row_bytes);
 
   // ---- per-lane LDS operand addresses ----
@@ -339,8 +341,8 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
   // ---- prologue: Q^T to registers, K(0), V(0), K(1) to LDS; S(0) ----
   {
-    // rows past N read as zero; the host keeps (N + kBM) rows below 2^32 bytes
-    const uint16_t* qp = q + ((int64_t)b * N + qi) * q_row_stride + (int64_t)h * D + 8 * g;
+    // rows past N are not read (their queries are never stored)
+    const uint16_t* qp = q + b * st.q[0] + (int64_t)qi * st.q[1] + h * st.q[2] + 8 * g;
 #pragma unroll
     for (int t = 0; t < kDT; ++t)
       qreg[t] = (qi < N) ? *reinterpret_cast<const s16x8*>(qp + 16 * t) : (s16x8){};
@@ -672,7 +674,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     for (int k = 0; k < kReads; ++k) {
       const int qrow = qw + k * kRowsPerRead + lane / kCh;
       if (qrow < N)
-        *reinterpret_cast<s16x8*>(o + ((int64_t)b * N + qrow) * q_row_stride + (int64_t)h * D + 8 * c) = val[k];
+        *reinterpret_cast<s16x8*>(o + b * st.o[0] + (int64_t)qrow * st.o[1] + h * st.o[2] + 8 * c) = val[k];
     }
   }
   if (lse != nullptr && g == 0 && qi < N) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
@@ -681,7 +683,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 // Host-side launcher (one instance per head dim, dtype and mask).
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          int Hkv, int N, int M, float scale, hipStream_t stream) {
+                          int Hkv, int N, int M, float scale, const attn_strides_t& st, hipStream_t stream) {
   // query heads per workgroup: the largest power of two that divides the GQA
   // group and leaves at least 64 rows (one K/V tile) per head
   const int group = Hq / Hkv;
@@ -702,15 +704,15 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
                       group, pack_shift};
   hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, M, Hq,
-                     Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, scale * kLog2e);
+                     Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, st, scale * kLog2e);
   return hipGetLastError();
 }
 
 hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                             int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
-                            hipStream_t stream) {
+                            const attn_strides_t& st, hipStream_t stream) {
 #define ATTN_PREFILL_CASE(DD, BB, CC) \
-  if (d == DD && bf16 == BB && causal == CC) return launch_prefill<DD, BB, CC>(q, k, v, o, lse, B, Hq, Hkv, N, M, scale, stream);
+  if (d == DD && bf16 == BB && causal == CC) return launch_prefill<DD, BB, CC>(q, k, v, o, lse, B, Hq, Hkv, N, M, scale, st, stream);
   ATTN_PREFILL_CASE(64, false, false)
   ATTN_PREFILL_CASE(64, false, true)
   ATTN_PREFILL_CASE(64, true, false)

@@ -30,6 +30,7 @@
 #define ATTN_MI355X_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -55,8 +56,20 @@ typedef enum {
   ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (hipGetLastError) */
   ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
   ATTN_ERR_ALIGNMENT = -10,     /* a tensor pointer is not 16-byte aligned */
-  ATTN_ERR_SCALE = -11          /* scale is negative, infinite or NaN */
+  ATTN_ERR_SCALE = -11,         /* scale is negative, infinite or NaN */
+  ATTN_ERR_LAYOUT = -12         /* strides: negative, not a multiple of 8 elements, or k and v
+                                   token strides differ or are below d */
 } attn_status_t;
+
+/*
+ * Element strides of the four prefill tensors, each {batch, token, head}; the
+ * head-dimension elements of one (batch, token, head) are contiguous.  For the
+ * contiguous layouts of attn_fwd they are q, o: {N*Hq*d, Hq*d, d} and
+ * k, v: {M*Hkv*d, Hkv*d, d}.
+ */
+typedef struct {
+  int64_t q[3], k[3], v[3], o[3];
+} attn_strides_t;
 
 /*
  * attn_fwd - fused multi-head / grouped-query attention forward (prefill).
@@ -77,6 +90,22 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
              attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_strided - attn_fwd on tensors laid out with arbitrary element strides
+ * (views such as the q, k, v slices of one fused [B, N, 3, H, d] projection, or
+ * head-major [B, H, N, d] tensors); same operation, masks, outputs and errors as
+ * attn_fwd ("fmha sm120: beyond torch.sdpa", sections 1 and 2).  lse stays
+ * [B, Hq, N] contiguous.  strides == NULL means the contiguous layouts.  Every
+ * stride must be >= 0 and a multiple of 8 elements (so that every row of d
+ * values starts 16-byte aligned), and k and v must share one token stride of at
+ * least d (otherwise ATTN_ERR_LAYOUT).  The largest element offset of each tensor must
+ * stay below 2^31, and (M + 64) times the k/v token stride below 2^31
+ * (otherwise ATTN_ERR_TOO_LARGE).  Outputs must not overlap inputs or each other.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
+                     attn_dtype_t dtype, const attn_strides_t* strides, hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes - bytes of fp32 partials that one split-KV decode call

@@ -26,7 +26,8 @@ def status_codes():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "lse_merge", "attn_status_string"])
+        ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv", "lse_merge",
+         "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -71,6 +72,56 @@ def fwd(**kw):
 ])
 def test_attn_fwd_rejects(kw, code):
     assert fwd(**kw) == code
+
+
+def contiguous_strides(B=1, Hq=2, Hkv=2, N=128, M=128, d=64):
+    s = _lib.Strides()
+    s.q[:] = [N * Hq * d, Hq * d, d]
+    s.o[:] = [N * Hq * d, Hq * d, d]
+    s.k[:] = [M * Hkv * d, Hkv * d, d]
+    s.v[:] = [M * Hkv * d, Hkv * d, d]
+    return s
+
+
+def fwd_strided(edit=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, N=128, M=128, d=64,
+             causal=0, scale=0.125, dtype=0, stream=None)
+    a.update(kw)
+    st = contiguous_strides(a["B"], a["Hq"], a["Hkv"], a["N"], a["M"], a["d"])
+    if edit:
+        edit(st)
+    return _lib.load().attn_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                        a["Hkv"], a["N"], a["M"], a["d"], a["causal"], a["scale"],
+                                        a["dtype"], ctypes.byref(st), a["stream"])
+
+
+def _set(field, i, val):
+    def edit(st):
+        getattr(st, field)[i] = val
+    return edit
+
+
+@pytest.mark.parametrize("edit,kw,code", [
+    (None, dict(q=None), -1), (None, dict(N=0), -2), (None, dict(d=96), -3), (None, dict(dtype=3), -4),
+    (None, dict(Hq=6, Hkv=4), -5), (None, dict(causal=1, N=256, M=128), -6),
+    (None, dict(scale=float("nan")), -11),
+    (_set("q", 1, -128), {}, -12), (_set("o", 2, 4), {}, -12), (_set("v", 0, 12), {}, -12),
+    (_set("v", 1, 256), {}, -12),      # k and v token strides differ
+    (_set("k", 1, 32), {}, -12),       # token stride below d (same for v)
+    (_set("q", 0, 1 << 31), {}, -9),   # largest q offset beyond 2^31 elements (needs B > 1)
+    (None, dict(q=FAKE + 8), -10),
+])
+def test_attn_fwd_strided_rejects(edit, kw, code):
+    if code == -9:
+        kw = dict(B=2)
+    assert fwd_strided(edit, **kw) == code
+
+
+def test_attn_fwd_strided_k_v_equal_small_token_stride_rejected():
+    def edit(st):
+        st.k[1] = 32
+        st.v[1] = 32
+    assert fwd_strided(edit) == -12
 
 
 def dec(**kw):

@@ -162,6 +162,40 @@ def test_prefill_causal_chunk_matches_full_rows():
         assert maxerr(Lc, Lf[:, :, 700 - n:]) <= 2 * TOL_LSE, n
 
 
+def test_prefill_strided_layouts():
+    """Strided views through attn_fwd_strided: q, k, v as slices of one fused
+    [B, N, 3, H, d] projection; head-major [B, H, N, d] tensors transposed to
+    [B, N, H, d] with a head-major output; results equal the contiguous call
+    bit for bit (the same kernel work per (batch, head))."""
+    say("case prefill strided layouts")
+    g = torch.Generator("cpu").manual_seed(4321)
+    B, N, H, d = 2, 333, 4, 128
+    qkv = torch.randn((B, N, 3, H, d), generator=g).to(torch.bfloat16).to(DEV)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert not q.is_contiguous()
+    scale = float(np.float32(d ** -0.5))
+    for causal in (False, True):
+        o_s, l_s = attn().attn_fwd(q, k, v, causal=causal, scale=scale)
+        o_c, l_c = attn().attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o_s, o_c) and torch.equal(l_s, l_c), causal
+        Or, Lr = oracle.attn_ref(q.cpu(), k.cpu(), v.cpu(), scale, causal)
+        assert maxerr(f64(o_s), Or) <= TOL_O["bf16"] and maxerr(f64(l_s), Lr) <= TOL_LSE
+    # head-major storage, GQA, fp16, d = 64, N < M causal, head-major output
+    Hq, Hkv, N, M, d = 8, 2, 200, 264, 64
+    qh = torch.randn((1, Hq, N, d), generator=g).to(torch.float16).to(DEV)
+    kh = torch.randn((1, Hkv, M, d), generator=g).to(torch.float16).to(DEV)
+    vh = torch.randn((1, Hkv, M, d), generator=g).to(torch.float16).to(DEV)
+    oh = torch.empty((1, Hq, N, d), dtype=torch.float16, device=DEV)
+    q, k, v, o = (t.transpose(1, 2) for t in (qh, kh, vh, oh))
+    attn().attn_fwd(q, k, v, causal=True, scale=0.125, o=o)
+    o_c, _ = attn().attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(oh.transpose(1, 2), o_c)
+    Or, _ = oracle.attn_ref(q.cpu(), k.cpu(), v.cpu(), 0.125, True)
+    assert maxerr(f64(o), Or) <= TOL_O["f16"]
+
+
 def test_prefill_deterministic():
     say("case prefill determinism")
     q, k, v = prefill_inputs(1, 8, 2, 520, 520, 128, "bf16", 5)
