@@ -16,7 +16,8 @@
 //  * merge kernel: one workgroup per (batch, query head, 16-column slice of d),
 //    one pass over the partials with a running max (no separate pass for the
 //    global log-sum-exp, no limit on the number of chunks), 16-byte loads, and
-//    eight independent loads in flight per thread.
+//    eight independent loads in flight per thread; the 64 per-thread states
+//    of a column are combined by lane shuffles and one LDS step.
 #include <algorithm>
 
 #include "device_common.h"
@@ -174,62 +175,81 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeCols = 16;                          // d columns per workgroup
 constexpr int kMergeGroups = kMergeThreads / (kMergeCols / 4);  // chunk groups (64)
 
+// (m, s, a[4]) merge of two running states, in log2 units: both rescaled to
+// the larger reference max.  A state with m = -inf (no chunk yet) is empty.
+struct MergeState {
+  float m, s, a[4];
+};
+__device__ __forceinline__ MergeState merge_states(const MergeState& x, const MergeState& y) {
+  const float mm = fmaxf(x.m, y.m);
+  const float rx = (x.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x.m - mm);
+  const float ry = (y.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(y.m - mm);
+  MergeState r;
+  r.m = mm;
+  r.s = fmaf(x.s, rx, y.s * ry);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.a[c] = fmaf(x.a[c], rx, y.a[c] * ry);
+  return r;
+}
+
 // One pass over the partials: each thread walks chunks grp, grp + 64, ... of one
 // (batch, head) and 4 consecutive columns, keeping a running max of lse_c (log2
 // units) with the matching rescaled weight sum and weighted output; the 64
-// groups are then combined with the same rule.  O = sum_c 2^(l_c - M) O_c /
-// sum_c 2^(l_c - M) for any reference M equals sum_c w_c O_c.
+// group states are then combined with the same rule, first across the lanes
+// of each wave (xor shuffles over the group bits of the lane id), then across
+// the 4 waves.  O = sum_c 2^(l_c - M) O_c / sum_c 2^(l_c - M) for any
+// reference M equals sum_c w_c O_c.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kMergeThreads)
 void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                       uint16_t* __restrict__ o, float* __restrict__ lse, int C) {
-  __shared__ float sm[kMergeGroups], ss[kMergeGroups];
-  __shared__ float sacc[kMergeGroups][kMergeCols + 1];
+  constexpr int kWaves = kMergeThreads / 64;
+  __shared__ MergeState part[kWaves][4];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cq = tid & 3, grp = tid >> 2;
   const int bh = blockIdx.x;
   const int col0 = blockIdx.y * kMergeCols + cq * 4;
   const float* lp = lse_part + (int64_t)bh * C;
   const float* op = o_part + (int64_t)bh * C * D + col0;
 
-  float m = -INFINITY, s = 0.f;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
   for (int c = grp; c < C; c += kMergeGroups) {
     const float l2 = lp[c] * kLog2e;
     const float4 ov = *reinterpret_cast<const float4*>(op + (int64_t)c * D);
-    const float mn = fmaxf(m, l2);
-    const float r = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first chunk (m = -inf)
+    const float mn = fmaxf(st.m, l2);
+    const float r = __builtin_amdgcn_exp2f(st.m - mn);   // 0 on the first chunk (m = -inf)
     const float w = __builtin_amdgcn_exp2f(l2 - mn);
-    s = fmaf(s, r, w);
-    a0 = fmaf(a0, r, w * ov.x);
-    a1 = fmaf(a1, r, w * ov.y);
-    a2 = fmaf(a2, r, w * ov.z);
-    a3 = fmaf(a3, r, w * ov.w);
-    m = mn;
+    st.s = fmaf(st.s, r, w);
+    st.a[0] = fmaf(st.a[0], r, w * ov.x);
+    st.a[1] = fmaf(st.a[1], r, w * ov.y);
+    st.a[2] = fmaf(st.a[2], r, w * ov.z);
+    st.a[3] = fmaf(st.a[3], r, w * ov.w);
+    st.m = mn;
   }
-  if (cq == 0) {
-    sm[grp] = m;
-    ss[grp] = s;
+  // lanes that share cq differ in lane bits 2..5
+#pragma unroll
+  for (int mask = 4; mask < 64; mask <<= 1) {
+    MergeState y;
+    y.m = __shfl_xor(st.m, mask);
+    y.s = __shfl_xor(st.s, mask);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y.a[c] = __shfl_xor(st.a[c], mask);
+    st = merge_states(st, y);
   }
-  sacc[grp][cq * 4 + 0] = a0;
-  sacc[grp][cq * 4 + 1] = a1;
-  sacc[grp][cq * 4 + 2] = a2;
-  sacc[grp][cq * 4 + 3] = a3;
+  if (lane < 4) part[wave][lane] = st;
   __syncthreads();
-  if (tid < kMergeCols) {
-    float M = -INFINITY;
-    for (int gi = 0; gi < kMergeGroups; ++gi) M = fmaxf(M, sm[gi]);
-    float S = 0.f, A = 0.f;
-    for (int gi = 0; gi < kMergeGroups; ++gi) {
-      const float r = (sm[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[gi] - M);
-      S = fmaf(ss[gi], r, S);
-      A = fmaf(sacc[gi][tid], r, A);
-    }
-    const int d = blockIdx.y * kMergeCols + tid;
-    o[(int64_t)bh * D + d] = (uint16_t)(pack2<BF16>(A / S, 0.f) & 0xffffu);
-    if (blockIdx.y == 0 && tid == 0 && lse != nullptr) lse[bh] = (M + log2f(S)) * kLn2;
+  if (tid < 4) {
+    MergeState r = part[0][tid];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = merge_states(r, part[w][tid]);
+    const float inv = 1.f / r.s;
+    const int d0 = blockIdx.y * kMergeCols + tid * 4;
+    const uint32_t w01 = pack2<BF16>(r.a[0] * inv, r.a[1] * inv);
+    const uint32_t w23 = pack2<BF16>(r.a[2] * inv, r.a[3] * inv);
+    *reinterpret_cast<uint2*>(o + (int64_t)bh * D + d0) = make_uint2(w01, w23);
+    if (blockIdx.y == 0 && tid == 0 && lse != nullptr) lse[bh] = (r.m + log2f(r.s)) * kLn2;
   }
 }
 
