@@ -58,8 +58,10 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
 }
 
 // Persistent grid: workgroup w handles items w, w + gridDim.x, ... where item
-// = c + C * (b * Hq + h), so every workgroup ends at about the same time.
-template <int D, bool BF16>
+// = c + C * (G-head slice of one GQA group, b, kv head), so every workgroup
+// ends at about the same time.  An item reads its chunk of K and V once and
+// serves G query heads of the group that share them (G = 1 without GQA).
+template <int D, bool BF16, int G>
 __global__ __launch_bounds__(kDecThreads)
 void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, float* __restrict__ o_part,
@@ -69,24 +71,30 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int kRowsPerPass = kDecThreads / kLanes;  // 16 (d=128) or 32 (d=64)
   constexpr int kPasses = kChunk / kRowsPerPass;      // rows per thread
   constexpr int kWaves = kDecThreads / 64;
-  __shared__ float red[2][kWaves];
-  __shared__ float opart[kWaves][D];
+  __shared__ float red[2][kWaves][G];
+  __shared__ float opart[kWaves][G][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = tid % kLanes;  // 16-byte column chunk
   const int r0 = tid / kLanes;   // first row of this thread
+  const int group = Hq / Hkv;
+  const int slices = group / G;  // G-head slices per GQA group
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int c = item % C;
-    const int bh = item / C;
-    const int h = bh % Hq, b = bh / Hq;
-    const int kvh = h / (Hq / Hkv);
+    const int rest = item / C;
+    const int hs = rest % slices, bkv = rest / slices;
+    const int kvh = bkv % Hkv, b = bkv / Hkv;
+    const int h0 = kvh * group + hs * G;  // first query head of this item
     const int key0 = c * kChunk;
     const int len = min(kChunk, M - key0);
 
     const uint16_t* kp = k + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
     const uint16_t* vp = v + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
-    const uint4 qv = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h) * D + col * 8);
+    uint4 qv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      qv[i] = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h0 + i) * D + col * 8);
 
     // issue the whole chunk: K then V
     uint4 kr[kPasses], vr[kPasses];
@@ -101,71 +109,100 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       vr[p] = row < len ? load_stream(vp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
     }
 
-    // scores in log2 units: x_j = scale * log2(e) * q.k_j
-    float x[kPasses];
-    float mx = -INFINITY;
+    // scores in log2 units: x_j = scale * log2(e) * q.k_j, per head
+    float x[kPasses][G];
+    float mx[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) mx[i] = -INFINITY;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int row = r0 + p * kRowsPerPass;
-      const float sdot = row_sum<kLanes>(dot8<BF16>(qv, kr[p], 0.f));
-      x[p] = row < len ? sdot * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[p]);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float sdot = row_sum<kLanes>(dot8<BF16>(qv[i], kr[p], 0.f));
+        x[p][i] = row < len ? sdot * scale_log2 : -INFINITY;
+        mx[i] = fmaxf(mx[i], x[p][i]);
+      }
     }
     // chunk max: over the rows of this wave, then over the waves
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = max_xor32(mx);
-    if (kLanes == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
-    if (lane == 0) red[0][wave] = mx;
-    __syncthreads();
-    float m = red[0][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[0][w]);
+    for (int i = 0; i < G; ++i) {
+      float m = fmaxf(mx[i], __shfl_xor(mx[i], 16));
+      m = max_xor32(m);
+      if (kLanes == 8) m = fmaxf(m, __shfl_xor(m, 8));
+      if (lane == 0) red[0][wave][i] = m;
+    }
+    __syncthreads();
+    float m[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      m[i] = red[0][0][i];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m[i] = fmaxf(m[i], red[0][w][i]);
+    }
 
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
+    float acc[G][8];
+    float l[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      l[i] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[i][t] = 0.f;
+    }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int row = r0 + p * kRowsPerPass;
-      const float e = row < len ? __builtin_amdgcn_exp2f(x[p] - m) : 0.f;
-      l += e;
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[p]);
+      f32x2 vv[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x2 vv = unpack2<BF16>(vw[t]);
-        acc[2 * t] = fmaf(e, vv[0], acc[2 * t]);
-        acc[2 * t + 1] = fmaf(e, vv[1], acc[2 * t + 1]);
+      for (int t = 0; t < 4; ++t) vv[t] = unpack2<BF16>(vw[t]);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float e = row < len ? __builtin_amdgcn_exp2f(x[p][i] - m[i]) : 0.f;
+        l[i] += e;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[i][2 * t] = fmaf(e, vv[t][0], acc[i][2 * t]);
+          acc[i][2 * t + 1] = fmaf(e, vv[t][1], acc[i][2 * t + 1]);
+        }
       }
     }
-    // l: the lanes of a row group hold the same e; sum over the row groups of
-    // the wave, then across waves.
-    l += __shfl_xor(l, 16);
-    l = sum_xor32(l);
-    if (kLanes == 8) l += __shfl_xor(l, 8);
-    // column partials: reduce the lanes that share a column chunk
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float a = acc[t];
-      if (kLanes == 8) a += __shfl_xor(a, 8);
-      a += __shfl_xor(a, 16);
-      a = sum_xor32(a);
-      acc[t] = a;
-    }
-    if (lane < kLanes) {
+    for (int i = 0; i < G; ++i) {
+      // l: the lanes of a row group hold the same e; sum over the row groups
+      // of the wave, then across waves.
+      float li = l[i] + __shfl_xor(l[i], 16);
+      li = sum_xor32(li);
+      if (kLanes == 8) li += __shfl_xor(li, 8);
+      // column partials: reduce the lanes that share a column chunk
 #pragma unroll
-      for (int t = 0; t < 8; ++t) opart[wave][lane * 8 + t] = acc[t];
+      for (int t = 0; t < 8; ++t) {
+        float a = acc[i][t];
+        if (kLanes == 8) a += __shfl_xor(a, 8);
+        a += __shfl_xor(a, 16);
+        a = sum_xor32(a);
+        acc[i][t] = a;
+      }
+      if (lane < kLanes) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) opart[wave][i][lane * 8 + t] = acc[i][t];
+      }
+      if (lane == 0) red[1][wave][i] = li;
     }
-    if (lane == 0) red[1][wave] = l;
     __syncthreads();
     if (tid < D) {
-      float lt = 0.f, ot = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        lt += red[1][w];
-        ot += opart[w][tid];
+      for (int i = 0; i < G; ++i) {
+        float lt = 0.f, ot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          lt += red[1][w][i];
+          ot += opart[w][i][tid];
+        }
+        const int64_t base = ((int64_t)b * Hq + h0 + i) * C + c;
+        o_part[base * D + tid] = ot / lt;
+        if (tid == 0) lse_part[base] = (m[i] + log2f(lt)) * kLn2;
       }
-      const int64_t base = (int64_t)bh * C + c;
-      o_part[base * D + tid] = ot / lt;
-      if (tid == 0) lse_part[base] = (m + log2f(lt)) * kLn2;
     }
     __syncthreads();  // opart / red reused by the next item
   }
@@ -273,21 +310,23 @@ static int resident_grid(K kernel, int threads) {
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                            int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream) {
   const int C = (M + kChunk - 1) / kChunk;
-  const int n_items = B * Hq * C;
   const float sl2 = scale * kLog2e;
-#define ATTN_DEC_CASE(DD, BB)                                                                          \
-  if (d == DD && bf16 == BB) {                                                                         \
-    static_assert(DD % 8 == 0, "");                                                                    \
-    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB>, kDecThreads));       \
-    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,        \
+  // query heads per item: the largest of 4, 2, 1 that divides the GQA group
+  const int group = Hq / Hkv;
+  const int g = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  const int n_items = B * (Hq / g) * C;
+#define ATTN_DEC_CASE(DD, BB, GG)                                                                      \
+  if (d == DD && bf16 == BB && g == GG) {                                                              \
+    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB, GG>, kDecThreads));   \
+    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB, GG>), dim3(grid), dim3(kDecThreads), 0, stream,    \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
                        Hq, Hkv, M, C, n_items, sl2);                                                   \
     return hipGetLastError();                                                                          \
   }
-  ATTN_DEC_CASE(64, false)
-  ATTN_DEC_CASE(64, true)
-  ATTN_DEC_CASE(128, false)
-  ATTN_DEC_CASE(128, true)
+  ATTN_DEC_CASE(64, false, 1) ATTN_DEC_CASE(64, false, 2) ATTN_DEC_CASE(64, false, 4)
+  ATTN_DEC_CASE(64, true, 1) ATTN_DEC_CASE(64, true, 2) ATTN_DEC_CASE(64, true, 4)
+  ATTN_DEC_CASE(128, false, 1) ATTN_DEC_CASE(128, false, 2) ATTN_DEC_CASE(128, false, 4)
+  ATTN_DEC_CASE(128, true, 1) ATTN_DEC_CASE(128, true, 2) ATTN_DEC_CASE(128, true, 4)
 #undef ATTN_DEC_CASE
   return hipErrorInvalidValue;
 }

@@ -279,6 +279,11 @@ DEC_SHAPES = [
     (2, 8, 2, 1000, 128, "bf16"),
     (1, 4, 4, 129, 64, "bf16"),
     (3, 16, 4, 4096, 128, "f16"),
+    # GQA groups of 3, 6, 8 and 16: one item serves 1, 2, 4 and 4 query heads
+    (2, 24, 8, 777, 128, "bf16"),
+    (1, 12, 2, 300, 64, "f16"),
+    (2, 32, 4, 2049, 128, "bf16"),
+    (1, 16, 1, 513, 64, "bf16"),
 ]
 
 
