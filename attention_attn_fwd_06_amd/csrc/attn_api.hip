@@ -115,7 +115,8 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
   if (chunk_size != kDecodeChunk) return ATTN_ERR_CHUNK_SIZE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
   const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
-  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535)
+  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535 ||
+      (int64_t)(M + kDecodeChunk) * d >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u))

@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "lds_stage.h"
 
 namespace attn {
 
@@ -208,6 +209,188 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 }
 
+// GQA decode on the matrix cores.  Item = (chunk c of 128 keys, batch b, kv
+// head, slice of G <= 16 query heads of its group).  The G heads are the 16
+// columns of v_mfma_f32_16x16x32 (columns >= G carry q = 0 and are never
+// stored):
+//   S^T[key][head] = K Q^T   A = K rows loaded from HBM straight into VGPRs,
+//                            B = Q^T (the q rows of the slice's heads)
+//   O^T[d][head]  = V^T P^T  A = V^T via ds_read_b64_tr_b16 from the V chunk
+//                            fetched into LDS (swizzled, rows past M read as
+//                            zeros), B = P^T from LDS as hi + lo 16-bit parts
+// so the chunk's K and V are read from HBM once for all G heads.  Wave w
+// scores keys 32w .. 32w + 31 and accumulates d rows w*D/4 .. +D/4 - 1 over all
+// 128 keys.  The chunk max and sum are exchanged through LDS; P is the fp32
+// 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
+// accuracy in P while l is the sum of the unrounded values.
+constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
+constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kDecThreads)
+void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                            const uint16_t* __restrict__ v, float* __restrict__ o_part,
+                            float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
+                            int n_items, float scale_log2) {
+  constexpr int kS = D / 32;                        // QK contraction steps
+  constexpr int kDB = D / 64;                       // 16-row d blocks per wave
+  constexpr int kWaves = kDecThreads / 64;
+  constexpr int kU = D / 8;                         // 16-byte units per row
+  constexpr int kRowsPerInst = kDecThreads / kU;    // rows per fetch instruction index
+  constexpr int kFetch = kChunk / kRowsPerInst;     // fetch instructions per wave
+  constexpr uint32_t kPBytes = kGqaCols * kPRow * 2;  // one P part
+  static_assert(kRowsPerInst % 16 == 0, "swizzle must repeat across fetch instructions");
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2 * kGqaCols * kPRow];
+  __shared__ float red[2][kWaves][kGqaCols];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int group = Hq / Hkv, slices = group / G;
+  const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_u16*)vbuf;
+  const uint32_t p_lds = (uint32_t)(uintptr_t)(lds_u16*)pbuf;
+  const bool out16 = ((uintptr_t)o_part & 15) == 0;
+
+  // V fetch: instruction i of wave w fills LDS units (i*kWaves + w)*64 + lane,
+  // i.e. row kRowsPerInst*i + rl, physical 16-byte chunk pc (holding logical
+  // chunk pc ^ swz(row)).
+  const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
+  const uint32_t voff_lane = (uint32_t)(rl * D * 2 + ((pc ^ swz<D>(rl)) << 4));
+  // V^T operand: in each 16-lane group of a ds_read_b64_tr_b16, lane s
+  // addresses V[K0 + s/4][D0 + 4*(s%4)], so lane i receives V[K0 + 0..3][D0 + i].
+  // Group g reads keys 32*ks + 8*g + 4*hh + 0..3 (k-step ks, half hh): slots
+  // 8g .. 8g + 7 of the k-step, the same key order the P^T read uses.
+  uint32_t va[kDB][2];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 8 * g + 4 * hh + (j >> 2);
+      const int col = wave * (D / 4) + 16 * db + 4 * (j & 3);
+      va[db][hh] = v_lds + (uint32_t)(row * D * 2 + ((((col >> 3) ^ swz<D>(row)) << 4) | ((col & 7) * 2)));
+    }
+  }
+  const uint32_t pa = p_lds + (uint32_t)((j * kPRow + 8 * g) * 2);               // P[j][32ks + 8g ..]
+  const uint32_t pw = p_lds + (uint32_t)((j * kPRow + 32 * wave + 4 * g) * 2);   // P[j][32w + 16kb + 4g ..]
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int c = item % C;
+    const int rest = item / C;
+    const int hs = rest % slices, bkv = rest / slices;
+    const int kvh = bkv % Hkv, b = bkv / Hkv;
+    const int h0 = kvh * group + hs * G;  // first query head of this item
+    const int key0 = c * kChunk;
+    const int len = min(kChunk, M - key0);
+    const int64_t slice = ((int64_t)b * Hkv + kvh) * M * D;
+
+    // V chunk -> LDS, no registers (bounds-checked: rows past M are zeros)
+    const i32x4 vdesc = make_desc(v + slice, D, M, D);
+#pragma unroll
+    for (int i = 0; i < kFetch; ++i)
+      dma16(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+            voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+
+    // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7
+    s16x8 ka[2][kS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * wave + 16 * kb + j;
+      const uint16_t* kp = k + slice + (int64_t)(key0 + row) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const uint4 t = row < len ? load_stream(kp + 32 * s) : make_uint4(0, 0, 0, 0);
+        ka[kb][s] = __builtin_bit_cast(s16x8, t);
+      }
+    }
+    // B operand of S^T: q of head h0 + j, d = 32s + 8g .. +7
+    s16x8 qb[kS];
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+      qb[s] = j < G ? *reinterpret_cast<const s16x8*>(q + ((int64_t)b * Hq + h0 + j) * D + 32 * s + 8 * g)
+                    : (s16x8){};
+
+    // scores in log2 units; element r of block kb is key 32w + 16kb + 4g + r
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 sa = {};
+#pragma unroll
+      for (int s = 0; s < kS; ++s) sa = mfma16x16x32<BF16>(ka[kb][s], qb[s], sa);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 32 * wave + 16 * kb + 4 * g + r;
+        x[kb][r] = key < len ? sa[r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[kb][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = max_xor32(mx);
+    if (g == 0) red[0][wave][j] = mx;
+    wait_tile_loads();  // this wave's part of the V chunk is in LDS
+    __syncthreads();    // V chunk and the per-wave maxima visible
+    float m = red[0][0][j];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[0][w][j]);
+
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(x[kb][r] - m);
+        lsum += p[r];
+      }
+      const uint32_t h01 = pack2<BF16>(p[0], p[1]), h23 = pack2<BF16>(p[2], p[3]);
+      const f32x2 r01 = unpack2<BF16>(h01), r23 = unpack2<BF16>(h23);
+      const uint32_t l01 = pack2<BF16>(p[0] - r01[0], p[1] - r01[1]);
+      const uint32_t l23 = pack2<BF16>(p[2] - r23[0], p[3] - r23[1]);
+      lds_write_b64(pw + 32u * kb, (u32x2){h01, h23});
+      lds_write_b64(pw + kPBytes + 32u * kb, (u32x2){l01, l23});
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum = sum_xor32(lsum);
+    if (g == 0) red[1][wave][j] = lsum;
+    __syncthreads();  // P and the per-wave sums visible
+
+    f32x4 oacc[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) oacc[db] = (f32x4){};
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 32; ++ks) {
+      const s16x8 ph = lds_read_b128(pa + 64u * ks);
+      const s16x8 pl = lds_read_b128(pa + kPBytes + 64u * ks);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const s16x4 lo = lds_read_tr16_b64(va[db][0] + (uint32_t)(32 * ks * D * 2));
+        const s16x4 hi = lds_read_tr16_b64(va[db][1] + (uint32_t)(32 * ks * D * 2));
+        const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = mfma16x16x32<BF16>(a, ph, oacc[db]);
+        oacc[db] = mfma16x16x32<BF16>(a, pl, oacc[db]);
+      }
+    }
+    float lt = red[1][0][j];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) lt += red[1][w][j];
+    if (j < G) {
+      const int64_t base = ((int64_t)b * Hq + h0 + j) * C + c;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        float* op = o_part + base * D + wave * (D / 4) + 16 * db + 4 * g;
+        const float4 o4 = make_float4(oacc[db][0] / lt, oacc[db][1] / lt, oacc[db][2] / lt, oacc[db][3] / lt);
+        if (out16) {
+          *reinterpret_cast<float4*>(op) = o4;
+        } else {
+          op[0] = o4.x; op[1] = o4.y; op[2] = o4.z; op[3] = o4.w;
+        }
+      }
+      if (wave == 0 && g == 0) lse_part[base] = (m + log2f(lt)) * kLn2;
+    }
+    __syncthreads();  // V, P and the sums are refilled by the next item
+  }
+}
+
 constexpr int kMergeThreads = 256;
 constexpr int kMergeCols = 16;                          // d columns per workgroup
 constexpr int kMergeGroups = kMergeThreads / (kMergeCols / 4);  // chunk groups (64)
@@ -311,22 +494,35 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
                            int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream) {
   const int C = (M + kChunk - 1) / kChunk;
   const float sl2 = scale * kLog2e;
-  // query heads per item: the largest of 4, 2, 1 that divides the GQA group
   const int group = Hq / Hkv;
-  const int g = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-  const int n_items = B * (Hq / g) * C;
-#define ATTN_DEC_CASE(DD, BB, GG)                                                                      \
-  if (d == DD && bf16 == BB && g == GG) {                                                              \
-    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB, GG>, kDecThreads));   \
-    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB, GG>), dim3(grid), dim3(kDecThreads), 0, stream,    \
+  if (group >= 2) {
+    // query heads per item: the largest divisor of the group that fits the
+    // 16 MFMA columns
+    int g = std::min(group, kGqaCols);
+    while (group % g != 0) --g;
+    const int n_items = B * (Hq / g) * C;
+#define ATTN_GQA_CASE(DD, BB)                                                                          \
+    if (d == DD && bf16 == BB) {                                                                       \
+      const int grid = std::min(n_items, resident_grid(decode_gqa_mfma_kernel<DD, BB>, kDecThreads));  \
+      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,   \
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, \
+                         Hq, Hkv, M, C, g, n_items, sl2);                                              \
+      return hipGetLastError();                                                                        \
+    }
+    ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)
+#undef ATTN_GQA_CASE
+    return hipErrorInvalidValue;
+  }
+  const int n_items = B * Hq * C;
+#define ATTN_DEC_CASE(DD, BB)                                                                          \
+  if (d == DD && bf16 == BB) {                                                                         \
+    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB, 1>, kDecThreads));    \
+    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB, 1>), dim3(grid), dim3(kDecThreads), 0, stream,     \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
                        Hq, Hkv, M, C, n_items, sl2);                                                   \
     return hipGetLastError();                                                                          \
   }
-  ATTN_DEC_CASE(64, false, 1) ATTN_DEC_CASE(64, false, 2) ATTN_DEC_CASE(64, false, 4)
-  ATTN_DEC_CASE(64, true, 1) ATTN_DEC_CASE(64, true, 2) ATTN_DEC_CASE(64, true, 4)
-  ATTN_DEC_CASE(128, false, 1) ATTN_DEC_CASE(128, false, 2) ATTN_DEC_CASE(128, false, 4)
-  ATTN_DEC_CASE(128, true, 1) ATTN_DEC_CASE(128, true, 2) ATTN_DEC_CASE(128, true, 4)
+  ATTN_DEC_CASE(64, false) ATTN_DEC_CASE(64, true) ATTN_DEC_CASE(128, false) ATTN_DEC_CASE(128, true)
 #undef ATTN_DEC_CASE
   return hipErrorInvalidValue;
 }

@@ -35,6 +35,22 @@ __device__ __forceinline__ f32x16 mfma32x32x16(s16x8 a, s16x8 b, f32x16 c) {
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// D[16x16] += A[16x32] * B[32x16] in fp32.  Lane l supplies row (l % 16) of A
+// and column (l % 16) of B, each as 8 consecutive contraction slots; lane group
+// l / 16 holds slots 8*(l/16) .. +7.  Accumulator element i of lane l is
+// D[4*(l/16) + i][l % 16].
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16x16x32(s16x8 a, s16x8 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Two fp32 values to one packed 16-bit pair (round to nearest even).
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
