@@ -4,15 +4,25 @@
 // flow; section 6: the reduce kernel).
 //
 // MI355X design (not the page's CUDA design):
-//  * chunk kernel: persistent grid of 256-thread workgroups (as many as fit
-//    on the chip at once), each taking (chunk of 128 keys, batch, query head)
-//    items in turn, so the grid drains evenly.  Every K and V load of a chunk
-//    (64 KB at d = 128) is issued up front, with a nontemporal hint: V does not depend on the scores, so the whole chunk is in flight
-//    at once and the kernel streams HBM.  A row of K/V (d * 2 bytes) is read by
-//    d/8 consecutive lanes, 16 bytes each (fully coalesced).
-//  * scores use fp32 accumulation (v_dot2_f32_{f16,bf16}) and a DPP sum over the
-//    lanes that share a key row; softmax statistics use exp2 with the scale
-//    folded into one multiply; partials are written in fp32, O_c normalised.
+//  * both chunk kernels run a persistent grid of 256-thread workgroups (as
+//    many as fit on the chip at once) that take chunk items in turn, so the
+//    grid drains evenly.  Every K and V load of a chunk (64 KB at d = 128) is
+//    issued up front with a nontemporal hint: V does not depend on the
+//    scores, so the whole chunk is in flight at once and the kernel streams
+//    HBM.  Partials are written in fp32 (O_c normalised) with nontemporal
+//    stores: through the write-back caches they cost several percent of the
+//    chunk kernel's time.
+//  * matrix-core kernel (GQA groups, and MHA launches of at least 2048
+//    items): an item is (chunk, batch, kv head, up to 16 query heads of the
+//    group), the heads being the columns of v_mfma_f32_16x16x32, so K and V
+//    are read once per kv head; Q, K and V are staged in LDS, V^T read back
+//    through transposed reads.
+//  * VALU kernel (small MHA launches): an item is (chunk, batch, query head);
+//    a row of K/V is read by d/8 consecutive lanes, 16 bytes each, scores use
+//    fp32 accumulation (v_dot2_f32_{f16,bf16}) and a DPP sum over the lanes
+//    of a row.  Its per-item path is shorter, which wins when the grid runs
+//    only a few rounds of items.
+//  * softmax statistics use exp2 with the scale folded into one multiply.
 //  * merge kernel: one workgroup per (batch, query head, 16-column slice of d),
 //    one pass over the partials with a running max (no separate pass for the
 //    global log-sum-exp, no limit on the number of chunks), 16-byte loads, and
@@ -59,10 +69,8 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
 }
 
 // Persistent grid: workgroup w handles items w, w + gridDim.x, ... where item
-// = c + C * (G-head slice of one GQA group, b, kv head), so every workgroup
-// ends at about the same time.  An item reads its chunk of K and V once and
-// serves G query heads of the group that share them (G = 1 without GQA).
-template <int D, bool BF16, int G>
+// = c + C * (b * Hq + h), so every workgroup ends at about the same time.
+template <int D, bool BF16>
 __global__ __launch_bounds__(kDecThreads)
 void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, float* __restrict__ o_part,
@@ -72,30 +80,24 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int kRowsPerPass = kDecThreads / kLanes;  // 16 (d=128) or 32 (d=64)
   constexpr int kPasses = kChunk / kRowsPerPass;      // rows per thread
   constexpr int kWaves = kDecThreads / 64;
-  __shared__ float red[2][kWaves][G];
-  __shared__ float opart[kWaves][G][D];
+  __shared__ float red[2][kWaves];
+  __shared__ float opart[kWaves][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = tid % kLanes;  // 16-byte column chunk
   const int r0 = tid / kLanes;   // first row of this thread
-  const int group = Hq / Hkv;
-  const int slices = group / G;  // G-head slices per GQA group
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int c = item % C;
-    const int rest = item / C;
-    const int hs = rest % slices, bkv = rest / slices;
-    const int kvh = bkv % Hkv, b = bkv / Hkv;
-    const int h0 = kvh * group + hs * G;  // first query head of this item
+    const int bh = item / C;
+    const int h = bh % Hq, b = bh / Hq;
+    const int kvh = h / (Hq / Hkv);
     const int key0 = c * kChunk;
     const int len = min(kChunk, M - key0);
 
     const uint16_t* kp = k + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
     const uint16_t* vp = v + (((int64_t)b * Hkv + kvh) * M + key0) * D + col * 8;
-    uint4 qv[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-      qv[i] = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h0 + i) * D + col * 8);
+    const uint4 qv = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + h) * D + col * 8);
 
     // issue the whole chunk: K then V
     uint4 kr[kPasses], vr[kPasses];
@@ -110,100 +112,71 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       vr[p] = row < len ? load_stream(vp + (int64_t)row * D) : make_uint4(0, 0, 0, 0);
     }
 
-    // scores in log2 units: x_j = scale * log2(e) * q.k_j, per head
-    float x[kPasses][G];
-    float mx[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) mx[i] = -INFINITY;
+    // scores in log2 units: x_j = scale * log2(e) * q.k_j
+    float x[kPasses];
+    float mx = -INFINITY;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int row = r0 + p * kRowsPerPass;
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float sdot = row_sum<kLanes>(dot8<BF16>(qv[i], kr[p], 0.f));
-        x[p][i] = row < len ? sdot * scale_log2 : -INFINITY;
-        mx[i] = fmaxf(mx[i], x[p][i]);
-      }
+      const float sdot = row_sum<kLanes>(dot8<BF16>(qv, kr[p], 0.f));
+      x[p] = row < len ? sdot * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[p]);
     }
     // chunk max: over the rows of this wave, then over the waves
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      float m = fmaxf(mx[i], __shfl_xor(mx[i], 16));
-      m = max_xor32(m);
-      if (kLanes == 8) m = fmaxf(m, __shfl_xor(m, 8));
-      if (lane == 0) red[0][wave][i] = m;
-    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = max_xor32(mx);
+    if (kLanes == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
+    if (lane == 0) red[0][wave] = mx;
     __syncthreads();
-    float m[G];
+    float m = red[0][0];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      m[i] = red[0][0][i];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) m[i] = fmaxf(m[i], red[0][w][i]);
-    }
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[0][w]);
 
-    float acc[G][8];
-    float l[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      l[i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[i][t] = 0.f;
-    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int row = r0 + p * kRowsPerPass;
+      const float e = row < len ? __builtin_amdgcn_exp2f(x[p] - m) : 0.f;
+      l += e;
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[p]);
-      f32x2 vv[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) vv[t] = unpack2<BF16>(vw[t]);
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float e = row < len ? __builtin_amdgcn_exp2f(x[p][i] - m[i]) : 0.f;
-        l[i] += e;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[i][2 * t] = fmaf(e, vv[t][0], acc[i][2 * t]);
-          acc[i][2 * t + 1] = fmaf(e, vv[t][1], acc[i][2 * t + 1]);
-        }
+      for (int t = 0; t < 4; ++t) {
+        const f32x2 vv = unpack2<BF16>(vw[t]);
+        acc[2 * t] = fmaf(e, vv[0], acc[2 * t]);
+        acc[2 * t + 1] = fmaf(e, vv[1], acc[2 * t + 1]);
       }
     }
+    // l: the lanes of a row group hold the same e; sum over the row groups of
+    // the wave, then across waves.
+    l += __shfl_xor(l, 16);
+    l = sum_xor32(l);
+    if (kLanes == 8) l += __shfl_xor(l, 8);
+    // column partials: reduce the lanes that share a column chunk
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      // l: the lanes of a row group hold the same e; sum over the row groups
-      // of the wave, then across waves.
-      float li = l[i] + __shfl_xor(l[i], 16);
-      li = sum_xor32(li);
-      if (kLanes == 8) li += __shfl_xor(li, 8);
-      // column partials: reduce the lanes that share a column chunk
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float a = acc[i][t];
-        if (kLanes == 8) a += __shfl_xor(a, 8);
-        a += __shfl_xor(a, 16);
-        a = sum_xor32(a);
-        acc[i][t] = a;
-      }
-      if (lane < kLanes) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) opart[wave][i][lane * 8 + t] = acc[i][t];
-      }
-      if (lane == 0) red[1][wave][i] = li;
+    for (int t = 0; t < 8; ++t) {
+      float a = acc[t];
+      if (kLanes == 8) a += __shfl_xor(a, 8);
+      a += __shfl_xor(a, 16);
+      a = sum_xor32(a);
+      acc[t] = a;
     }
+    if (lane < kLanes) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) opart[wave][lane * 8 + t] = acc[t];
+    }
+    if (lane == 0) red[1][wave] = l;
     __syncthreads();
     if (tid < D) {
+      float lt = 0.f, ot = 0.f;
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        float lt = 0.f, ot = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          lt += red[1][w][i];
-          ot += opart[w][i][tid];
-        }
-        const int64_t base = ((int64_t)b * Hq + h0 + i) * C + c;
-        o_part[base * D + tid] = ot / lt;
-        if (tid == 0) lse_part[base] = (m[i] + log2f(lt)) * kLn2;
+      for (int w = 0; w < kWaves; ++w) {
+        lt += red[1][w];
+        ot += opart[w][tid];
       }
+      const int64_t base = (int64_t)bh * C + c;
+      __builtin_nontemporal_store(ot / lt, o_part + base * D + tid);
+      if (tid == 0) __builtin_nontemporal_store((m + log2f(lt)) * kLn2, lse_part + base);
     }
     __syncthreads();  // opart / red reused by the next item
   }
@@ -213,18 +186,23 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // head, slice of G <= 16 query heads of its group).  The G heads are the 16
 // columns of v_mfma_f32_16x16x32 (columns >= G carry q = 0 and are never
 // stored):
-//   S^T[key][head] = K Q^T   A = K rows loaded from HBM straight into VGPRs,
-//                            B = Q^T (the q rows of the slice's heads)
-//   O^T[d][head]  = V^T P^T  A = V^T via ds_read_b64_tr_b16 from the V chunk
-//                            fetched into LDS (swizzled, rows past M read as
-//                            zeros), B = P^T from LDS as hi + lo 16-bit parts
-// so the chunk's K and V are read from HBM once for all G heads.  Wave w
+//   S^T[key][head] = K Q^T   A = K rows, B = Q^T (the q rows of the slice's
+//                            heads), both read from LDS
+//   O^T[d][head]  = V^T P^T  A = V^T via ds_read_b64_tr_b16 from LDS,
+//                            B = P^T from LDS as hi + lo 16-bit parts
+// so the chunk's K and V are read from HBM once for all G heads.  Q, K and V
+// reach LDS through bounds-checked buffer loads (rows past the end read as
+// zeros) that write whole swizzled rows, so every fetch instruction reads
+// 1 KB of contiguous HBM; K and V carry the streaming hint.  (K read straight
+// into MFMA operand registers would take each 128-byte line in two 64-byte
+// halves from separate instructions, which streams markedly slower.)  Wave w
 // scores keys 32w .. 32w + 31 and accumulates d rows w*D/4 .. +D/4 - 1 over all
 // 128 keys.  The chunk max and sum are exchanged through LDS; P is the fp32
 // 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
 // accuracy in P while l is the sum of the unrounded values.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
 constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
+constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(kDecThreads)
@@ -240,20 +218,26 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   constexpr int kFetch = kChunk / kRowsPerInst;     // fetch instructions per wave
   constexpr uint32_t kPBytes = kGqaCols * kPRow * 2;  // one P part
   static_assert(kRowsPerInst % 16 == 0, "swizzle must repeat across fetch instructions");
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[kChunk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf[kChunk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t qbuf[kGqaCols * D];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2 * kGqaCols * kPRow];
   __shared__ float red[2][kWaves][kGqaCols];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   const int group = Hq / Hkv, slices = group / G;
+  const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_u16*)kbuf;
   const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_u16*)vbuf;
+  const uint32_t q_lds = (uint32_t)(uintptr_t)(lds_u16*)qbuf;
   const uint32_t p_lds = (uint32_t)(uintptr_t)(lds_u16*)pbuf;
   const bool out16 = ((uintptr_t)o_part & 15) == 0;
 
-  // V fetch: instruction i of wave w fills LDS units (i*kWaves + w)*64 + lane,
-  // i.e. row kRowsPerInst*i + rl, physical 16-byte chunk pc (holding logical
-  // chunk pc ^ swz(row)).
+  // K/V fetch: instruction i of wave w fills LDS units (i*kWaves + w)*64 +
+  // lane, i.e. row kRowsPerInst*i + rl, physical 16-byte chunk pc (holding
+  // logical chunk pc ^ swz(row)).  The Q fetch (16 rows) uses instruction 0 of
+  // the first kQInst waves.
+  constexpr int kQInst = kGqaCols * kU / 64;
   const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
   const uint32_t voff_lane = (uint32_t)(rl * D * 2 + ((pc ^ swz<D>(rl)) << 4));
   // V^T operand: in each 16-lane group of a ds_read_b64_tr_b16, lane s
@@ -283,31 +267,36 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int len = min(kChunk, M - key0);
     const int64_t slice = ((int64_t)b * Hkv + kvh) * M * D;
 
-    // V chunk -> LDS, no registers (bounds-checked: rows past M are zeros)
+    // Q rows h0 .. h0 + 15, K chunk, V chunk -> LDS, no registers; the
+    // buffer loads are bounds-checked, so Q rows >= G and K/V rows past M
+    // read as zeros.  K and V are streamed (read once).
+    const i32x4 qdesc = make_desc(q + ((int64_t)b * Hq + h0) * D, D, G, D);
+    const i32x4 kdesc = make_desc(k + slice, D, M, D);
     const i32x4 vdesc = make_desc(v + slice, D, M, D);
+    if (wave < kQInst) dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
 #pragma unroll
     for (int i = 0; i < kFetch; ++i)
-      dma16(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-            voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+      dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                  voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+#pragma unroll
+    for (int i = 0; i < kFetch; ++i)
+      dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                  voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+    wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
+    __syncthreads();    // Q and K visible
 
-    // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7
-    s16x8 ka[2][kS];
+    // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7; B operand:
+    // q of head h0 + j, same d.  Logical chunk 4s + g of a row whose swizzle
+    // is swz(j) (rows of a 16-row block share their low four bits with j).
+    s16x8 ka[2][kS], qb[kS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = 32 * wave + 16 * kb + j;
-      const uint16_t* kp = k + slice + (int64_t)(key0 + row) * D + 8 * g;
+    for (int s = 0; s < kS; ++s) {
+      const uint32_t cx = (uint32_t)(((4 * s + g) ^ swz<D>(j)) << 4);
+      qb[s] = lds_read_b128(q_lds + (uint32_t)(j * D * 2) + cx);
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const uint4 t = row < len ? load_stream(kp + 32 * s) : make_uint4(0, 0, 0, 0);
-        ka[kb][s] = __builtin_bit_cast(s16x8, t);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        ka[kb][s] = lds_read_b128(k_lds + (uint32_t)((32 * wave + 16 * kb + j) * D * 2) + cx);
     }
-    // B operand of S^T: q of head h0 + j, d = 32s + 8g .. +7
-    s16x8 qb[kS];
-#pragma unroll
-    for (int s = 0; s < kS; ++s)
-      qb[s] = j < G ? *reinterpret_cast<const s16x8*>(q + ((int64_t)b * Hq + h0 + j) * D + 32 * s + 8 * g)
-                    : (s16x8){};
 
     // scores in log2 units; element r of block kb is key 32w + 16kb + 4g + r
     float x[2][4];
@@ -378,14 +367,15 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         float* op = o_part + base * D + wave * (D / 4) + 16 * db + 4 * g;
-        const float4 o4 = make_float4(oacc[db][0] / lt, oacc[db][1] / lt, oacc[db][2] / lt, oacc[db][3] / lt);
+        const f32x4 o4 = oacc[db] / lt;
         if (out16) {
-          *reinterpret_cast<float4*>(op) = o4;
+          __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(op));
         } else {
-          op[0] = o4.x; op[1] = o4.y; op[2] = o4.z; op[3] = o4.w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(o4[r], op + r);
         }
       }
-      if (wave == 0 && g == 0) lse_part[base] = (m + log2f(lt)) * kLn2;
+      if (wave == 0 && g == 0) __builtin_nontemporal_store((m + log2f(lt)) * kLn2, lse_part + base);
     }
     __syncthreads();  // V, P and the sums are refilled by the next item
   }
@@ -495,7 +485,10 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   const int C = (M + kChunk - 1) / kChunk;
   const float sl2 = scale * kLog2e;
   const int group = Hq / Hkv;
-  if (group >= 2) {
+  // GQA groups run on the matrix-core kernel (K/V read once per kv head), and
+  // so do large MHA launches; a small MHA launch (a few rounds of items)
+  // finishes sooner on the VALU kernel's shorter per-item path.
+  if (group >= 2 || (int64_t)B * Hq * C >= kMfmaMinItems) {
     // query heads per item: the largest divisor of the group that fits the
     // 16 MFMA columns
     int g = std::min(group, kGqaCols);
@@ -516,8 +509,8 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   const int n_items = B * Hq * C;
 #define ATTN_DEC_CASE(DD, BB)                                                                          \
   if (d == DD && bf16 == BB) {                                                                         \
-    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB, 1>, kDecThreads));    \
-    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB, 1>), dim3(grid), dim3(kDecThreads), 0, stream,     \
+    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB>, kDecThreads));    \
+    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,     \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
                        Hq, Hkv, M, C, n_items, sl2);                                                   \
     return hipGetLastError();                                                                          \

@@ -45,18 +45,30 @@ __device__ __forceinline__ i32x4 make_desc(const uint16_t* base, int64_t row_str
 // is instead waited for explicitly (vmcnt) by the fetching wave before the
 // barrier that publishes it.  s_nop: one wait state between the M0 write and
 // its use.  M0 is listed as clobbered (nothing else in these kernels keeps a
-// value in M0).
+// value in M0).  kStream adds the nontemporal hint for data read exactly once
+// (it then neither displaces nor hits cached lines in L2 and the MALL).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool kStream = false>
 __device__ __forceinline__ void dma16(i32x4 desc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc)
-               : "memory", "m0");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector memory operations are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Workgroup barrier: this wave's LDS reads are complete (lgkmcnt(0)) so the
 // buffers they read can be refilled after it.  The asm statements keep the

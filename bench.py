@@ -33,9 +33,11 @@ PREFILL = "prefill_causal_gqa_bf16_d128"
 DECODE = "long_decode_fp16_d128"
 KERNEL_SOURCES = {
     "prefill": ["attention_attn_fwd_06_amd/csrc/prefill_fwd.hip",
-                "attention_attn_fwd_06_amd/csrc/device_common.h"],
+                "attention_attn_fwd_06_amd/csrc/device_common.h",
+                "attention_attn_fwd_06_amd/csrc/lds_stage.h"],
     "decode": ["attention_attn_fwd_06_amd/csrc/decode.hip",
-               "attention_attn_fwd_06_amd/csrc/device_common.h"],
+               "attention_attn_fwd_06_amd/csrc/device_common.h",
+               "attention_attn_fwd_06_amd/csrc/lds_stage.h"],
 }
 
 
@@ -228,7 +230,7 @@ def main():
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                   "frac": round(chunk_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                                   "traffic": read_traffic("decode", DECODE),
-                                  "kernel": "decode_chunk_kernel<128,f16>",
+                                  "kernel": "decode_gqa_mfma_kernel<128,f16>",
                                   "per_launch": f"{chunk_bytes:.6g} B (K+V+q)"}
         if not do_p:
             out["value"], out["unit"], out["dtype"] = out["decode"]["value"], "GB/s", "f16"

@@ -284,6 +284,9 @@ DEC_SHAPES = [
     (1, 12, 2, 300, 64, "f16"),
     (2, 32, 4, 2049, 128, "bf16"),
     (1, 16, 1, 513, 64, "bf16"),
+    # larger MHA launches, one with a tail chunk
+    (2, 8, 8, 16461, 64, "f16"),
+    (1, 16, 16, 16384, 128, "bf16"),
 ]
 
 
