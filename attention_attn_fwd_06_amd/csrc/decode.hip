@@ -23,11 +23,12 @@
 //    of a row.  Its per-item path is shorter, which wins when the grid runs
 //    only a few rounds of items.
 //  * softmax statistics use exp2 with the scale folded into one multiply.
-//  * merge kernel: one workgroup per (batch, query head, 16-column slice of d),
-//    one pass over the partials with a running max (no separate pass for the
-//    global log-sum-exp, no limit on the number of chunks), 16-byte loads, and
-//    eight independent loads in flight per thread; the 64 per-thread states
-//    of a column are combined by lane shuffles and one LDS step.
+//  * merge kernel: one workgroup per (batch, query head, slice of 16 to 128
+//    columns; the widest slice that still gives 512 workgroups), one pass
+//    over the partials with a running max (no separate pass for the global
+//    log-sum-exp, no limit on the number of chunks), 16-byte loads, and eight
+//    independent loads in flight per thread; the per-thread states of a
+//    column are combined by lane shuffles and one LDS step.
 #include <algorithm>
 
 #include "device_common.h"
@@ -382,8 +383,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 }
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeCols = 16;                          // d columns per workgroup
-constexpr int kMergeGroups = kMergeThreads / (kMergeCols / 4);  // chunk groups (64)
 
 // (m, s, a[4]) merge of two running states, in log2 units: both rescaled to
 // the larger reference max.  A state with m = -inf (no chunk yet) is empty.
@@ -402,30 +401,34 @@ __device__ __forceinline__ MergeState merge_states(const MergeState& x, const Me
   return r;
 }
 
-// One pass over the partials: each thread walks chunks grp, grp + 64, ... of one
-// (batch, head) and 4 consecutive columns, keeping a running max of lse_c (log2
-// units) with the matching rescaled weight sum and weighted output; the 64
-// group states are then combined with the same rule, first across the lanes
-// of each wave (xor shuffles over the group bits of the lane id), then across
-// the 4 waves.  O = sum_c 2^(l_c - M) O_c / sum_c 2^(l_c - M) for any
-// reference M equals sum_c w_c O_c.
-template <int D, bool BF16>
+// One pass over the partials.  A workgroup covers one (batch, head) and QW
+// column quads (4*QW columns); thread t takes quad t % QW and chunk group
+// t / QW, walking chunks grp, grp + G, ... (G = 256 / QW groups) with a running
+// max of lse_c (log2 units), the matching rescaled weight sum and the weighted
+// output.  Lanes of one wave that share a quad read consecutive chunks' pieces
+// of 16*QW contiguous bytes.  The G group states are combined with the same
+// rule, first across the lanes of each wave (xor shuffles over the group bits
+// of the lane id), then across the 4 waves.  O = sum_c 2^(l_c - M) O_c /
+// sum_c 2^(l_c - M) for any reference M equals sum_c w_c O_c.
+template <int D, bool BF16, int QW>
 __global__ __launch_bounds__(kMergeThreads)
 void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                       uint16_t* __restrict__ o, float* __restrict__ lse, int C) {
   constexpr int kWaves = kMergeThreads / 64;
-  __shared__ MergeState part[kWaves][4];
+  constexpr int kGroups = kMergeThreads / QW;
+  static_assert(QW >= 1 && QW <= 32 && 4 * QW <= D, "column quads per workgroup");
+  __shared__ MergeState part[kWaves][QW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cq = tid & 3, grp = tid >> 2;
+  const int cq = tid % QW, grp = tid / QW;
   const int bh = blockIdx.x;
-  const int col0 = blockIdx.y * kMergeCols + cq * 4;
+  const int col0 = blockIdx.y * (4 * QW) + cq * 4;
   const float* lp = lse_part + (int64_t)bh * C;
   const float* op = o_part + (int64_t)bh * C * D + col0;
 
   MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
-  for (int c = grp; c < C; c += kMergeGroups) {
+  for (int c = grp; c < C; c += kGroups) {
     const float l2 = lp[c] * kLog2e;
     const float4 ov = *reinterpret_cast<const float4*>(op + (int64_t)c * D);
     const float mn = fmaxf(st.m, l2);
@@ -438,9 +441,9 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
     st.a[3] = fmaf(st.a[3], r, w * ov.w);
     st.m = mn;
   }
-  // lanes that share cq differ in lane bits 2..5
+  // lanes that share cq differ in the lane bits from log2(QW) up
 #pragma unroll
-  for (int mask = 4; mask < 64; mask <<= 1) {
+  for (int mask = QW; mask < 64; mask <<= 1) {
     MergeState y;
     y.m = __shfl_xor(st.m, mask);
     y.s = __shfl_xor(st.s, mask);
@@ -448,14 +451,14 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
     for (int c = 0; c < 4; ++c) y.a[c] = __shfl_xor(st.a[c], mask);
     st = merge_states(st, y);
   }
-  if (lane < 4) part[wave][lane] = st;
+  if (lane < QW) part[wave][lane] = st;
   __syncthreads();
-  if (tid < 4) {
+  if (tid < QW) {
     MergeState r = part[0][tid];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) r = merge_states(r, part[w][tid]);
     const float inv = 1.f / r.s;
-    const int d0 = blockIdx.y * kMergeCols + tid * 4;
+    const int d0 = blockIdx.y * (4 * QW) + tid * 4;
     const uint32_t w01 = pack2<BF16>(r.a[0] * inv, r.a[1] * inv);
     const uint32_t w23 = pack2<BF16>(r.a[2] * inv, r.a[3] * inv);
     *reinterpret_cast<uint2*>(o + (int64_t)bh * D + d0) = make_uint2(w01, w23);
@@ -522,17 +525,27 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
 
 hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq,
                           int C, int d, bool bf16, hipStream_t stream) {
-  const dim3 grid(B * Hq, d / kMergeCols);
-#define ATTN_MERGE_CASE(DD, BB)                                                                  \
-  if (d == DD && bf16 == BB) {                                                                   \
-    hipLaunchKernelGGL((lse_merge_kernel<DD, BB>), grid, dim3(kMergeThreads), 0, stream, o_part, \
-                       lse_part, (uint16_t*)o, lse, C);                                          \
-    return hipGetLastError();                                                                    \
+  // Column quads per workgroup: the widest (longest contiguous reads, fewest
+  // chunk groups to combine) that still gives at least kMergeMinGroups
+  // workgroups, and at least 4 quads.
+  constexpr int64_t kMergeMinGroups = 512;
+  int qw = 32;
+  while (qw > 4 && (qw * 4 > d || (int64_t)B * Hq * (d / (4 * qw)) < kMergeMinGroups)) qw >>= 1;
+  const dim3 grid(B * Hq, d / (4 * qw));
+#define ATTN_MERGE_CASE(DD, BB, QQ)                                                                  \
+  if (d == DD && bf16 == BB && qw == QQ) {                                                           \
+    hipLaunchKernelGGL((lse_merge_kernel<DD, BB, QQ>), grid, dim3(kMergeThreads), 0, stream, o_part, \
+                       lse_part, (uint16_t*)o, lse, C);                                              \
+    return hipGetLastError();                                                                        \
   }
-  ATTN_MERGE_CASE(64, false)
-  ATTN_MERGE_CASE(64, true)
-  ATTN_MERGE_CASE(128, false)
-  ATTN_MERGE_CASE(128, true)
+#define ATTN_MERGE_QW(DD, BB) ATTN_MERGE_CASE(DD, BB, 4) ATTN_MERGE_CASE(DD, BB, 8) ATTN_MERGE_CASE(DD, BB, 16)
+  ATTN_MERGE_QW(64, false)
+  ATTN_MERGE_QW(64, true)
+  ATTN_MERGE_QW(128, false)
+  ATTN_MERGE_QW(128, true)
+  ATTN_MERGE_CASE(128, false, 32)
+  ATTN_MERGE_CASE(128, true, 32)
+#undef ATTN_MERGE_QW
 #undef ATTN_MERGE_CASE
   return hipErrorInvalidValue;
 }

@@ -9,7 +9,9 @@ already resident in HBM.  The decode rotates between two independent K/V sets
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 (4*B*Hq*N*M*d, halved for the causal mask) over the prefill kernel's average
 duration, measured with HIP events on the launch stream; the decode result is
-reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).
+reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).  The
+``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8, M=16384,
+d=128, bf16; K/V counted once per kv head), timed separately after the steps.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--prewarm-s 1.5] [--no-cpu-baseline]
 """
@@ -31,6 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
 PREFILL = "prefill_causal_gqa_bf16_d128"
 DECODE = "long_decode_fp16_d128"
+DECODE_GQA = "gqa_decode_bf16_d128"
 KERNEL_SOURCES = {
     "prefill": ["attention_attn_fwd_06_amd/csrc/prefill_fwd.hip",
                 "attention_attn_fwd_06_amd/csrc/device_common.h",
@@ -98,6 +101,48 @@ def cpu_baseline(budget_s: float = 15.0):
                       f"FLOPs credited with the causal-halved count"}
 
 
+def gqa_decode_rate(attn, w, args, dev):
+    """Grouped-query decode (K/V read once per kv head): chunk + merge per step on
+    two alternating K/V sets, timed with HIP events on the launch stream."""
+    import torch
+    from workloads import decode_bytes, make_inputs
+    q, k0, v0 = (t.to(dev) for t in make_inputs(w, args.seed))
+    _, k1, v1 = (t.to(dev) for t in make_inputs(w, args.seed + 1))
+    kv = [(k0, v0), (k1, v1)]
+    C = w.num_chunks
+    o_part = torch.empty((w.B, w.Hq, C, w.d), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kk, vv = kv[i % 2]
+        if ev: ev[0].record(stream)
+        attn.attn_decode_splitkv(q, kk, vv, w.chunk, w.scale, o_part=o_part, lse_part=lse_part, stream=stream)
+        if ev: ev[1].record(stream)
+        attn.lse_merge(o_part, lse_part, o=o, lse=lse, stream=stream)
+        if ev: ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    c_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
+    cm_ms = statistics.mean(e[0].elapsed_time(e[2]) for e in events)
+    nbytes = decode_bytes(w.B, w.Hq, w.Hkv, w.M, w.d)
+    chunk_bytes = nbytes - w.B * w.Hq * w.d * 2
+    gbps = nbytes / (cm_ms * 1e-3) / 1e9
+    return {"workload": w.desc, "value": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "chunk_merge_ms": round(cm_ms, 4), "chunk_ms": round(c_ms, 4),
+            "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
+            "kernel": "decode_gqa_mfma_kernel<128,bf16>", "algorithmic_bytes": nbytes,
+            "bytes_note": "K and V counted once per kv head"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,7 +152,7 @@ def main():
                     help="seconds of untimed steps before the counted warm-up (clock ramp)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_gqa", "copy"], default=None,
                     help="run one part only (for counter collection)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -234,6 +279,10 @@ def main():
                                   "per_launch": f"{chunk_bytes:.6g} B (K+V+q)"}
         if not do_p:
             out["value"], out["unit"], out["dtype"] = out["decode"]["value"], "GB/s", "f16"
+    if args.only in (None, "decode_gqa"):
+        out["decode_gqa"] = gqa_decode_rate(attn, WORKLOADS[DECODE_GQA], args, dev)
+        if args.only == "decode_gqa":
+            out["value"], out["unit"], out["dtype"] = out["decode_gqa"]["value"], "GB/s", "bf16"
     if args.only is None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -264,7 +264,7 @@ def check_decode(q, k, v, chunk, scale, dtype, label):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
-@pytest.mark.parametrize("name", ["small_decode_fp16_d128", "long_decode_fp16_d128"])
+@pytest.mark.parametrize("name", ["small_decode_fp16_d128", "long_decode_fp16_d128", "gqa_decode_bf16_d128"])
 def test_decode_workload_whole(name):
     w = WORKLOADS[name]
     say(f"case {w.name}")
@@ -304,6 +304,25 @@ def test_lse_merge_standalone(C, d, dt):
     g = torch.Generator("cpu").manual_seed(C)
     op = torch.randn((2, 3, C, d), generator=g)
     lp = torch.randn((2, 3, C), generator=g) * 4.0
+    o, lse = attn().lse_merge(op.to(DEV), lp.to(DEV), torch_dtype(dt))
+    torch.cuda.synchronize()
+    Or, Lr = oracle.lse_merge_ref(op, lp)
+    assert maxerr(f64(o), Or) <= TOL_O[dt]
+    assert maxerr(f64(lse), Lr) <= TOL_LSE
+
+
+# (batch, head) counts that select every column width of the merge workgroup:
+# 4*QW columns per workgroup, QW in {4, 8, 16, 32} (d = 128) and {4, 8, 16} (d = 64)
+@pytest.mark.parametrize("B,Hq,C,d,dt", [(4, 32, 50, 128, "bf16"), (8, 32, 7, 128, "f16"),
+                                         (16, 32, 3, 128, "bf16"), (8, 32, 20, 64, "f16"),
+                                         (16, 32, 5, 64, "bf16"), (3, 5, 130, 64, "bf16")])
+def test_lse_merge_column_widths(B, Hq, C, d, dt):
+    say(f"case lse_merge B={B} Hq={Hq} C={C} d={d} {dt}")
+    g = torch.Generator("cpu").manual_seed(B * 1000 + C)
+    # partials in the range of attention outputs (|O_c| < 4, where rounding O to
+    # bf16 stays within the bf16 bound); over 65536 outputs a unit normal would not
+    op = torch.randn((B, Hq, C, d), generator=g) * 0.5
+    lp = torch.randn((B, Hq, C), generator=g) * 4.0
     o, lse = attn().lse_merge(op.to(DEV), lp.to(DEV), torch_dtype(dt))
     torch.cuda.synchronize()
     Or, Lr = oracle.lse_merge_ref(op, lp)

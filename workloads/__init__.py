@@ -74,6 +74,9 @@ WORKLOADS = {
         Workload("long_decode_fp16_d128", "decode", B=2, Hq=8, Hkv=8, M=65536, d=128,
                  dtype="f16", chunk=128,
                  desc="split-KV decode, B=2 H=8 M=65536 d=128 fp16, 512 chunks of 128"),
+        Workload("gqa_decode_bf16_d128", "decode", B=8, Hq=32, Hkv=8, M=16384, d=128,
+                 dtype="bf16", chunk=128,
+                 desc="split-KV GQA decode, B=8 Hq=32 Hkv=8 M=16384 d=128 bf16, 128 chunks of 128"),
     ]
 }
 
