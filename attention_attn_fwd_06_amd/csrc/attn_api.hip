@@ -14,7 +14,8 @@ hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o
                             int Hq, int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
                             const attn_strides_t& st, hipStream_t stream);
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
-                           int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream);
+                           int B, int Hq, int Hkv, int M, int d, int chunk, bool bf16, float scale,
+                           hipStream_t stream);
 hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq,
                           int C, int d, bool bf16, hipStream_t stream);
 }  // namespace attn
@@ -22,7 +23,8 @@ hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, f
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // 32-bit element offsets per dimension product
-constexpr int kDecodeChunk = 128;
+constexpr int kDecodeChunk = 128;       // chunk sizes are multiples of this
+constexpr int kDecodeChunkMax = 8192;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_head_dim(int d) { return d == 64 || d == 128; }
@@ -43,7 +45,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
     case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N <= M (bottom-right mask)";
-    case ATTN_ERR_CHUNK_SIZE: return "decode chunk size must be 128";
+    case ATTN_ERR_CHUNK_SIZE: return "decode chunk size must be a multiple of 128, at most 8192";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
@@ -112,7 +114,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
   if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
-  if (chunk_size != kDecodeChunk) return ATTN_ERR_CHUNK_SIZE;
+  if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
   const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
   if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535 ||
@@ -121,8 +123,8 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u))
     return ATTN_ERR_ALIGNMENT;
-  return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, dtype == ATTN_BF16,
-                                             scale, stream));
+  return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, chunk_size,
+                                             dtype == ATTN_BF16, scale, stream));
 }
 
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int num_chunks,

@@ -183,8 +183,10 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 }
 
-// GQA decode on the matrix cores.  Item = (chunk c of 128 keys, batch b, kv
-// head, slice of G <= 16 query heads of its group).  The G heads are the 16
+// GQA decode on the matrix cores.  Item = (chunk c of `chunk` keys, a
+// multiple of 128, batch b, kv head, slice of G <= 16 query heads of its
+// group); the chunk is walked in 128-key sub-chunks with the online-softmax
+// rescale between them.  The G heads are the 16
 // columns of v_mfma_f32_16x16x32 (columns >= G carry q = 0 and are never
 // stored):
 //   S^T[key][head] = K Q^T   A = K rows, B = Q^T (the q rows of the slice's
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kDecThreads)
 void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
-                            int n_items, float scale_log2) {
+                            int chunk, int n_items, float scale_log2) {
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kDB = D / 64;                       // 16-row d blocks per wave
   constexpr int kWaves = kDecThreads / 64;
@@ -264,101 +266,115 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int hs = rest % slices, bkv = rest / slices;
     const int kvh = bkv % Hkv, b = bkv / Hkv;
     const int h0 = kvh * group + hs * G;  // first query head of this item
-    const int key0 = c * kChunk;
-    const int len = min(kChunk, M - key0);
+    const int c_end = min(M, (c + 1) * chunk);
     const int64_t slice = ((int64_t)b * Hkv + kvh) * M * D;
 
-    // Q rows h0 .. h0 + 15, K chunk, V chunk -> LDS, no registers; the
-    // buffer loads are bounds-checked, so Q rows >= G and K/V rows past M
-    // read as zeros.  K and V are streamed (read once).
+    // Q rows h0 .. h0 + 15 (once per item), then per 128-key sub-chunk its K
+    // and V -> LDS, no registers; the buffer loads are bounds-checked, so Q
+    // rows >= G and K/V rows past M read as zeros.  K and V are streamed
+    // (read once).
     const i32x4 qdesc = make_desc(q + ((int64_t)b * Hq + h0) * D, D, G, D);
     const i32x4 kdesc = make_desc(k + slice, D, M, D);
     const i32x4 vdesc = make_desc(v + slice, D, M, D);
     if (wave < kQInst) dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
-#pragma unroll
-    for (int i = 0; i < kFetch; ++i)
-      dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                  voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
-#pragma unroll
-    for (int i = 0; i < kFetch; ++i)
-      dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                  voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
-    wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
-    __syncthreads();    // Q and K visible
 
-    // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7; B operand:
-    // q of head h0 + j, same d.  Logical chunk 4s + g of a row whose swizzle
-    // is swz(j) (rows of a 16-row block share their low four bits with j).
-    s16x8 ka[2][kS], qb[kS];
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      const uint32_t cx = (uint32_t)(((4 * s + g) ^ swz<D>(j)) << 4);
-      qb[s] = lds_read_b128(q_lds + (uint32_t)(j * D * 2) + cx);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ka[kb][s] = lds_read_b128(k_lds + (uint32_t)((32 * wave + 16 * kb + j) * D * 2) + cx);
-    }
-
-    // scores in log2 units; element r of block kb is key 32w + 16kb + 4g + r
-    float x[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x4 sa = {};
-#pragma unroll
-      for (int s = 0; s < kS; ++s) sa = mfma16x16x32<BF16>(ka[kb][s], qb[s], sa);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 32 * wave + 16 * kb + 4 * g + r;
-        x[kb][r] = key < len ? sa[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[kb][r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = max_xor32(mx);
-    if (g == 0) red[0][wave][j] = mx;
-    wait_tile_loads();  // this wave's part of the V chunk is in LDS
-    __syncthreads();    // V chunk and the per-wave maxima visible
-    float m = red[0][0][j];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[0][w][j]);
-
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(x[kb][r] - m);
-        lsum += p[r];
-      }
-      const uint32_t h01 = pack2<BF16>(p[0], p[1]), h23 = pack2<BF16>(p[2], p[3]);
-      const f32x2 r01 = unpack2<BF16>(h01), r23 = unpack2<BF16>(h23);
-      const uint32_t l01 = pack2<BF16>(p[0] - r01[0], p[1] - r01[1]);
-      const uint32_t l23 = pack2<BF16>(p[2] - r23[0], p[3] - r23[1]);
-      lds_write_b64(pw + 32u * kb, (u32x2){h01, h23});
-      lds_write_b64(pw + kPBytes + 32u * kb, (u32x2){l01, l23});
-    }
-    lsum += __shfl_xor(lsum, 16);
-    lsum = sum_xor32(lsum);
-    if (g == 0) red[1][wave][j] = lsum;
-    __syncthreads();  // P and the per-wave sums visible
-
+    // running state of head j across the sub-chunks: the reference max (log2
+    // units, shared by all waves), this wave's sum and its O^T rows
+    float m_run = -INFINITY, l_w = 0.f;
     f32x4 oacc[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db) oacc[db] = (f32x4){};
+    for (int key0 = c * chunk; key0 < c_end; key0 += kChunk) {
+      const int len = min(kChunk, c_end - key0);
+      const bool last = key0 + kChunk >= c_end;
 #pragma unroll
-    for (int ks = 0; ks < kChunk / 32; ++ks) {
-      const s16x8 ph = lds_read_b128(pa + 64u * ks);
-      const s16x8 pl = lds_read_b128(pa + kPBytes + 64u * ks);
+      for (int i = 0; i < kFetch; ++i)
+        dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                    voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const s16x4 lo = lds_read_tr16_b64(va[db][0] + (uint32_t)(32 * ks * D * 2));
-        const s16x4 hi = lds_read_tr16_b64(va[db][1] + (uint32_t)(32 * ks * D * 2));
-        const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma16x16x32<BF16>(a, ph, oacc[db]);
-        oacc[db] = mfma16x16x32<BF16>(a, pl, oacc[db]);
+      for (int i = 0; i < kFetch; ++i)
+        dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                    voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+      wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
+      __syncthreads();    // Q and K visible
+
+      // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7; B operand:
+      // q of head h0 + j, same d.  Logical chunk 4s + g of a row whose swizzle
+      // is swz(j) (rows of a 16-row block share their low four bits with j).
+      s16x8 ka[2][kS], qb[kS];
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const uint32_t cx = (uint32_t)(((4 * s + g) ^ swz<D>(j)) << 4);
+        qb[s] = lds_read_b128(q_lds + (uint32_t)(j * D * 2) + cx);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          ka[kb][s] = lds_read_b128(k_lds + (uint32_t)((32 * wave + 16 * kb + j) * D * 2) + cx);
       }
+
+      // scores in log2 units; element r of block kb is key 32w + 16kb + 4g + r
+      float x[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 sa = {};
+#pragma unroll
+        for (int s = 0; s < kS; ++s) sa = mfma16x16x32<BF16>(ka[kb][s], qb[s], sa);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 32 * wave + 16 * kb + 4 * g + r;
+          x[kb][r] = key < len ? sa[r] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, x[kb][r]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = max_xor32(mx);
+      if (g == 0) red[0][wave][j] = mx;
+      wait_tile_loads();  // this wave's part of the V sub-chunk is in LDS
+      __syncthreads();    // V sub-chunk and the per-wave maxima visible
+      float m = m_run;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) m = fmaxf(m, red[0][w][j]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m);  // 0 on the first sub-chunk
+      m_run = m;
+
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(x[kb][r] - m);
+          lsum += p[r];
+        }
+        const uint32_t h01 = pack2<BF16>(p[0], p[1]), h23 = pack2<BF16>(p[2], p[3]);
+        const f32x2 r01 = unpack2<BF16>(h01), r23 = unpack2<BF16>(h23);
+        const uint32_t l01 = pack2<BF16>(p[0] - r01[0], p[1] - r01[1]);
+        const uint32_t l23 = pack2<BF16>(p[2] - r23[0], p[3] - r23[1]);
+        lds_write_b64(pw + 32u * kb, (u32x2){h01, h23});
+        lds_write_b64(pw + kPBytes + 32u * kb, (u32x2){l01, l23});
+      }
+      lsum += __shfl_xor(lsum, 16);
+      lsum = sum_xor32(lsum);
+      l_w = fmaf(l_w, alpha, lsum);
+      if (last && g == 0) red[1][wave][j] = l_w;
+      __syncthreads();  // P (and, after the last sub-chunk, the per-wave sums) visible
+
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < kChunk / 32; ++ks) {
+        const s16x8 ph = lds_read_b128(pa + 64u * ks);
+        const s16x8 pl = lds_read_b128(pa + kPBytes + 64u * ks);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const s16x4 lo = lds_read_tr16_b64(va[db][0] + (uint32_t)(32 * ks * D * 2));
+          const s16x4 hi = lds_read_tr16_b64(va[db][1] + (uint32_t)(32 * ks * D * 2));
+          const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = mfma16x16x32<BF16>(a, ph, oacc[db]);
+          oacc[db] = mfma16x16x32<BF16>(a, pl, oacc[db]);
+        }
+      }
+      if (!last) __syncthreads();  // K, V, P and the maxima are refilled by the next sub-chunk
     }
     float lt = red[1][0][j];
 #pragma unroll
@@ -376,9 +392,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(o4[r], op + r);
         }
       }
-      if (wave == 0 && g == 0) __builtin_nontemporal_store((m + log2f(lt)) * kLn2, lse_part + base);
+      if (wave == 0 && g == 0) __builtin_nontemporal_store((m_run + log2f(lt)) * kLn2, lse_part + base);
     }
-    __syncthreads();  // V, P and the sums are refilled by the next item
+    __syncthreads();  // Q, K, V, P and the sums are refilled by the next item
   }
 }
 
@@ -484,14 +500,16 @@ static int resident_grid(K kernel, int threads) {
 }
 
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
-                           int B, int Hq, int Hkv, int M, int d, bool bf16, float scale, hipStream_t stream) {
-  const int C = (M + kChunk - 1) / kChunk;
+                           int B, int Hq, int Hkv, int M, int d, int chunk, bool bf16, float scale,
+                           hipStream_t stream) {
+  const int C = (M + chunk - 1) / chunk;
   const float sl2 = scale * kLog2e;
   const int group = Hq / Hkv;
-  // GQA groups run on the matrix-core kernel (K/V read once per kv head), and
-  // so do large MHA launches; a small MHA launch (a few rounds of items)
-  // finishes sooner on the VALU kernel's shorter per-item path.
-  if (group >= 2 || (int64_t)B * Hq * C >= kMfmaMinItems) {
+  // GQA groups and chunks longer than 128 keys run on the matrix-core kernel
+  // (K/V read once per kv head), and so do large MHA launches; a small MHA
+  // launch (a few rounds of items) finishes sooner on the VALU kernel's
+  // shorter per-item path.
+  if (group >= 2 || chunk != kChunk || (int64_t)B * Hq * C >= kMfmaMinItems) {
     // query heads per item: the largest divisor of the group that fits the
     // 16 MFMA columns
     int g = std::min(group, kGqaCols);
@@ -502,7 +520,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
       const int grid = std::min(n_items, resident_grid(decode_gqa_mfma_kernel<DD, BB>, kDecThreads));  \
       hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,   \
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, \
-                         Hq, Hkv, M, C, g, n_items, sl2);                                              \
+                         Hq, Hkv, M, C, g, chunk, n_items, sl2);                                       \
       return hipGetLastError();                                                                        \
     }
     ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)

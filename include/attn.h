@@ -52,7 +52,7 @@ typedef enum {
   ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
-  ATTN_ERR_CHUNK_SIZE = -7,     /* decode chunk size other than 128 */
+  ATTN_ERR_CHUNK_SIZE = -7,     /* decode chunk size not a multiple of 128 or above 8192 */
   ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (hipGetLastError) */
   ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
   ATTN_ERR_ALIGNMENT = -10,     /* a tensor pointer is not 16-byte aligned */
@@ -126,8 +126,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size);
  * be shorter.  For each chunk: s_j = scale * q.k_j, m_c = max_j s_j,
  * p_j = exp(s_j - m_c), l_c = sum p_j, o_part = (sum_j p_j v_j) / l_c (normalised),
  * lse_part = m_c + ln l_c ("CUDA Flash Decoding", section 2.2 step 1).  No mask.
- * Requires chunk_size == 128, d in {64, 128}, Hq % Hkv == 0, a finite scale >= 0,
- * B*Hq <= 65535, and B*Hkv*M*d, B*Hq*C*d below 2^31.
+ * Requires chunk_size a multiple of 128 and at most 8192 (longer chunks mean fewer
+ * partials for lse_merge to read), d in {64, 128}, Hq % Hkv == 0, a finite
+ * scale >= 0, B*Hq <= 65535, and B*Hkv*M*d, B*Hq*C*d and (M + 128)*d below 2^31.
  */
 int attn_decode_splitkv(const void* q, const void* k, const void* v,
                         float* o_part, float* lse_part,

@@ -137,7 +137,7 @@ def dec(**kw):
     (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1),
     (dict(M=0), -2), (dict(chunk=0), -2), (dict(B=-1), -2),
     (dict(d=80), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
-    (dict(chunk=64), -7), (dict(chunk=256), -7),
+    (dict(chunk=64), -7), (dict(chunk=192), -7), (dict(chunk=8320), -7),
     (dict(scale=-1.0), -11),
     (dict(B=70000, Hq=1, Hkv=1, M=128), -9),
     (dict(k=FAKE + 4), -10), (dict(op=FAKE + 1), -10),

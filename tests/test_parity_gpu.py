@@ -298,6 +298,19 @@ def test_decode_shapes(shape):
     check_decode(q, k, v, 128, float(np.float32(d ** -0.5)), dt, str(shape))
 
 
+# chunks longer than 128 keys (walked as 128-key sub-chunks with the online
+# rescale between them), with short last chunks and sub-chunks
+@pytest.mark.parametrize("shape", [(1, 8, 2, 1000, 128, "bf16", 256), (2, 4, 4, 3000, 64, "f16", 512),
+                                   (1, 16, 2, 777, 128, "f16", 1024), (1, 4, 1, 9000, 64, "bf16", 8192),
+                                   (2, 8, 8, 2049, 128, "f16", 384), (1, 32, 4, 130, 128, "bf16", 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_decode_chunk_sizes(shape):
+    B, Hq, Hkv, M, d, dt, chunk = shape
+    say(f"case decode chunk {shape}")
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=M + chunk)
+    check_decode(q, k, v, chunk, float(np.float32(d ** -0.5)), dt, str(shape))
+
+
 @pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
 def test_lse_merge_standalone(C, d, dt):
     say(f"case lse_merge C={C} d={d} {dt}")
