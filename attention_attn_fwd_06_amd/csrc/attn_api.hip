@@ -27,7 +27,7 @@ constexpr int kDecodeChunk = 128;       // chunk sizes are multiples of this
 constexpr int kDecodeChunkMax = 8192;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool valid_head_dim(int d) { return d == 64 || d == 128; }
+bool valid_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
 bool valid_dtype(int dt) { return dt == ATTN_F16 || dt == ATTN_BF16; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }

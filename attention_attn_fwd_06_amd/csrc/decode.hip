@@ -54,11 +54,12 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc)
   return acc;
 }
 
-// Sum over the kLanes (8 or 16) consecutive lanes that share one key row.
+// Sum over the kLanes (4, 8 or 16) consecutive lanes that share one key row.
 template <int kLanes>
 __device__ __forceinline__ float row_sum(float x) {
   if constexpr (kLanes == 16) return sum16(x);
-  else return sum8(x);
+  else if constexpr (kLanes == 8) return sum8(x);
+  else return sum4(x);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -78,7 +79,7 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                          float* __restrict__ lse_part, int Hq, int Hkv, int M, int C,
                          int n_items, float scale_log2) {
   constexpr int kLanes = D / 8;                       // lanes per key row
-  constexpr int kRowsPerPass = kDecThreads / kLanes;  // 16 (d=128) or 32 (d=64)
+  constexpr int kRowsPerPass = kDecThreads / kLanes;  // 16, 32 or 64 (d = 128, 64, 32)
   constexpr int kPasses = kChunk / kRowsPerPass;      // rows per thread
   constexpr int kWaves = kDecThreads / 64;
   __shared__ float red[2][kWaves];
@@ -126,7 +127,8 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // chunk max: over the rows of this wave, then over the waves
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = max_xor32(mx);
-    if (kLanes == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
+    if (kLanes <= 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
+    if (kLanes == 4) mx = fmaxf(mx, __shfl_xor(mx, 4));
     if (lane == 0) red[0][wave] = mx;
     __syncthreads();
     float m = red[0][0];
@@ -152,12 +154,14 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // the wave, then across waves.
     l += __shfl_xor(l, 16);
     l = sum_xor32(l);
-    if (kLanes == 8) l += __shfl_xor(l, 8);
+    if (kLanes <= 8) l += __shfl_xor(l, 8);
+    if (kLanes == 4) l += __shfl_xor(l, 4);
     // column partials: reduce the lanes that share a column chunk
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       float a = acc[t];
-      if (kLanes == 8) a += __shfl_xor(a, 8);
+      if (kLanes == 4) a += __shfl_xor(a, 4);
+      if (kLanes <= 8) a += __shfl_xor(a, 8);
       a += __shfl_xor(a, 16);
       a = sum_xor32(a);
       acc[t] = a;
@@ -200,7 +204,8 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // into MFMA operand registers would take each 128-byte line in two 64-byte
 // halves from separate instructions, which streams markedly slower.)  Wave w
 // scores keys 32w .. 32w + 31 and accumulates d rows w*D/4 .. +D/4 - 1 over all
-// 128 keys.  The chunk max and sum are exchanged through LDS; P is the fp32
+// 128 keys (at d = 32 waves 0 and 1 hold the two 16-row blocks).  The chunk
+// max and sum are exchanged through LDS; P is the fp32
 // 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
 // accuracy in P while l is the sum of the unrounded values.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
@@ -214,8 +219,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
                             int chunk, int n_items, float scale_log2) {
   constexpr int kS = D / 32;                        // QK contraction steps
-  constexpr int kDB = D / 64;                       // 16-row d blocks per wave
   constexpr int kWaves = kDecThreads / 64;
+  constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
+  constexpr int kPVWaves = D / 16 / kDB;            // waves with O^T rows (all but at d = 32)
   constexpr int kU = D / 8;                         // 16-byte units per row
   constexpr int kRowsPerInst = kDecThreads / kU;    // rows per fetch instruction index
   constexpr int kFetch = kChunk / kRowsPerInst;     // fetch instructions per wave
@@ -253,7 +259,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int row = 8 * g + 4 * hh + (j >> 2);
-      const int col = wave * (D / 4) + 16 * db + 4 * (j & 3);
+      const int col = 16 * (wave * kDB + db) + 4 * (j & 3);
       va[db][hh] = v_lds + (uint32_t)(row * D * 2 + ((((col >> 3) ^ swz<D>(row)) << 4) | ((col & 7) * 2)));
     }
   }
@@ -363,6 +369,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks) {
+        if (wave >= kPVWaves) break;
         const s16x8 ph = lds_read_b128(pa + 64u * ks);
         const s16x8 pl = lds_read_b128(pa + kPBytes + 64u * ks);
 #pragma unroll
@@ -383,7 +390,8 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       const int64_t base = ((int64_t)b * Hq + h0 + j) * C + c;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        float* op = o_part + base * D + wave * (D / 4) + 16 * db + 4 * g;
+        if (wave >= kPVWaves) break;
+        float* op = o_part + base * D + 16 * (wave * kDB + db) + 4 * g;
         const f32x4 o4 = oacc[db] / lt;
         if (out16) {
           __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(op));
@@ -523,6 +531,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
                          Hq, Hkv, M, C, g, chunk, n_items, sl2);                                       \
       return hipGetLastError();                                                                        \
     }
+    ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
     ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)
 #undef ATTN_GQA_CASE
     return hipErrorInvalidValue;
@@ -536,6 +545,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
                        Hq, Hkv, M, C, n_items, sl2);                                                   \
     return hipGetLastError();                                                                          \
   }
+  ATTN_DEC_CASE(32, false) ATTN_DEC_CASE(32, true)
   ATTN_DEC_CASE(64, false) ATTN_DEC_CASE(64, true) ATTN_DEC_CASE(128, false) ATTN_DEC_CASE(128, true)
 #undef ATTN_DEC_CASE
   return hipErrorInvalidValue;
@@ -557,6 +567,8 @@ hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, f
     return hipGetLastError();                                                                        \
   }
 #define ATTN_MERGE_QW(DD, BB) ATTN_MERGE_CASE(DD, BB, 4) ATTN_MERGE_CASE(DD, BB, 8) ATTN_MERGE_CASE(DD, BB, 16)
+  ATTN_MERGE_CASE(32, false, 4) ATTN_MERGE_CASE(32, false, 8)
+  ATTN_MERGE_CASE(32, true, 4) ATTN_MERGE_CASE(32, true, 8)
   ATTN_MERGE_QW(64, false)
   ATTN_MERGE_QW(64, true)
   ATTN_MERGE_QW(128, false)

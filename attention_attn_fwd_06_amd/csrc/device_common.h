@@ -122,6 +122,11 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 // Sum over each aligned group of 8 lanes.
+__device__ __forceinline__ float sum4(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  return x;
+}
 __device__ __forceinline__ float sum8(float x) {
   x += dpp<kDppXor1>(x);
   x += dpp<kDppXor2>(x);

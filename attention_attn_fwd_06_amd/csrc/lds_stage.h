@@ -19,11 +19,16 @@ namespace attn {
 //    bits take 4 distinct values;
 //  d = 64 (128-byte rows, two per bank row): swz = 4*((row/2)%2) + (row/4)%4
 //    permutes 0..7 over the 8 rows of one parity, and rows 2 apart differ in
-//    bit 2.
+//    bit 2;
+//  d = 32 (64-byte rows, four per bank row): swz = (row/4)%4 permutes 0..3
+//    over the 4 rows of one residue mod 4 among 16 consecutive rows; 4
+//    consecutive rows fill one bank row whatever the swizzle.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
+  static_assert(D == 32 || D == 64 || D == 128, "head dims with a swizzle");
   if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return (row >> 2) & 3;
 }
 
 // Buffer descriptor over one (batch, kv head) slice of K or V: base address,

@@ -638,6 +638,10 @@ hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o
                             const attn_strides_t& st, hipStream_t stream) {
 #define ATTN_PREFILL_CASE(DD, BB, CC) \
   if (d == DD && bf16 == BB && causal == CC) return launch_prefill<DD, BB, CC>(q, k, v, o, lse, B, Hq, Hkv, N, M, scale, st, stream);
+  ATTN_PREFILL_CASE(32, false, false)
+  ATTN_PREFILL_CASE(32, false, true)
+  ATTN_PREFILL_CASE(32, true, false)
+  ATTN_PREFILL_CASE(32, true, true)
   ATTN_PREFILL_CASE(64, false, false)
   ATTN_PREFILL_CASE(64, false, true)
   ATTN_PREFILL_CASE(64, true, false)

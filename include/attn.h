@@ -48,7 +48,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL_POINTER = -1,   /* a required pointer is NULL */
   ATTN_ERR_BAD_DIMENSION = -2,  /* a size is <= 0 */
-  ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not in {64, 128} */
+  ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not in {32, 64, 128} */
   ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
@@ -84,7 +84,7 @@ typedef struct {
  * of the key sequence (a chunk of a longer prefill), so the last query sees every
  * key; for N == M this is the page's top-left mask.  Causal requires N <= M;
  * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
- * including the row maximum).  Requires d in {64, 128}, Hq % Hkv == 0, a finite
+ * including the row maximum).  Requires d in {32, 64, 128}, Hq % Hkv == 0, a finite
  * scale >= 0, and B*(N+256)*Hq*d, B*(M+64)*Hkv*d below 2^31.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -127,7 +127,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size);
  * p_j = exp(s_j - m_c), l_c = sum p_j, o_part = (sum_j p_j v_j) / l_c (normalised),
  * lse_part = m_c + ln l_c ("CUDA Flash Decoding", section 2.2 step 1).  No mask.
  * Requires chunk_size a multiple of 128 and at most 8192 (longer chunks mean fewer
- * partials for lse_merge to read), d in {64, 128}, Hq % Hkv == 0, a finite
+ * partials for lse_merge to read), d in {32, 64, 128}, Hq % Hkv == 0, a finite
  * scale >= 0, B*Hq <= 65535, and B*Hkv*M*d, B*Hq*C*d and (M + 128)*d below 2^31.
  */
 int attn_decode_splitkv(const void* q, const void* k, const void* v,
@@ -143,7 +143,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v,
  *
  * g = max_c lse_c + ln sum_c exp(lse_c - max_c lse_c), w_c = exp(lse_c - g),
  * o = sum_c w_c o_part[c], lse = g ("CUDA Flash Decoding", section 2.2 step 2).
- * Requires num_chunks >= 1 and d in {64, 128}.
+ * Requires num_chunks >= 1 and d in {32, 64, 128}.
  */
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
               int B, int Hq, int num_chunks, int d, attn_dtype_t out_dtype,

@@ -62,7 +62,7 @@ def fwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
     (dict(B=0), -2), (dict(Hq=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(M=-5), -2), (dict(d=0), -2),
-    (dict(d=96), -3), (dict(d=256), -3), (dict(d=32), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(d=16), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4),
     (dict(Hq=6, Hkv=4), -5),
     (dict(causal=1, N=256, M=128), -6),

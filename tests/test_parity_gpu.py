@@ -101,6 +101,11 @@ SHAPES = [
     (2, 64, 200, 8, 2, 128, "bf16", True),
     (1, 100, 1000, 4, 1, 64, "f16", True),
     (1, 130, 515, 8, 8, 128, "f16", True),
+    # head dim 32 (the pages' smallest supported head dim)
+    (1, 200, 333, 4, 4, 32, "f16", False),
+    (2, 300, 300, 8, 2, 32, "bf16", True),
+    (1, 70, 530, 4, 1, 32, "f16", True),
+    (1, 1, 1, 1, 1, 32, "bf16", False),
 ]
 
 
@@ -287,6 +292,10 @@ DEC_SHAPES = [
     # larger MHA launches, one with a tail chunk
     (2, 8, 8, 16461, 64, "f16"),
     (1, 16, 16, 16384, 128, "bf16"),
+    # head dim 32: VALU (small MHA), matrix-core (GQA and large MHA)
+    (1, 4, 4, 300, 32, "f16"),
+    (2, 16, 4, 1000, 32, "bf16"),
+    (4, 8, 8, 8200, 32, "f16"),
 ]
 
 
@@ -302,7 +311,8 @@ def test_decode_shapes(shape):
 # rescale between them), with short last chunks and sub-chunks
 @pytest.mark.parametrize("shape", [(1, 8, 2, 1000, 128, "bf16", 256), (2, 4, 4, 3000, 64, "f16", 512),
                                    (1, 16, 2, 777, 128, "f16", 1024), (1, 4, 1, 9000, 64, "bf16", 8192),
-                                   (2, 8, 8, 2049, 128, "f16", 384), (1, 32, 4, 130, 128, "bf16", 8192)],
+                                   (2, 8, 8, 2049, 128, "f16", 384), (1, 32, 4, 130, 128, "bf16", 8192),
+                                   (1, 8, 2, 2000, 32, "bf16", 512)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_decode_chunk_sizes(shape):
     B, Hq, Hkv, M, d, dt, chunk = shape
@@ -325,10 +335,12 @@ def test_lse_merge_standalone(C, d, dt):
 
 
 # (batch, head) counts that select every column width of the merge workgroup:
-# 4*QW columns per workgroup, QW in {4, 8, 16, 32} (d = 128) and {4, 8, 16} (d = 64)
+# 4*QW columns per workgroup, QW in {4, 8, 16, 32} (d = 128), {4, 8, 16} (d = 64)
+# and {4, 8} (d = 32)
 @pytest.mark.parametrize("B,Hq,C,d,dt", [(4, 32, 50, 128, "bf16"), (8, 32, 7, 128, "f16"),
                                          (16, 32, 3, 128, "bf16"), (8, 32, 20, 64, "f16"),
-                                         (16, 32, 5, 64, "bf16"), (3, 5, 130, 64, "bf16")])
+                                         (16, 32, 5, 64, "bf16"), (3, 5, 130, 64, "bf16"),
+                                         (2, 3, 40, 32, "f16"), (16, 32, 9, 32, "bf16")])
 def test_lse_merge_column_widths(B, Hq, C, d, dt):
     say(f"case lse_merge B={B} Hq={Hq} C={C} d={d} {dt}")
     g = torch.Generator("cpu").manual_seed(B * 1000 + C)
