@@ -30,12 +30,20 @@ notes of the repository):
     this mask and N <= M, since key 0 is always allowed).
   * Inputs are the already-rounded fp16/bf16 values upcast exactly to
     float64; ``scale`` is the fp32 value handed to the GPU, upcast.
+  * Paged KV (the pages name it only as future work, with no layout): pages
+    of block_size consecutive keys of every KV head, [num_blocks, block_size,
+    Hkv, d]; key t of sequence b is row t % block_size of page
+    block_table[b, t // block_size]; sequence b holds seq_lens[b] keys.  A
+    paged decode computes exactly the decode of each sequence's gathered keys;
+    chunks past a sequence's end have O_c = 0 and lse_c = -inf (no weight in
+    the merge).
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref"]
+__all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref", "paged_decode_partials_ref",
+           "paged_decode_ref"]
 
 
 def _f64(x) -> np.ndarray:
@@ -157,5 +165,45 @@ def decode_ref(q, k, v, scale: float, chunk: int):
     """Split-KV decode end to end: partials, then merge.  Returns
     (O [B, Hq, d], lse [B, Hq], o_part, lse_part)."""
     o_part, lse_part = decode_partials_ref(q, k, v, scale, chunk)
+    O, lse = lse_merge_ref(o_part, lse_part)
+    return O, lse, o_part, lse_part
+
+
+def paged_decode_partials_ref(q, k_cache, v_cache, block_table, seq_lens, scale: float, chunk: int):
+    """Split-KV decode partials over a paged KV cache (see the module notes for
+    the page layout).
+
+    q [B, Hq, d]; k_cache, v_cache [num_blocks, block_size, Hkv, d];
+    block_table [B, max_blocks] page ids; seq_lens [B] key counts.  Returns
+    o_part [B, Hq, C, d] and lse_part [B, Hq, C] with
+    C = ceil(max_blocks * block_size / chunk): sequence b's chunks are those of
+    ``decode_partials_ref`` on its gathered keys, the chunks past its end are
+    O_c = 0, lse_c = -inf.
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    bt = np.asarray(block_table, dtype=np.int64)
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    B, Hq, d = q.shape
+    _, bs, Hkv, dk = kc.shape
+    if dk != d or vc.shape != kc.shape or bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("shape mismatch between q, the caches, block_table and seq_lens")
+    C = -(-(bt.shape[1] * bs) // chunk)
+    o_part = np.zeros((B, Hq, C, d))
+    lse_part = np.full((B, Hq, C), -np.inf)
+    for b in range(B):
+        t = np.arange(int(sl[b]))                       # the sequence's keys
+        pages, rows = bt[b, t // bs], t % bs
+        kb = kc[pages, rows].transpose(1, 0, 2)[None]   # [1, Hkv, len, d]
+        vb = vc[pages, rows].transpose(1, 0, 2)[None]
+        op, lp = decode_partials_ref(q[b:b + 1], kb, vb, scale, chunk)
+        o_part[b, :, :op.shape[2]] = op[0]
+        lse_part[b, :, :lp.shape[2]] = lp[0]
+    return o_part, lse_part
+
+
+def paged_decode_ref(q, k_cache, v_cache, block_table, seq_lens, scale: float, chunk: int):
+    """Paged split-KV decode end to end.  Returns (O [B, Hq, d], lse [B, Hq],
+    o_part, lse_part)."""
+    o_part, lse_part = paged_decode_partials_ref(q, k_cache, v_cache, block_table, seq_lens, scale, chunk)
     O, lse = lse_merge_ref(o_part, lse_part)
     return O, lse, o_part, lse_part

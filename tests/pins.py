@@ -1,7 +1,8 @@
 """Checks that pin the CPU oracle to something other than itself.
 
 Every check takes the oracle as a parameter (a module exposing ``attn_ref``,
-``decode_partials_ref``, ``lse_merge_ref`` and ``decode_ref``) and raises
+``decode_partials_ref``, ``lse_merge_ref``, ``decode_ref`` and the paged
+variants) and raises
 AssertionError when the oracle disagrees with:
   * a pure-Python brute force (``tests/brute.py``) on tiny inputs and on the
     whole of the two small workloads;
@@ -301,12 +302,63 @@ def check_two_keys_closed_form(ora):
     _close(lse[0, 0, 0], math.log(math.exp(s0) + math.exp(s1)), what="two-key lse")
 
 
+def _pages(k, bs, seed):
+    """Store contiguous K [B, Hkv, M, d] in pages [num_blocks, bs, Hkv, d] in a
+    shuffled page order (plus one unused page); returns (cache, block_table)."""
+    B, Hkv, M, d = k.shape
+    nblk = -(-M // bs)
+    order = np.random.default_rng(seed).permutation(B * nblk + 1)
+    cache = _rand((B * nblk + 1, bs, Hkv, d), seed + 1)   # unused rows hold noise
+    table = np.zeros((B, nblk), dtype=np.int64)
+    for b in range(B):
+        for j in range(nblk):
+            p = order[b * nblk + j]
+            table[b, j] = p
+            rows = k[b, :, j * bs:(j + 1) * bs].transpose(1, 0, 2)   # [rows, Hkv, d]
+            cache[p, :rows.shape[0]] = rows
+    return cache, table
+
+
+def check_paged_decode_is_decode_of_gathered_keys(ora):
+    """Keys stored in shuffled pages decode exactly like the contiguous keys."""
+    B, Hq, Hkv, M, d, bs = 2, 4, 2, 37, 5, 8
+    q, k, v = _rand((B, Hq, d), 300), _rand((B, Hkv, M, d), 301), _rand((B, Hkv, M, d), 302)
+    kc, bt = _pages(k, bs, 303)
+    vc, bt2 = _pages(v, bs, 303)
+    assert (bt == bt2).all()
+    for chunk in (4, 16, 64):
+        O, L, op, lp = ora.paged_decode_ref(q, kc, vc, bt, np.full(B, M), 0.6, chunk)
+        Or, Lr, opr, lpr = ora.decode_ref(q, k, v, 0.6, chunk)
+        _close(O, Or, what=f"paged output, chunk {chunk}")
+        _close(L, Lr, what=f"paged lse, chunk {chunk}")
+        _close(op[:, :, :opr.shape[2]], opr, what=f"paged partials, chunk {chunk}")
+
+
+def check_paged_decode_variable_lengths(ora):
+    """Sequence b with seq_lens[b] keys decodes like its truncated keys; chunks
+    past the end carry no weight."""
+    B, Hq, Hkv, M, d, bs = 3, 2, 1, 40, 4, 8
+    q, k, v = _rand((B, Hq, d), 310), _rand((B, Hkv, M, d), 311), _rand((B, Hkv, M, d), 312)
+    kc, bt = _pages(k, bs, 313)
+    vc, _ = _pages(v, bs, 313)
+    lens = np.array([1, 17, 40])
+    O, L, op, lp = ora.paged_decode_ref(q, kc, vc, bt, lens, 0.7, 16)
+    assert op.shape[2] == 3
+    for b, n in enumerate(lens):
+        Or, Lr, opr, lpr = ora.decode_ref(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.7, 16)
+        _close(O[b], Or[0], what=f"seq {b} output")
+        _close(L[b], Lr[0], what=f"seq {b} lse")
+        nc = opr.shape[2]
+        assert np.all(lp[b, :, nc:] == -np.inf) and np.all(op[b, :, nc:] == 0.0), "empty chunks"
+
+
 FAST_CHECKS = [
     check_brute_prefill_tiny, check_brute_decode_tiny, check_sdpa,
     check_identity_v_rows_are_probabilities, check_constant_v, check_single_key,
     check_causal_row0, check_zero_scale, check_key_shift, check_permutation,
     check_gqa_is_repeated_mha, check_decode_is_single_query_attention,
     check_merge_identities, check_two_keys_closed_form, check_causal_chunk_is_tail_of_full,
+    check_paged_decode_is_decode_of_gathered_keys, check_paged_decode_variable_lengths,
 ]
 
 

@@ -34,6 +34,10 @@ MUTANTS = {
     "merge_weights_unnormalised": ("w = np.exp(lse_part - g)", "w = np.exp(lse_part - mx)"),
     "merge_lse_without_max": ("g = mx + np.log(", "g = np.log("),
     "merge_plain_average": ("O = np.sum(w[..., None] * o_part, axis=-2)", "O = np.mean(o_part, axis=-2)"),
+    "paged_row_shifted": ("pages, rows = bt[b, t // bs], t % bs", "pages, rows = bt[b, t // bs], (t + 1) % bs"),
+    "paged_page_in_order": ("pages, rows = bt[b, t // bs], t % bs", "pages, rows = t // bs, t % bs"),
+    "paged_ignores_length": ("t = np.arange(int(sl[b]))", "t = np.arange(bt.shape[1] * bs)"),
+    "paged_empty_chunks_weighted": ("lse_part = np.full((B, Hq, C), -np.inf)", "lse_part = np.zeros((B, Hq, C))"),
 }
 
 
