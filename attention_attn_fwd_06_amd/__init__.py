@@ -14,7 +14,8 @@ from . import _lib
 
 __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
-    "attn_decode_workspace_bytes", "attn_status_string", "attn_decode",
+    "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
+    "attn_decode_paged",
 ]
 
 ATTN_F16 = 0
@@ -118,6 +119,61 @@ def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = No
     if st != 0:
         raise AttnError(st, "attn_decode_splitkv")
     return o_part, lse_part
+
+
+def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
+                              scale: float | None = None, o_part=None, lse_part=None, stream=None):
+    """Split-KV decode partials over a paged KV cache.
+
+    q [B,Hq,d]; k_cache, v_cache: views [num_blocks, block_size, Hkv, d] with a
+    contiguous last dimension (token-major pages as they are, head-major pages
+    [num_blocks, Hkv, block_size, d] passed as ``.transpose(1, 2)``), both with
+    the same strides; block_table [B, max_blocks] int32; seq_lens [B] int32.
+    Returns (o_part [B,Hq,C,d], lse_part [B,Hq,C]) with
+    C = ceil(max_blocks * block_size / chunk_size).
+    """
+    _check(q, "q")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be a 4-D view with a contiguous last dimension")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 tensor")
+    B, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = k_cache.shape
+    max_blocks = block_table.shape[1]
+    if dk != d or tuple(block_table.shape) != (B, max_blocks) or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape mismatch between q, the caches, block_table and seq_lens")
+    C = -(-(max_blocks * block_size) // chunk_size)
+    if scale is None:
+        scale = d ** -0.5
+    if o_part is None:
+        o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    pk = _lib.PagedKv(block_table.data_ptr(), seq_lens.data_ptr(), num_blocks, block_size, max_blocks,
+                      k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    st = _lib.load().attn_decode_paged_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                               ctypes.byref(pk), o_part.data_ptr(), lse_part.data_ptr(),
+                                               B, Hq, Hkv, d, chunk_size, float(scale), _dtype_code(q),
+                                               _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_splitkv")
+    return o_part, lse_part
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
+                      scale: float | None = None, stream=None):
+    """Paged split-KV decode end to end (partials, then the merge)."""
+    o_part, lse_part = attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size,
+                                                 scale, stream=stream)
+    o, lse = lse_merge(o_part, lse_part, q.dtype, stream=stream)
+    return o, lse, o_part, lse_part
 
 
 def lse_merge(o_part, lse_part, out_dtype=torch.float16, o=None, lse=None, return_lse: bool = True,

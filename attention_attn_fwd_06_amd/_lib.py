@@ -17,6 +17,13 @@ class Strides(ctypes.Structure):
                 ("v", ctypes.c_int64 * 3), ("o", ctypes.c_int64 * 3)]
 
 
+class PagedKv(ctypes.Structure):
+    """attn_paged_kv_t: page table, sequence lengths and element strides of a paged KV cache."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("num_blocks", ctypes.c_int),
+                ("block_size", ctypes.c_int), ("max_blocks", ctypes.c_int), ("page_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+
+
 SYMBOLS = {
     # name: (restype, argtypes)
     "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 7
@@ -26,6 +33,9 @@ SYMBOLS = {
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
                             + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_decode_paged_splitkv": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.POINTER(PagedKv)]
+                                  + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 5
+                                  + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "lse_merge": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4
                   + [ctypes.c_int, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),

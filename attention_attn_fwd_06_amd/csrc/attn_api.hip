@@ -18,6 +18,11 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
                            hipStream_t stream);
 hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq,
                           int C, int d, bool bf16, hipStream_t stream);
+hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
+                                 int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
+                                 int64_t head_stride, float* o_part, float* lse_part, int B, int Hq, int Hkv,
+                                 int d, int chunk, bool bf16, float scale, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -41,7 +46,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
     case ATTN_ERR_BAD_DIMENSION: return "a size argument is not positive";
-    case ATTN_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case ATTN_ERR_HEAD_DIM: return "head dimension must be 32, 64 or 128";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
     case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N <= M (bottom-right mask)";
@@ -50,7 +55,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
-    case ATTN_ERR_LAYOUT: return "strides must be >= 0 and multiples of 8 elements; k and v need one token stride >= d";
+    case ATTN_ERR_LAYOUT:
+      return "strides must be >= 0 and multiples of 8 elements (k and v: one token stride >= d; paged: "
+             "block_size a multiple of 16, 15 * token_stride + d < 2^31)";
     default: return "unknown status";
   }
 }
@@ -125,6 +132,37 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
     return ATTN_ERR_ALIGNMENT;
   return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, chunk_size,
                                              dtype == ATTN_BF16, scale, stream));
+}
+
+int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                              const attn_paged_kv_t* pages, float* o_part, float* lse_part, int B, int Hq,
+                              int Hkv, int d, int chunk_size, float scale, attn_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !pages || !o_part || !lse_part || !pages->block_table || !pages->seq_lens)
+    return ATTN_ERR_NULL_POINTER;
+  const attn_paged_kv_t& pk = *pages;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || chunk_size <= 0 || pk.num_blocks <= 0 || pk.block_size <= 0 ||
+      pk.max_blocks <= 0)
+    return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  if (pk.block_size % 16 != 0 || pk.page_stride < 0 || pk.token_stride < 0 || pk.head_stride < 0 ||
+      pk.page_stride % 8 || pk.token_stride % 8 || pk.head_stride % 8 || 15 * pk.token_stride + d >= kMaxElems)
+    return ATTN_ERR_LAYOUT;
+  const int64_t M = (int64_t)pk.max_blocks * pk.block_size;
+  const int64_t C = (M + chunk_size - 1) / chunk_size;
+  if (M >= ((int64_t)1 << 30) || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u) || (reinterpret_cast<uintptr_t>(pk.block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pk.seq_lens) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(attn::decode_paged_dispatch(q, k_cache, v_cache, pk.block_table, pk.seq_lens, pk.num_blocks,
+                                                   pk.block_size, pk.max_blocks, pk.page_stride, pk.token_stride,
+                                                   pk.head_stride, o_part, lse_part, B, Hq, Hkv, d, chunk_size,
+                                                   dtype == ATTN_BF16, scale, stream));
 }
 
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int num_chunks,

@@ -209,15 +209,25 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
 // accuracy in P while l is the sum of the unrounded values.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
+
+// Paged KV cache (device pointers and element strides; K and V share them).
+// Page p holds block_size consecutive keys of every KV head: key row r of kv
+// head h starts at p*page_stride + r*token_stride + h*head_stride.
+struct PagedKv {
+  const int32_t* block_table;  // [B, max_blocks]
+  const int32_t* seq_lens;     // [B]
+  int64_t page_stride, token_stride, head_stride;
+  int num_blocks, block_size, max_blocks;
+};
 constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
 constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool PAGED>
 __global__ __launch_bounds__(kDecThreads)
 void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
-                            int chunk, int n_items, float scale_log2) {
+                            int chunk, int n_items, float scale_log2, PagedKv pk) {
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
   constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
@@ -249,6 +259,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   constexpr int kQInst = kGqaCols * kU / 64;
   const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
   const uint32_t voff_lane = (uint32_t)(rl * D * 2 + ((pc ^ swz<D>(rl)) << 4));
+  // paged: a wave's fetch instruction covers kWaveRows consecutive key rows
+  // (4, 8 or 16), which never straddle a page (block_size % 16 == 0), so each
+  // instruction gets its own page descriptor and the lanes offset into it
+  constexpr int kWaveRows = 64 / kU;
+  const uint32_t voff_paged =
+      PAGED ? (uint32_t)((int64_t)(lane / kU) * pk.token_stride * 2) + (uint32_t)((pc ^ swz<D>(rl)) << 4) : 0u;
   // V^T operand: in each 16-lane group of a ds_read_b64_tr_b16, lane s
   // addresses V[K0 + s/4][D0 + 4*(s%4)], so lane i receives V[K0 + 0..3][D0 + i].
   // Group g reads keys 32*ks + 8*g + 4*hh + 0..3 (k-step ks, half hh): slots
@@ -266,14 +282,49 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   const uint32_t pa = p_lds + (uint32_t)((j * kPRow + 8 * g) * 2);               // P[j][32ks + 8g ..]
   const uint32_t pw = p_lds + (uint32_t)((j * kPRow + 32 * wave + 4 * g) * 2);   // P[j][32w + 16kb + 4g ..]
 
+  // paged: the page ids of the next sub-chunk (and, across items, the next
+  // sequence length) are loaded right after the current fetches are issued,
+  // so their latency hides behind those fetches.  Table reads are clamped to
+  // the table; entries past a sequence's end are read but never used.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // keeps page descriptors scalar
+  int nx_item = -1, nx_key0 = 0, nx_seq = 0;
+  int nx_pg[kFetch];
+  auto load_pages = [&](int bb, int kk, int (&pg)[kFetch]) {
+#pragma unroll
+    for (int i = 0; i < kFetch; ++i) {
+      const int e = min((kk + kRowsPerInst * i + wave_u * kWaveRows) / pk.block_size, pk.max_blocks - 1);
+      pg[i] = __builtin_amdgcn_readfirstlane(pk.block_table[(int64_t)bb * pk.max_blocks + e]);
+    }
+  };
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int c = item % C;
     const int rest = item / C;
     const int hs = rest % slices, bkv = rest / slices;
     const int kvh = bkv % Hkv, b = bkv / Hkv;
     const int h0 = kvh * group + hs * G;  // first query head of this item
-    const int c_end = min(M, (c + 1) * chunk);
-    const int64_t slice = ((int64_t)b * Hkv + kvh) * M * D;
+    int seq = M;  // keys of this sequence
+    if constexpr (PAGED) {
+      seq = nx_item == item ? nx_seq : __builtin_amdgcn_readfirstlane(pk.seq_lens[b]);
+      seq = min(max(seq, 0), pk.max_blocks * pk.block_size);
+      if (c * chunk >= seq) {
+        // chunk past the sequence's end: O_c = 0, lse_c = -inf (no weight in the merge)
+        if (j < G) {
+          const int64_t base = ((int64_t)b * Hq + h0 + j) * C + c;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            if (wave >= kPVWaves) break;
+            float* op = o_part + base * D + 16 * (wave * kDB + db) + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(0.f, op + r);
+          }
+          if (wave == 0 && g == 0) __builtin_nontemporal_store(-INFINITY, lse_part + base);
+        }
+        continue;  // uniform over the workgroup; no LDS was touched
+      }
+    }
+    const int c_end = min(seq, (c + 1) * chunk);
+    const int64_t slice = PAGED ? 0 : ((int64_t)b * Hkv + kvh) * M * D;
 
     // Q rows h0 .. h0 + 15 (once per item), then per 128-key sub-chunk its K
     // and V -> LDS, no registers; the buffer loads are bounds-checked, so Q
@@ -293,14 +344,63 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     for (int key0 = c * chunk; key0 < c_end; key0 += kChunk) {
       const int len = min(kChunk, c_end - key0);
       const bool last = key0 + kChunk >= c_end;
+      if constexpr (PAGED) {
+        // this wave's rows of instruction i: rg .. rg + kWaveRows - 1, of which
+        // nv exist; page ids outside [0, num_blocks) read as no rows
+        int pg[kFetch];
+        if (nx_item == item && nx_key0 == key0) {
 #pragma unroll
-      for (int i = 0; i < kFetch; ++i)
-        dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                    voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+          for (int i = 0; i < kFetch; ++i) pg[i] = nx_pg[i];
+        } else {
+          load_pages(b, key0, pg);
+        }
+        int64_t off[kFetch];
+        int nv[kFetch];
 #pragma unroll
-      for (int i = 0; i < kFetch; ++i)
-        dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                    voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+        for (int i = 0; i < kFetch; ++i) {
+          const int rg = key0 + kRowsPerInst * i + wave_u * kWaveRows;
+          nv[i] = min(kWaveRows, seq - rg);
+          int page = pg[i];
+          if (page < 0 || page >= pk.num_blocks) nv[i] = 0;
+          if (nv[i] <= 0) page = 0;
+          off[i] = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
+                   (int64_t)(rg % pk.block_size) * pk.token_stride;
+        }
+#pragma unroll
+        for (int i = 0; i < kFetch; ++i)
+          dma16<true>(make_desc_rows(k + off[i], pk.token_stride, max(nv[i], 0), D),
+                      k_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
+#pragma unroll
+        for (int i = 0; i < kFetch; ++i)
+          dma16<true>(make_desc_rows(v + off[i], pk.token_stride, max(nv[i], 0), D),
+                      v_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
+        // prefetch the next sub-chunk's page ids (the next item's, with its length)
+        if (key0 + kChunk < c_end) {
+          nx_item = item;
+          nx_key0 = key0 + kChunk;
+          nx_seq = seq;
+          load_pages(b, nx_key0, nx_pg);
+        } else {
+          const int n = item + (int)gridDim.x;
+          nx_item = -1;
+          if (n < n_items) {
+            const int bn = n / C / slices / Hkv;
+            nx_item = n;
+            nx_key0 = (n % C) * chunk;
+            nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bn]);
+            load_pages(bn, nx_key0, nx_pg);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kFetch; ++i)
+          dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                      voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+#pragma unroll
+        for (int i = 0; i < kFetch; ++i)
+          dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                      voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+      }
       wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
       __syncthreads();    // Q and K visible
 
@@ -456,8 +556,10 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
     const float l2 = lp[c] * kLog2e;
     const float4 ov = *reinterpret_cast<const float4*>(op + (int64_t)c * D);
     const float mn = fmaxf(st.m, l2);
-    const float r = __builtin_amdgcn_exp2f(st.m - mn);   // 0 on the first chunk (m = -inf)
-    const float w = __builtin_amdgcn_exp2f(l2 - mn);
+    // an empty state (m = -inf) or an empty chunk (lse = -inf) has no weight,
+    // also when both are empty (mn = -inf)
+    const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
+    const float w = l2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l2 - mn);
     st.s = fmaf(st.s, r, w);
     st.a[0] = fmaf(st.a[0], r, w * ov.x);
     st.a[1] = fmaf(st.a[1], r, w * ov.y);
@@ -490,9 +592,10 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
   }
 }
 
-// Resident workgroups per CU for a kernel, times the CU count (cached per device).
-template <typename K>
-static int resident_grid(K kernel, int threads) {
+// Resident workgroups per CU for a kernel, times the CU count (cached per
+// kernel and device: the template parameter gives every kernel its own cache).
+template <auto Kernel>
+static int resident_grid(int threads) {
   constexpr int kMaxDev = 64;
   static int cache[kMaxDev] = {0};
   int dev = 0;
@@ -500,7 +603,7 @@ static int resident_grid(K kernel, int threads) {
   if (dev < kMaxDev && cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int g = cus * per_cu;
   if (dev < kMaxDev) cache[dev] = g;
@@ -525,10 +628,10 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
     const int n_items = B * (Hq / g) * C;
 #define ATTN_GQA_CASE(DD, BB)                                                                          \
     if (d == DD && bf16 == BB) {                                                                       \
-      const int grid = std::min(n_items, resident_grid(decode_gqa_mfma_kernel<DD, BB>, kDecThreads));  \
-      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,   \
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, \
-                         Hq, Hkv, M, C, g, chunk, n_items, sl2);                                       \
+      const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false>>(kDecThreads)); \
+      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,      \
+                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{});                                 \
       return hipGetLastError();                                                                        \
     }
     ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
@@ -539,7 +642,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   const int n_items = B * Hq * C;
 #define ATTN_DEC_CASE(DD, BB)                                                                          \
   if (d == DD && bf16 == BB) {                                                                         \
-    const int grid = std::min(n_items, resident_grid(decode_chunk_kernel<DD, BB>, kDecThreads));    \
+    const int grid = std::min(n_items, resident_grid<decode_chunk_kernel<DD, BB>>(kDecThreads));    \
     hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,     \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
                        Hq, Hkv, M, C, n_items, sl2);                                                   \
@@ -548,6 +651,33 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   ATTN_DEC_CASE(32, false) ATTN_DEC_CASE(32, true)
   ATTN_DEC_CASE(64, false) ATTN_DEC_CASE(64, true) ATTN_DEC_CASE(128, false) ATTN_DEC_CASE(128, true)
 #undef ATTN_DEC_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
+                                 int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
+                                 int64_t head_stride, float* o_part, float* lse_part, int B, int Hq, int Hkv,
+                                 int d, int chunk, bool bf16, float scale, hipStream_t stream) {
+  const int M = max_blocks * block_size;  // longest sequence the table can describe
+  const int C = (M + chunk - 1) / chunk;
+  const float sl2 = scale * kLog2e;
+  const int group = Hq / Hkv;
+  int g = std::min(group, kGqaCols);
+  while (group % g != 0) --g;
+  const int n_items = B * (Hq / g) * C;
+  const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
+#define ATTN_PAGED_CASE(DD, BB)                                                                        \
+  if (d == DD && bf16 == BB) {                                                                         \
+    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true>>(kDecThreads)); \
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, o_part,     \
+                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk);                               \
+    return hipGetLastError();                                                                          \
+  }
+  ATTN_PAGED_CASE(32, false) ATTN_PAGED_CASE(32, true) ATTN_PAGED_CASE(64, false) ATTN_PAGED_CASE(64, true)
+  ATTN_PAGED_CASE(128, false) ATTN_PAGED_CASE(128, true)
+#undef ATTN_PAGED_CASE
   return hipErrorInvalidValue;
 }
 

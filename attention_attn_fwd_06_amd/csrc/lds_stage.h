@@ -42,6 +42,12 @@ __device__ __forceinline__ i32x4 make_desc(const uint16_t* base, int64_t row_str
   const uint64_t addr = (uint64_t)(uintptr_t)base;
   return (i32x4){(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
+// The same over M >= 0 rows: with M == 0 the size is 0 and every offset reads as zero.
+__device__ __forceinline__ i32x4 make_desc_rows(const uint16_t* base, int64_t row_stride, int M, int D) {
+  const int64_t bytes = M > 0 ? ((int64_t)(M - 1) * row_stride + D) * 2 : 0;
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  return (i32x4){(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
 
 // One buffer_load_dwordx4 ... lds: lane L's 16 bytes at byte offset voff of the
 // buffer go to LDS byte address lds + 16 * L (M0 holds lds).  Inline asm, so

@@ -10,6 +10,10 @@
  *   attn_decode_splitkv  Flash-Decoding step 1: per-chunk partial outputs O_c and
  *                        log-sum-exp lse_c of a single query ("CUDA Flash Decoding",
  *                        section 2.2, step 1).
+ *   attn_decode_paged_splitkv  the same partials over a paged KV cache with
+ *                        per-sequence lengths (attention over KV-cache blocks, listed
+ *                        as future work on the "fmha sm120" page; layout is the
+ *                        library's, see attn_paged_kv_t).
  *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
  *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
  *                        section 2.2, step 2, and section 6 "reduce kernel").
@@ -134,6 +138,51 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v,
                         float* o_part, float* lse_part,
                         int B, int Hq, int Hkv, int M, int d, int chunk_size, float scale,
                         attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Paged KV cache for attn_decode_paged_splitkv (the "fmha sm120" page lists
+ * attention over KV-cache blocks as future work and defines no layout; this is
+ * the library's).  A page holds block_size consecutive keys of every KV head;
+ * element (page p, key row r, kv head h, column c) of k_cache / v_cache is at
+ * p*page_stride + r*token_stride + h*head_stride + c (elements; the columns are
+ * contiguous).  [num_blocks, block_size, Hkv, d] token-major pages have strides
+ * {block_size*Hkv*d, Hkv*d, d}; [num_blocks, Hkv, block_size, d] head-major pages
+ * {Hkv*block_size*d, d, block_size*d}.  Key t of sequence b is row
+ * t % block_size of page block_table[b*max_blocks + t / block_size]; sequence b
+ * holds seq_lens[b] keys (1 .. max_blocks*block_size).  block_table and seq_lens
+ * are device memory, read by the kernel.
+ */
+typedef struct {
+  const int32_t* block_table;   /* [B, max_blocks] page ids in [0, num_blocks) */
+  const int32_t* seq_lens;      /* [B] keys per sequence */
+  int num_blocks;               /* pages in each cache */
+  int block_size;               /* keys per page, a multiple of 16 */
+  int max_blocks;               /* columns of block_table */
+  int64_t page_stride, token_stride, head_stride;  /* element strides, multiples of 8 */
+} attn_paged_kv_t;
+
+/*
+ * attn_decode_paged_splitkv - attn_decode_splitkv over a paged KV cache with
+ * per-sequence lengths.
+ *
+ *   q        [B, Hq, d]     dtype, read
+ *   k_cache, v_cache        dtype, read (layout in attn_paged_kv_t, same strides)
+ *   o_part   [B, Hq, C, d]  fp32, written;  lse_part [B, Hq, C] fp32, written
+ *
+ * with C = ceil(max_blocks*block_size / chunk_size).  Sequence b's chunks are
+ * those of attn_decode_splitkv on its keys; chunks past its end get o_part = 0
+ * and lse_part = -inf, which lse_merge gives no weight.  Page ids outside
+ * [0, num_blocks) and lengths outside [0, max_blocks*block_size] are clamped
+ * to no keys rather than read.  Requires the attn_decode_splitkv conditions on
+ * B, Hq, Hkv, d, chunk_size and scale, block_size % 16 == 0, strides >= 0 and
+ * multiples of 8 with 15*token_stride + d below 2^31 (else ATTN_ERR_LAYOUT),
+ * and max_blocks*block_size below 2^30.  The workspace size is
+ * attn_decode_workspace_bytes(B, Hq, max_blocks*block_size, d, chunk_size).
+ */
+int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                              const attn_paged_kv_t* pages, float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int d, int chunk_size, float scale,
+                              attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * lse_merge - combine chunk partials into the decode output.

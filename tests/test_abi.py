@@ -26,8 +26,8 @@ def status_codes():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv", "lse_merge",
-         "attn_status_string"])
+        ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
+         "attn_decode_paged_splitkv", "lse_merge", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -144,6 +144,32 @@ def dec(**kw):
 ])
 def test_decode_rejects(kw, code):
     assert dec(**kw) == code
+
+
+def paged(**kw):
+    """attn_decode_paged_splitkv with a page table whose pointers are fake."""
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, op=FAKE, lp=FAKE, B=2, Hq=8, Hkv=2, d=128, chunk=128, scale=0.088,
+             dtype=1, stream=None, bt=FAKE, sl=FAKE, nb=64, bs=16, mb=32, ps=16 * 2 * 128, ts=2 * 128, hs=128,
+             pages=True)
+    a.update(kw)
+    pk = _lib.PagedKv(a["bt"], a["sl"], a["nb"], a["bs"], a["mb"], a["ps"], a["ts"], a["hs"])
+    return _lib.load().attn_decode_paged_splitkv(a["q"], a["kc"], a["vc"], ctypes.byref(pk) if a["pages"] else None,
+                                                 a["op"], a["lp"], a["B"], a["Hq"], a["Hkv"], a["d"], a["chunk"],
+                                                 a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(pages=False), -1), (dict(bt=None), -1), (dict(sl=None), -1),
+    (dict(op=None), -1),
+    (dict(B=0), -2), (dict(nb=0), -2), (dict(bs=0), -2), (dict(mb=0), -2),
+    (dict(d=96), -3), (dict(dtype=2), -4), (dict(Hq=8, Hkv=3), -5), (dict(chunk=100), -7),
+    (dict(scale=float("nan")), -11),
+    (dict(bs=24), -12), (dict(ts=-8), -12), (dict(ps=12), -12), (dict(hs=4), -12), (dict(ts=1 << 28), -12),
+    (dict(mb=1 << 26, bs=16), -9), (dict(B=70000, Hq=1, Hkv=1), -9),
+    (dict(kc=FAKE + 8), -10), (dict(bt=FAKE + 2), -10), (dict(lp=FAKE + 2), -10),
+])
+def test_paged_decode_rejects(kw, code):
+    assert paged(**kw) == code
 
 
 def mrg(**kw):

@@ -321,6 +321,92 @@ def test_decode_chunk_sizes(shape):
     check_decode(q, k, v, chunk, float(np.float32(d ** -0.5)), dt, str(shape))
 
 
+# paged KV cache: shuffled pages, NaN in every row no sequence owns (rows past
+# a sequence's end inside its last page, and spare pages), table slots past a
+# sequence holding -1 or out-of-range ids, so a stray read shows up as NaN
+def paged_inputs(B, Hq, Hkv, lens, d, dt, bs, seed, head_major):
+    M = max(lens)
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=seed)
+    nblk = [-(-n // bs) for n in lens]
+    max_blocks = max(nblk) + 1
+    total = sum(nblk) + 3
+    order = torch.randperm(total, generator=torch.Generator().manual_seed(seed)).tolist()
+    tdt = torch_dtype(dt)
+    shape = (total, Hkv, bs, d) if head_major else (total, bs, Hkv, d)
+    kc = torch.full(shape, float("nan"), dtype=tdt)
+    vc = torch.full(shape, float("nan"), dtype=tdt)
+    kv_k = kc.transpose(1, 2) if head_major else kc   # [pages, bs, Hkv, d] views
+    kv_v = vc.transpose(1, 2) if head_major else vc
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for j in range(nblk[b]):
+            pg = order[nxt]
+            nxt += 1
+            table[b, j] = pg
+            lo, hi = j * bs, min((j + 1) * bs, lens[b])
+            kv_k[pg, :hi - lo] = k[b, :, lo:hi].transpose(0, 1)
+            kv_v[pg, :hi - lo] = v[b, :, lo:hi].transpose(0, 1)
+        if nblk[b] < max_blocks:
+            table[b, nblk[b]] = total + 5 if b % 2 else -1
+    return q, kc, vc, kv_k, kv_v, table, torch.tensor(lens, dtype=torch.int32)
+
+
+PAGED_CASES = [
+    # B, Hq, Hkv, lens, d, dtype, block_size, chunk, head_major
+    (3, 8, 2, (1, 200, 1000), 128, "bf16", 16, 128, False),
+    (2, 4, 4, (777, 64), 64, "f16", 64, 256, True),
+    (4, 32, 8, (5000, 3, 128, 4097), 128, "f16", 256, 512, False),
+    (2, 16, 1, (130, 16), 32, "bf16", 32, 128, True),
+    (1, 2, 1, (2048,), 128, "f16", 128, 128, False),
+    (2, 12, 4, (300, 2000), 64, "bf16", 48, 1024, False),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_decode_paged(case):
+    B, Hq, Hkv, lens, d, dt, bs, chunk, head_major = case
+    say(f"case paged decode {case}")
+    q, kc, vc, kv_k, kv_v, table, sl = paged_inputs(B, Hq, Hkv, list(lens), d, dt, bs, seed=sum(lens), head_major=head_major)
+    scale = float(np.float32(d ** -0.5))
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    kvk_d = kd.transpose(1, 2) if head_major else kd
+    kvv_d = vd.transpose(1, 2) if head_major else vd
+    o, lse, op, lp = attn().attn_decode_paged(q.to(DEV), kvk_d, kvv_d, table.to(DEV), sl.to(DEV), chunk, scale)
+    torch.cuda.synchronize()
+    Or, Lr, OPr, LPr = oracle.paged_decode_ref(q, kv_k, kv_v, table.clamp(min=0), sl, scale, chunk)
+    OPg, LPg = f64(op), f64(lp)
+    full = np.isfinite(LPr)
+    assert np.array_equal(np.isfinite(LPg), full), "empty chunks must be exactly the chunks past each end"
+    assert np.all(OPg[~full] == 0.0)
+    errs = dict(o=maxerr(f64(o), Or), lse=maxerr(f64(lse), Lr),
+                o_part=maxerr(OPg[full], OPr[full]), lse_part=maxerr(LPg[full], LPr[full]))
+    say(f"  {case}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
+    assert errs["o"] <= TOL_O[dt] and errs["o_part"] <= TOL_O[dt], errs
+    assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
+
+
+def test_decode_paged_matches_contiguous():
+    """One sequence in pages in order decodes like the contiguous decode."""
+    say("case paged vs contiguous decode")
+    B, Hq, Hkv, M, d = 2, 8, 2, 1500, 128
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, "bf16", seed=21)
+    bs = 32
+    nb = -(-M // bs)
+    pad = nb * bs - M
+    kp = torch.nn.functional.pad(k, (0, 0, 0, pad)).reshape(B, Hkv, nb, bs, d).permute(0, 2, 3, 1, 4)
+    vp = torch.nn.functional.pad(v, (0, 0, 0, pad)).reshape(B, Hkv, nb, bs, d).permute(0, 2, 3, 1, 4)
+    kc = kp.reshape(B * nb, bs, Hkv, d).contiguous().to(DEV)
+    vc = vp.reshape(B * nb, bs, Hkv, d).contiguous().to(DEV)
+    table = torch.arange(B * nb, dtype=torch.int32).reshape(B, nb).to(DEV)
+    sl = torch.full((B,), M, dtype=torch.int32, device=DEV)
+    o1, l1, _, _ = attn().attn_decode_paged(q.to(DEV), kc, vc, table, sl, 128, 0.09)
+    o2, l2, _, _ = attn().attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), 128, 0.09)
+    torch.cuda.synchronize()
+    assert maxerr(f64(o1), f64(o2)) <= TOL_O["bf16"]
+    assert maxerr(f64(l1), f64(l2)) <= TOL_LSE
+
+
 @pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
 def test_lse_merge_standalone(C, d, dt):
     say(f"case lse_merge C={C} d={d} {dt}")
