@@ -288,7 +288,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // the table; entries past a sequence's end are read but never used.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // keeps page descriptors scalar
   int nx_item = -1, nx_key0 = 0, nx_seq = 0;
-  int nx_pg[kFetch];
+  int pg[kFetch];  // page ids of the current sub-chunk, then the prefetched ones
   auto load_pages = [&](int bb, int kk, int (&pg)[kFetch]) {
 #pragma unroll
     for (int i = 0; i < kFetch; ++i) {
@@ -347,39 +347,27 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       if constexpr (PAGED) {
         // this wave's rows of instruction i: rg .. rg + kWaveRows - 1, of which
         // nv exist; page ids outside [0, num_blocks) read as no rows
-        int pg[kFetch];
-        if (nx_item == item && nx_key0 == key0) {
-#pragma unroll
-          for (int i = 0; i < kFetch; ++i) pg[i] = nx_pg[i];
-        } else {
-          load_pages(b, key0, pg);
-        }
-        int64_t off[kFetch];
-        int nv[kFetch];
+        if (nx_item != item || nx_key0 != key0) load_pages(b, key0, pg);
 #pragma unroll
         for (int i = 0; i < kFetch; ++i) {
           const int rg = key0 + kRowsPerInst * i + wave_u * kWaveRows;
-          nv[i] = min(kWaveRows, seq - rg);
+          int nv = min(kWaveRows, seq - rg);
           int page = pg[i];
-          if (page < 0 || page >= pk.num_blocks) nv[i] = 0;
-          if (nv[i] <= 0) page = 0;
-          off[i] = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
-                   (int64_t)(rg % pk.block_size) * pk.token_stride;
-        }
-#pragma unroll
-        for (int i = 0; i < kFetch; ++i)
-          dma16<true>(make_desc_rows(k + off[i], pk.token_stride, max(nv[i], 0), D),
+          if (page < 0 || page >= pk.num_blocks) nv = 0;
+          if (nv <= 0) page = 0;
+          const int64_t off = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
+                              (int64_t)(rg % pk.block_size) * pk.token_stride;
+          dma16<true>(make_desc_rows(k + off, pk.token_stride, max(nv, 0), D),
                       k_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
-#pragma unroll
-        for (int i = 0; i < kFetch; ++i)
-          dma16<true>(make_desc_rows(v + off[i], pk.token_stride, max(nv[i], 0), D),
+          dma16<true>(make_desc_rows(v + off, pk.token_stride, max(nv, 0), D),
                       v_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
+        }
         // prefetch the next sub-chunk's page ids (the next item's, with its length)
         if (key0 + kChunk < c_end) {
           nx_item = item;
           nx_key0 = key0 + kChunk;
           nx_seq = seq;
-          load_pages(b, nx_key0, nx_pg);
+          load_pages(b, nx_key0, pg);
         } else {
           const int n = item + (int)gridDim.x;
           nx_item = -1;
@@ -388,7 +376,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             nx_item = n;
             nx_key0 = (n % C) * chunk;
             nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bn]);
-            load_pages(bn, nx_key0, nx_pg);
+            load_pages(bn, nx_key0, pg);
           }
         }
       } else {
@@ -401,7 +389,10 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
                       voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
       }
-      wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
+      // paged: K and V of one instruction are issued together (each descriptor
+      // lives briefly, and this measured faster than K first), so wait for both
+      if constexpr (PAGED) wait_tile_loads();
+      else wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
       __syncthreads();    // Q and K visible
 
       // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7; B operand:
