@@ -37,13 +37,19 @@ notes of the repository):
     paged decode computes exactly the decode of each sequence's gathered keys;
     chunks past a sequence's end have O_c = 0 and lse_c = -inf (no weight in
     the merge).
+  * FP8 KV (the "fmha sm120" page lists fp8 KV quantisation as future work,
+    with no format): K and V are OCP FP8 E4M3 codes with one fp32 scale each,
+    K = k_scale * e4m3(k), V = v_scale * e4m3(v); the decode of these values is
+    the plain decode.  E4M3 (OCP "e4m3fn"): sign bit, 4 exponent bits with bias
+    7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN;
+    there are no infinities.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref", "paged_decode_partials_ref",
-           "paged_decode_ref"]
+           "paged_decode_ref", "e4m3_decode", "decode_fp8kv_partials_ref", "decode_fp8kv_ref"]
 
 
 def _f64(x) -> np.ndarray:
@@ -205,5 +211,31 @@ def paged_decode_ref(q, k_cache, v_cache, block_table, seq_lens, scale: float, c
     """Paged split-KV decode end to end.  Returns (O [B, Hq, d], lse [B, Hq],
     o_part, lse_part)."""
     o_part, lse_part = paged_decode_partials_ref(q, k_cache, v_cache, block_table, seq_lens, scale, chunk)
+    O, lse = lse_merge_ref(o_part, lse_part)
+    return O, lse, o_part, lse_part
+
+
+def e4m3_decode(codes):
+    """Values of OCP FP8 E4M3 codes (uint8), from the format's definition."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_fp8kv_partials_ref(q, k_codes, v_codes, k_scale: float, v_scale: float, scale: float, chunk: int):
+    """Split-KV decode partials with K/V given as E4M3 codes and fp32 scales:
+    the decode of K = k_scale * e4m3(k), V = v_scale * e4m3(v)."""
+    k = e4m3_decode(k_codes) * float(np.float32(k_scale))
+    v = e4m3_decode(v_codes) * float(np.float32(v_scale))
+    return decode_partials_ref(q, k, v, scale, chunk)
+
+
+def decode_fp8kv_ref(q, k_codes, v_codes, k_scale: float, v_scale: float, scale: float, chunk: int):
+    """FP8-KV split-KV decode end to end.  Returns (O, lse, o_part, lse_part)."""
+    o_part, lse_part = decode_fp8kv_partials_ref(q, k_codes, v_codes, k_scale, v_scale, scale, chunk)
     O, lse = lse_merge_ref(o_part, lse_part)
     return O, lse, o_part, lse_part

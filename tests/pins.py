@@ -352,6 +352,37 @@ def check_paged_decode_variable_lengths(ora):
         assert np.all(lp[b, :, nc:] == -np.inf) and np.all(op[b, :, nc:] == 0.0), "empty chunks"
 
 
+def check_e4m3_decode(ora):
+    """The E4M3 decoder against torch's float8_e4m3fn on all 256 codes, and
+    values the format fixes."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = ora.e4m3_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(lib)), "NaN codes"
+    ok = ~np.isnan(lib)
+    _close(mine[ok], lib[ok], tol=0.0, what="e4m3 values")
+    fixed = {0x00: 0.0, 0x38: 1.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x7E: 448.0, 0xFE: -448.0, 0x41: 2.25}
+    for c, val in fixed.items():
+        _close(ora.e4m3_decode(np.array([c], dtype=np.uint8)), [val], tol=0.0, what=f"code {c:#x}")
+
+
+def check_fp8kv_decode_is_decode_of_scaled_values(ora):
+    B, Hq, Hkv, M, d = 2, 4, 2, 21, 5
+    q = _rand((B, Hq, d), 400)
+    g = np.random.default_rng(401)
+    kc = g.integers(0, 256, (B, Hkv, M, d)).astype(np.uint8)
+    vc = g.integers(0, 256, (B, Hkv, M, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x10     # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x22
+    lib = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    ks, vs = float(np.float32(0.02)), 3.0    # the fp32 scales a caller hands over
+    O, L, op, lp = ora.decode_fp8kv_ref(q, kc, vc, ks, vs, 0.5, 8)
+    Or, Lr, opr, lpr = ora.decode_ref(q, lib(kc) * ks, lib(vc) * vs, 0.5, 8)
+    _close(O, Or, what="fp8 kv output")
+    _close(L, Lr, what="fp8 kv lse")
+    _close(op, opr, what="fp8 kv partials")
+
+
 FAST_CHECKS = [
     check_brute_prefill_tiny, check_brute_decode_tiny, check_sdpa,
     check_identity_v_rows_are_probabilities, check_constant_v, check_single_key,
@@ -359,6 +390,7 @@ FAST_CHECKS = [
     check_gqa_is_repeated_mha, check_decode_is_single_query_attention,
     check_merge_identities, check_two_keys_closed_form, check_causal_chunk_is_tail_of_full,
     check_paged_decode_is_decode_of_gathered_keys, check_paged_decode_variable_lengths,
+    check_e4m3_decode, check_fp8kv_decode_is_decode_of_scaled_values,
 ]
 
 

@@ -38,6 +38,12 @@ MUTANTS = {
     "paged_page_in_order": ("pages, rows = bt[b, t // bs], t % bs", "pages, rows = t // bs, t % bs"),
     "paged_ignores_length": ("t = np.arange(int(sl[b]))", "t = np.arange(bt.shape[1] * bs)"),
     "paged_empty_chunks_weighted": ("lse_part = np.full((B, Hq, C), -np.inf)", "lse_part = np.zeros((B, Hq, C))"),
+    "e4m3_bias_8": ("np.exp2((e - 7).astype(np.float64))", "np.exp2((e - 8).astype(np.float64))"),
+    "e4m3_subnormal_as_normal": ("(m / 8.0) * 2.0 ** -6", "(1.0 + m / 8.0) * 2.0 ** -7"),
+    "e4m3_sign_dropped": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = 1.0"),
+    "fp8kv_k_scale_dropped": ("k = e4m3_decode(k_codes) * float(np.float32(k_scale))", "k = e4m3_decode(k_codes)"),
+    "fp8kv_scales_swapped": ("v = e4m3_decode(v_codes) * float(np.float32(v_scale))",
+                             "v = e4m3_decode(v_codes) * float(np.float32(k_scale))"),
 }
 
 
