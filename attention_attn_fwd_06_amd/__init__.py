@@ -15,7 +15,7 @@ from . import _lib
 __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
-    "attn_decode_paged",
+    "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv",
 ]
 
 ATTN_F16 = 0
@@ -165,6 +165,40 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
     if st != 0:
         raise AttnError(st, "attn_decode_paged_splitkv")
     return o_part, lse_part
+
+
+def attn_decode_fp8kv_splitkv(q, k, v, k_scale: float, v_scale: float, chunk_size: int = 128,
+                              scale: float | None = None, o_part=None, lse_part=None, stream=None):
+    """q [B,Hq,d] fp16/bf16; k, v [B,Hkv,M,d] E4M3 codes (torch.float8_e4m3fn or uint8);
+    K = k_scale * e4m3(k), V = v_scale * e4m3(v).  Returns (o_part, lse_part)."""
+    _check(q, "q")
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n)
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold E4M3 codes (torch.float8_e4m3fn or uint8)")
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    C = -(-M // chunk_size)
+    if scale is None:
+        scale = d ** -0.5
+    if o_part is None:
+        o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_decode_fp8kv_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(k_scale),
+                                               float(v_scale), o_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv,
+                                               M, d, chunk_size, float(scale), _dtype_code(q), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fp8kv_splitkv")
+    return o_part, lse_part
+
+
+def attn_decode_fp8kv(q, k, v, k_scale: float, v_scale: float, chunk_size: int = 128,
+                      scale: float | None = None, stream=None):
+    """FP8-KV split-KV decode end to end (partials, then the merge)."""
+    o_part, lse_part = attn_decode_fp8kv_splitkv(q, k, v, k_scale, v_scale, chunk_size, scale, stream=stream)
+    o, lse = lse_merge(o_part, lse_part, q.dtype, stream=stream)
+    return o, lse, o_part, lse_part
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,

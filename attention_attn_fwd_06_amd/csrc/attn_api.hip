@@ -23,6 +23,9 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
                                  int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
                                  int64_t head_stride, float* o_part, float* lse_part, int B, int Hq, int Hkv,
                                  int d, int chunk, bool bf16, float scale, hipStream_t stream);
+hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                                 float* o_part, float* lse_part, int B, int Hq, int Hkv, int M, int d, int chunk,
+                                 bool bf16, float scale, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -54,7 +57,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
-    case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    case ATTN_ERR_SCALE: return "scales must be finite and >= 0";
     case ATTN_ERR_LAYOUT:
       return "strides must be >= 0 and multiples of 8 elements (k and v: one token stride >= d; paged: "
              "block_size a multiple of 16, 15 * token_stride + d < 2^31)";
@@ -132,6 +135,29 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
     return ATTN_ERR_ALIGNMENT;
   return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, chunk_size,
                                              dtype == ATTN_BF16, scale, stream));
+}
+
+int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                              float* o_part, float* lse_part, int B, int Hq, int Hkv, int M, int d, int chunk_size,
+                              float scale, attn_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o_part || !lse_part) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || chunk_size <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite(k_scale) || k_scale < 0.f || !std::isfinite(v_scale) ||
+      v_scale < 0.f)
+    return ATTN_ERR_SCALE;
+  const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
+  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535 ||
+      (int64_t)(M + kDecodeChunk) * d >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(attn::decode_fp8kv_dispatch(q, k, v, k_scale, v_scale, o_part, lse_part, B, Hq, Hkv, M, d,
+                                                   chunk_size, dtype == ATTN_BF16, scale, stream));
 }
 
 int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,

@@ -64,6 +64,12 @@ __device__ __forceinline__ float row_sum(float x) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes of FP8 codes, streamed.
+__device__ __forceinline__ uint4 load_stream8(const uint8_t* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // 16-byte load that streams past the caches (K/V are read exactly once).
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -209,6 +215,7 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
 // accuracy in P while l is the sum of the unrounded values.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // Paged KV cache (device pointers and element strides; K and V share them).
 // Page p holds block_size consecutive keys of every KV head: key row r of kv
@@ -222,12 +229,13 @@ struct PagedKv {
 constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
 constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
 
-template <int D, bool BF16, bool PAGED>
+template <int D, bool BF16, bool PAGED, bool KV8>
 __global__ __launch_bounds__(kDecThreads)
 void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
-                            int chunk, int n_items, float scale_log2, PagedKv pk) {
+                            int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale) {
+  static_assert(!(PAGED && KV8), "paged FP8 KV is not built");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
   constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
@@ -294,6 +302,26 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     for (int i = 0; i < kFetch; ++i) {
       const int e = min((kk + kRowsPerInst * i + wave_u * kWaveRows) / pk.block_size, pk.max_blocks - 1);
       pg[i] = __builtin_amdgcn_readfirstlane(pk.block_table[(int64_t)bb * pk.max_blocks + e]);
+    }
+  };
+
+  // FP8 KV: each thread's 16-byte pieces of a 128-key sub-chunk; after the
+  // current pieces are converted, the next sub-chunk's (or next item's first)
+  // are loaded into the same registers, so that load overlaps this sub-chunk's
+  // products.  kv8_item / kv8_key0 name what the registers hold (-1: nothing).
+  constexpr int kPR8 = D / 16;                       // 16-byte pieces per FP8 row
+  constexpr int kPieces8 = kChunk * kPR8 / kDecThreads;
+  uint4 kr8[kPieces8], vr8[kPieces8];
+  int kv8_item = -1, kv8_key0 = 0;
+  auto load8 = [&](int bb, int kvhh, int kk) {
+    const int64_t base = ((int64_t)bb * Hkv + kvhh) * M * D;
+#pragma unroll
+    for (int p = 0; p < kPieces8; ++p) {
+      const int u = p * kDecThreads + tid, row = u / kPR8;
+      const bool ok = kk + row < M;
+      const int64_t off = base + (int64_t)(kk + row) * D + 16 * (u % kPR8);
+      kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
+      vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -379,6 +407,47 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             load_pages(bn, nx_key0, pg);
           }
         }
+      } else if constexpr (KV8) {
+        // FP8 KV: 16-byte pieces of E4M3 rows (consecutive threads read
+        // consecutive pieces), converted exactly to 16 bits in registers and
+        // written to the same swizzled layout; rows past M read as zeros
+        if (kv8_item != item || kv8_key0 != key0) load8(b, kvh, key0);
+        auto put = [&](uint32_t base, const uint4& w, int row, int pc8) {
+          const uint32_t* b4 = reinterpret_cast<const uint32_t*>(&w);
+          uint32_t h[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], true);
+            h[2 * t] = pack2<BF16>(lo[0], lo[1]);
+            h[2 * t + 1] = pack2<BF16>(hi[0], hi[1]);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int lc = 2 * pc8 + half;
+            *(lds_u32x4*)(uintptr_t)(base + (uint32_t)(row * D * 2 + ((lc ^ swz<D>(row)) << 4))) =
+                (u32x4){h[4 * half], h[4 * half + 1], h[4 * half + 2], h[4 * half + 3]};
+          }
+        };
+#pragma unroll
+        for (int p = 0; p < kPieces8; ++p) {
+          const int u = p * kDecThreads + tid;
+          put(k_lds, kr8[p], u / kPR8, u % kPR8);
+          put(v_lds, vr8[p], u / kPR8, u % kPR8);
+        }
+        // prefetch the next sub-chunk, or the next item's first one
+        kv8_item = -1;
+        if (key0 + kChunk < c_end) {
+          kv8_item = item;
+          kv8_key0 = key0 + kChunk;
+          load8(b, kvh, kv8_key0);
+        } else if (item + (int)gridDim.x < n_items) {
+          const int n = item + (int)gridDim.x;
+          const int bkv_n = n / C / slices;
+          kv8_item = n;
+          kv8_key0 = (n % C) * chunk;
+          load8(bkv_n / Hkv, bkv_n % Hkv, kv8_key0);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < kFetch; ++i)
@@ -392,6 +461,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       // paged: K and V of one instruction are issued together (each descriptor
       // lives briefly, and this measured faster than K first), so wait for both
       if constexpr (PAGED) wait_tile_loads();
+      else if constexpr (KV8) wait_vm<2 * kPieces8>();  // Q landed; only the prefetch may be in flight
       else wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
       __syncthreads();    // Q and K visible
 
@@ -426,7 +496,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = max_xor32(mx);
       if (g == 0) red[0][wave][j] = mx;
-      wait_tile_loads();  // this wave's part of the V sub-chunk is in LDS
+      if constexpr (!KV8) wait_tile_loads();  // this wave's part of the V sub-chunk is in LDS
       __syncthreads();    // V sub-chunk and the per-wave maxima visible
       float m = m_run;
 #pragma unroll
@@ -483,7 +553,8 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       for (int db = 0; db < kDB; ++db) {
         if (wave >= kPVWaves) break;
         float* op = o_part + base * D + 16 * (wave * kDB + db) + 4 * g;
-        const f32x4 o4 = oacc[db] / lt;
+        f32x4 o4 = oacc[db] / lt;
+        if constexpr (KV8) o4 *= v_scale;  // V = v_scale * e4m3(v)
         if (out16) {
           __builtin_nontemporal_store(o4, reinterpret_cast<f32x4*>(op));
         } else {
@@ -619,10 +690,10 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
     const int n_items = B * (Hq / g) * C;
 #define ATTN_GQA_CASE(DD, BB)                                                                          \
     if (d == DD && bf16 == BB) {                                                                       \
-      const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false>>(kDecThreads)); \
-      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+      const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, false>>(kDecThreads)); \
+      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,      \
-                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{});                                 \
+                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{}, 1.f);                                 \
       return hipGetLastError();                                                                        \
     }
     ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
@@ -660,15 +731,38 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
   const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
 #define ATTN_PAGED_CASE(DD, BB)                                                                        \
   if (d == DD && bf16 == BB) {                                                                         \
-    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true>>(kDecThreads)); \
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, false>>(kDecThreads)); \
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, o_part,     \
-                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk);                               \
+                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, 1.f);                               \
     return hipGetLastError();                                                                          \
   }
   ATTN_PAGED_CASE(32, false) ATTN_PAGED_CASE(32, true) ATTN_PAGED_CASE(64, false) ATTN_PAGED_CASE(64, true)
   ATTN_PAGED_CASE(128, false) ATTN_PAGED_CASE(128, true)
 #undef ATTN_PAGED_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                                 float* o_part, float* lse_part, int B, int Hq, int Hkv, int M, int d, int chunk,
+                                 bool bf16, float scale, hipStream_t stream) {
+  const int C = (M + chunk - 1) / chunk;
+  const float sl2 = scale * k_scale * kLog2e;  // K = k_scale * e4m3(k): the scores carry k_scale
+  const int group = Hq / Hkv;
+  int g = std::min(group, kGqaCols);
+  while (group % g != 0) --g;
+  const int n_items = B * (Hq / g) * C;
+#define ATTN_FP8_CASE(DD, BB)                                                                          \
+  if (d == DD && bf16 == BB) {                                                                         \
+    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, true>>(kDecThreads)); \
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false, true>), dim3(grid), dim3(kDecThreads), 0, stream, \
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv,   \
+                       M, C, g, chunk, n_items, sl2, PagedKv{}, v_scale);                                      \
+    return hipGetLastError();                                                                          \
+  }
+  ATTN_FP8_CASE(32, false) ATTN_FP8_CASE(32, true) ATTN_FP8_CASE(64, false) ATTN_FP8_CASE(64, true)
+  ATTN_FP8_CASE(128, false) ATTN_FP8_CASE(128, true)
+#undef ATTN_FP8_CASE
   return hipErrorInvalidValue;
 }
 

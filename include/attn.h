@@ -14,6 +14,9 @@
  *                        per-sequence lengths (attention over KV-cache blocks, listed
  *                        as future work on the "fmha sm120" page; layout is the
  *                        library's, see attn_paged_kv_t).
+ *   attn_decode_fp8kv_splitkv  the same partials with K and V stored as FP8 E4M3
+ *                        codes and per-tensor scales (fp8 KV quantisation, listed as
+ *                        future work on the "fmha sm120" page).
  *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
  *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
  *                        section 2.2, step 2, and section 6 "reduce kernel").
@@ -182,6 +185,25 @@ typedef struct {
 int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,
                               const attn_paged_kv_t* pages, float* o_part, float* lse_part,
                               int B, int Hq, int Hkv, int d, int chunk_size, float scale,
+                              attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_fp8kv_splitkv - attn_decode_splitkv with K and V stored as FP8.
+ *
+ *   q        [B, Hq, d]     dtype (fp16 or bf16), read
+ *   k, v     [B, Hkv, M, d] OCP FP8 E4M3 codes (one byte each), read
+ *   o_part, lse_part        as attn_decode_splitkv
+ *
+ * The keys and values are K = k_scale * e4m3(k) and V = v_scale * e4m3(v) (one
+ * fp32 scale per tensor; the "fmha sm120" page lists fp8 KV quantisation as
+ * future work and fixes no format).  Codes are converted exactly to dtype
+ * inside the kernel; the products and sums are those of attn_decode_splitkv.
+ * NaN codes (S.1111.111) give NaN.  Requires the attn_decode_splitkv
+ * conditions and finite scales >= 0 (else ATTN_ERR_SCALE).
+ */
+int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                              float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int M, int d, int chunk_size, float scale,
                               attn_dtype_t dtype, hipStream_t stream);
 
 /*

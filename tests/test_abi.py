@@ -27,7 +27,7 @@ def status_codes():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
-         "attn_decode_paged_splitkv", "lse_merge", "attn_status_string"])
+         "attn_decode_paged_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -170,6 +170,24 @@ def paged(**kw):
 ])
 def test_paged_decode_rejects(kw, code):
     assert paged(**kw) == code
+
+
+def fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.01, vs=2.0, op=FAKE, lp=FAKE, B=1, Hq=8, Hkv=2, M=512, d=128, chunk=128,
+             scale=0.088, dtype=1, stream=None)
+    a.update(kw)
+    return _lib.load().attn_decode_fp8kv_splitkv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["op"], a["lp"], a["B"],
+                                                 a["Hq"], a["Hkv"], a["M"], a["d"], a["chunk"], a["scale"],
+                                                 a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(lp=None), -1), (dict(M=0), -2), (dict(d=48), -3), (dict(dtype=5), -4),
+    (dict(Hq=6, Hkv=4), -5), (dict(chunk=96), -7), (dict(ks=-1.0), -11), (dict(vs=float("inf")), -11),
+    (dict(ks=float("nan")), -11), (dict(B=70000, Hq=1, Hkv=1), -9), (dict(v=FAKE + 8), -10),
+])
+def test_fp8kv_decode_rejects(kw, code):
+    assert fp8(**kw) == code
 
 
 def mrg(**kw):

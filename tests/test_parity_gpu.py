@@ -407,6 +407,42 @@ def test_decode_paged_matches_contiguous():
     assert maxerr(f64(l1), f64(l2)) <= TOL_LSE
 
 
+# FP8 KV: K, V quantised to E4M3 codes with per-tensor scales (codes drawn by
+# rounding N(0,1) values / scale to E4M3, as a caller's quantiser would)
+def fp8kv_inputs(B, Hq, Hkv, M, d, dt, seed):
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=seed)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(3.0 / 448.0))
+    kc = (k.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc = (v.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q, kc, vc, ks, vs
+
+
+FP8_CASES = [
+    # B, Hq, Hkv, M, d, dtype, chunk
+    (2, 8, 2, 1000, 128, "bf16", 128),
+    (1, 4, 4, 777, 64, "f16", 256),
+    (2, 32, 8, 4096, 128, "f16", 512),
+    (1, 16, 1, 300, 32, "bf16", 128),
+    (3, 8, 8, 129, 128, "bf16", 1024),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_fp8kv(case):
+    B, Hq, Hkv, M, d, dt, chunk = case
+    say(f"case fp8 kv decode {case}")
+    q, kc, vc, ks, vs = fp8kv_inputs(B, Hq, Hkv, M, d, dt, seed=M + d)
+    scale = float(np.float32(d ** -0.5))
+    o, lse, op, lp = attn().attn_decode_fp8kv(q.to(DEV), kc.to(DEV), vc.to(DEV), ks, vs, chunk, scale)
+    torch.cuda.synchronize()
+    Or, Lr, OPr, LPr = oracle.decode_fp8kv_ref(q, kc.numpy(), vc.numpy(), ks, vs, scale, chunk)
+    errs = dict(o=maxerr(f64(o), Or), lse=maxerr(f64(lse), Lr), o_part=maxerr(f64(op), OPr),
+                lse_part=maxerr(f64(lp), LPr))
+    say(f"  {case}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
+    assert errs["o"] <= TOL_O[dt] and errs["o_part"] <= TOL_O[dt], errs
+    assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
+
+
 @pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
 def test_lse_merge_standalone(C, d, dt):
     say(f"case lse_merge C={C} d={d} {dt}")
