@@ -11,7 +11,9 @@ Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 duration, measured with HIP events on the launch stream; the decode result is
 reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).  The
 ``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8, M=16384,
-d=128, bf16; K/V counted once per kv head), timed separately after the steps.
+d=128, bf16; K/V counted once per kv head), timed separately after the steps, and
+``decode_paged`` / ``decode_fp8kv`` the same workload's chunk kernel through the
+paged-KV and FP8-KV entry points.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--prewarm-s 1.5] [--no-cpu-baseline]
 """
@@ -141,6 +143,64 @@ def gqa_decode_rate(attn, w, args, dev):
             "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
             "kernel": "decode_gqa_mfma_kernel<128,bf16>", "algorithmic_bytes": nbytes,
             "bytes_note": "K and V counted once per kv head"}
+
+
+def _time_chunk(fn, args):
+    """Mean HIP-event time (ms) of fn(i) on the current stream over args.steps calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in ev)
+
+
+def paged_and_fp8_rates(attn, w, args, dev):
+    """The grouped-query decode workload through the paged-KV entry point (block
+    16, token-major pages in shuffled order, every sequence full length) and the
+    FP8-KV entry point (E4M3 codes); chunk kernel alone, two input sets
+    alternated.  Bytes: K and V once per kv head (1 byte per element for FP8)."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(args.seed)
+    q = torch.randn((w.B, w.Hq, w.d), generator=g).to(torch.bfloat16).to(dev)
+    C = w.num_chunks
+    o_part = torch.empty((w.B, w.Hq, C, w.d), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device=dev)
+    out = {}
+    bs = 16
+    nb = w.B * w.M // bs
+    sets = []
+    for _ in range(2):
+        kc = torch.randn((nb, bs, w.Hkv, w.d), dtype=torch.bfloat16, device=dev)
+        vc = torch.randn((nb, bs, w.Hkv, w.d), dtype=torch.bfloat16, device=dev)
+        table = torch.randperm(nb, generator=g).to(torch.int32).reshape(w.B, w.M // bs).to(dev)
+        sets.append((kc, vc, table))
+    lens = torch.full((w.B,), w.M, dtype=torch.int32, device=dev)
+    ms = _time_chunk(lambda i: attn.attn_decode_paged_splitkv(q, sets[i % 2][0], sets[i % 2][1], sets[i % 2][2], lens,
+                                                              w.chunk, w.scale, o_part=o_part, lse_part=lse_part), args)
+    nbytes = 2.0 * w.B * w.Hkv * w.M * w.d * 2 + w.B * w.Hq * w.d * 2
+    out["decode_paged"] = {"workload": w.desc + ", paged KV: 16-key token-major pages, shuffled",
+                           "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                           "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "chunk_ms": round(ms, 4),
+                           "kernel": "decode_gqa_mfma_kernel<128,bf16,paged>"}
+    del sets
+    sets8 = [(torch.randint(0, 126, (w.B, w.Hkv, w.M, w.d), dtype=torch.uint8, device=dev),
+              torch.randint(0, 126, (w.B, w.Hkv, w.M, w.d), dtype=torch.uint8, device=dev)) for _ in range(2)]
+    ms8 = _time_chunk(lambda i: attn.attn_decode_fp8kv_splitkv(q, sets8[i % 2][0], sets8[i % 2][1], 0.01, 0.01,
+                                                               w.chunk, w.scale, o_part=o_part, lse_part=lse_part),
+                      args)
+    nbytes8 = 2.0 * w.B * w.Hkv * w.M * w.d + w.B * w.Hq * w.d * 2
+    out["decode_fp8kv"] = {"workload": w.desc + ", K/V as FP8 E4M3 codes",
+                           "value": round(nbytes8 / (ms8 * 1e-3) / 1e9, 1), "unit": "GB/s",
+                           "frac": round(nbytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "chunk_ms": round(ms8, 4),
+                           "kernel": "decode_gqa_mfma_kernel<128,bf16,fp8kv>"}
+    return out
 
 
 def main():
@@ -281,6 +341,7 @@ def main():
             out["value"], out["unit"], out["dtype"] = out["decode"]["value"], "GB/s", "f16"
     if args.only in (None, "decode_gqa"):
         out["decode_gqa"] = gqa_decode_rate(attn, WORKLOADS[DECODE_GQA], args, dev)
+        out.update(paged_and_fp8_rates(attn, WORKLOADS[DECODE_GQA], args, dev))
         if args.only == "decode_gqa":
             out["value"], out["unit"], out["dtype"] = out["decode_gqa"]["value"], "GB/s", "bf16"
     if args.only is None and not args.no_cpu_baseline:
