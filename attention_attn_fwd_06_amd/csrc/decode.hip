@@ -12,11 +12,14 @@
 //    HBM.  Partials are written in fp32 (O_c normalised) with nontemporal
 //    stores: through the write-back caches they cost several percent of the
 //    chunk kernel's time.
-//  * matrix-core kernel (GQA groups, and MHA launches of at least 2048
-//    items): an item is (chunk, batch, kv head, up to 16 query heads of the
-//    group), the heads being the columns of v_mfma_f32_16x16x32, so K and V
-//    are read once per kv head; Q, K and V are staged in LDS, V^T read back
-//    through transposed reads.
+//  * matrix-core kernel (GQA groups, chunks longer than 128 keys, MHA
+//    launches of at least 2048 items, and every paged or FP8 call): an item
+//    is (chunk, batch, kv head, up to 16 query heads of the group), the heads
+//    being the columns of v_mfma_f32_16x16x32, so K and V are read once per
+//    kv head; Q, K and V are staged in LDS, V^T read back through transposed
+//    reads.  Its paged mode fetches each instruction's rows from their page
+//    through a per-page descriptor; its FP8 mode streams E4M3 code rows and
+//    converts them to 16 bits on the way into LDS.
 //  * VALU kernel (small MHA launches): an item is (chunk, batch, query head);
 //    a row of K/V is read by d/8 consecutive lanes, 16 bytes each, scores use
 //    fp32 accumulation (v_dot2_f32_{f16,bf16}) and a DPP sum over the lanes
@@ -196,9 +199,8 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // GQA decode on the matrix cores.  Item = (chunk c of `chunk` keys, a
 // multiple of 128, batch b, kv head, slice of G <= 16 query heads of its
 // group); the chunk is walked in 128-key sub-chunks with the online-softmax
-// rescale between them.  The G heads are the 16
-// columns of v_mfma_f32_16x16x32 (columns >= G carry q = 0 and are never
-// stored):
+// rescale between them.  The G heads are the 16 columns of
+// v_mfma_f32_16x16x32 (columns >= G carry q = 0 and are never stored):
 //   S^T[key][head] = K Q^T   A = K rows, B = Q^T (the q rows of the slice's
 //                            heads), both read from LDS
 //   O^T[d][head]  = V^T P^T  A = V^T via ds_read_b64_tr_b16 from LDS,
@@ -209,11 +211,15 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // 1 KB of contiguous HBM; K and V carry the streaming hint.  (K read straight
 // into MFMA operand registers would take each 128-byte line in two 64-byte
 // halves from separate instructions, which streams markedly slower.)  Wave w
-// scores keys 32w .. 32w + 31 and accumulates d rows w*D/4 .. +D/4 - 1 over all
-// 128 keys (at d = 32 waves 0 and 1 hold the two 16-row blocks).  The chunk
-// max and sum are exchanged through LDS; P is the fp32
-// 2^(x - m) split into two 16-bit parts, so the products keep fp32-level
-// accuracy in P while l is the sum of the unrounded values.
+// scores keys 32w .. 32w + 31 and accumulates d rows w*D/4 .. +D/4 - 1 over
+// all 128 keys (at d = 32 waves 0 and 1 hold the two 16-row blocks).  The
+// chunk max and sum are exchanged through LDS; P is the fp32 2^(x - m) split
+// into two 16-bit parts, so the products keep fp32-level accuracy in P while
+// l is the sum of the unrounded values.
+//   PAGED: K/V rows come from a paged cache (PagedKv); rows past a sequence's
+// end read as zeros and chunks past it store O_c = 0, lse_c = -inf.
+//   KV8: K/V are FP8 E4M3 codes; k_scale is folded into scale_log2 by the
+// host and v_scale multiplies the stored partial.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
