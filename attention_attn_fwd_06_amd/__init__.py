@@ -122,7 +122,8 @@ def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = No
 
 
 def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
-                              scale: float | None = None, o_part=None, lse_part=None, stream=None):
+                              scale: float | None = None, o_part=None, lse_part=None, stream=None,
+                              k_scale: float | None = None, v_scale: float | None = None):
     """Split-KV decode partials over a paged KV cache.
 
     q [B,Hq,d]; k_cache, v_cache: views [num_blocks, block_size, Hkv, d] with a
@@ -130,7 +131,8 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
     [num_blocks, Hkv, block_size, d] passed as ``.transpose(1, 2)``), both with
     the same strides; block_table [B, max_blocks] int32; seq_lens [B] int32.
     Returns (o_part [B,Hq,C,d], lse_part [B,Hq,C]) with
-    C = ceil(max_blocks * block_size / chunk_size).
+    C = ceil(max_blocks * block_size / chunk_size).  Caches of E4M3 codes
+    (torch.float8_e4m3fn or uint8) take k_scale and v_scale (FP8 KV).
     """
     _check(q, "q")
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"), (seq_lens, "seq_lens")):
@@ -158,6 +160,16 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
         lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
     pk = _lib.PagedKv(block_table.data_ptr(), seq_lens.data_ptr(), num_blocks, block_size, max_blocks,
                       k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    if k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if k_scale is None or v_scale is None:
+            raise ValueError("FP8 caches need k_scale and v_scale")
+        st = _lib.load().attn_decode_paged_fp8kv_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                         float(k_scale), float(v_scale), ctypes.byref(pk),
+                                                         o_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv, d,
+                                                         chunk_size, float(scale), _dtype_code(q), _stream(stream))
+        if st != 0:
+            raise AttnError(st, "attn_decode_paged_fp8kv_splitkv")
+        return o_part, lse_part
     st = _lib.load().attn_decode_paged_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                                ctypes.byref(pk), o_part.data_ptr(), lse_part.data_ptr(),
                                                B, Hq, Hkv, d, chunk_size, float(scale), _dtype_code(q),
@@ -202,10 +214,11 @@ def attn_decode_fp8kv(q, k, v, k_scale: float, v_scale: float, chunk_size: int =
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
-                      scale: float | None = None, stream=None):
+                      scale: float | None = None, stream=None, k_scale: float | None = None,
+                      v_scale: float | None = None):
     """Paged split-KV decode end to end (partials, then the merge)."""
     o_part, lse_part = attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size,
-                                                 scale, stream=stream)
+                                                 scale, stream=stream, k_scale=k_scale, v_scale=v_scale)
     o, lse = lse_merge(o_part, lse_part, q.dtype, stream=stream)
     return o, lse, o_part, lse_part
 

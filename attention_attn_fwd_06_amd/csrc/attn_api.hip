@@ -22,7 +22,8 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
                                  const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
                                  int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
                                  int64_t head_stride, float* o_part, float* lse_part, int B, int Hq, int Hkv,
-                                 int d, int chunk, bool bf16, float scale, hipStream_t stream);
+                                 int d, int chunk, bool bf16, float scale, bool fp8, float k_scale,
+                                 float v_scale, hipStream_t stream);
 hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
                                  float* o_part, float* lse_part, int B, int Hq, int Hkv, int M, int d, int chunk,
                                  bool bf16, float scale, hipStream_t stream);
@@ -160,9 +161,14 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
                                                    chunk_size, dtype == ATTN_BF16, scale, stream));
 }
 
-int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                              const attn_paged_kv_t* pages, float* o_part, float* lse_part, int B, int Hq,
-                              int Hkv, int d, int chunk_size, float scale, attn_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the 16-bit and FP8 paged entry points.
+int paged_decode(const void* q, const void* k_cache, const void* v_cache, const attn_paged_kv_t* pages,
+                 float* o_part, float* lse_part, int B, int Hq, int Hkv, int d, int chunk_size, float scale,
+                 attn_dtype_t dtype, bool fp8, float k_scale, float v_scale, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !pages || !o_part || !lse_part || !pages->block_table || !pages->seq_lens)
     return ATTN_ERR_NULL_POINTER;
   const attn_paged_kv_t& pk = *pages;
@@ -173,9 +179,14 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
-  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite(k_scale) || k_scale < 0.f || !std::isfinite(v_scale) ||
+      v_scale < 0.f)
+    return ATTN_ERR_SCALE;
+  // element strides; FP8 elements are bytes, so the 16-byte alignment of a row needs multiples of 16 there
+  const int64_t align = fp8 ? 16 : 8;
   if (pk.block_size % 16 != 0 || pk.page_stride < 0 || pk.token_stride < 0 || pk.head_stride < 0 ||
-      pk.page_stride % 8 || pk.token_stride % 8 || pk.head_stride % 8 || 15 * pk.token_stride + d >= kMaxElems)
+      pk.page_stride % align || pk.token_stride % align || pk.head_stride % align ||
+      15 * pk.token_stride + d >= kMaxElems)
     return ATTN_ERR_LAYOUT;
   const int64_t M = (int64_t)pk.max_blocks * pk.block_size;
   const int64_t C = (M + chunk_size - 1) / chunk_size;
@@ -188,7 +199,26 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
   return launch_status(attn::decode_paged_dispatch(q, k_cache, v_cache, pk.block_table, pk.seq_lens, pk.num_blocks,
                                                    pk.block_size, pk.max_blocks, pk.page_stride, pk.token_stride,
                                                    pk.head_stride, o_part, lse_part, B, Hq, Hkv, d, chunk_size,
-                                                   dtype == ATTN_BF16, scale, stream));
+                                                   dtype == ATTN_BF16, scale, fp8, k_scale, v_scale, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                              const attn_paged_kv_t* pages, float* o_part, float* lse_part, int B, int Hq,
+                              int Hkv, int d, int chunk_size, float scale, attn_dtype_t dtype, hipStream_t stream) {
+  return paged_decode(q, k_cache, v_cache, pages, o_part, lse_part, B, Hq, Hkv, d, chunk_size, scale, dtype, false,
+                      1.f, 1.f, stream);
+}
+
+int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                                    float v_scale, const attn_paged_kv_t* pages, float* o_part, float* lse_part,
+                                    int B, int Hq, int Hkv, int d, int chunk_size, float scale, attn_dtype_t dtype,
+                                    hipStream_t stream) {
+  return paged_decode(q, k_cache, v_cache, pages, o_part, lse_part, B, Hq, Hkv, d, chunk_size, scale, dtype, true,
+                      k_scale, v_scale, stream);
 }
 
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int Hq, int num_chunks,

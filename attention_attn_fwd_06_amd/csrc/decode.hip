@@ -219,7 +219,8 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 //   PAGED: K/V rows come from a paged cache (PagedKv); rows past a sequence's
 // end read as zeros and chunks past it store O_c = 0, lse_c = -inf.
 //   KV8: K/V are FP8 E4M3 codes; k_scale is folded into scale_log2 by the
-// host and v_scale multiplies the stored partial.
+// host and v_scale multiplies the stored partial.  With PAGED as well, each
+// lane looks up its own row's page.
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
@@ -241,7 +242,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
                             int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale) {
-  static_assert(!(PAGED && KV8), "paged FP8 KV is not built");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
   constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
@@ -320,14 +320,36 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   uint4 kr8[kPieces8], vr8[kPieces8];
   int kv8_item = -1, kv8_key0 = 0;
   auto load8 = [&](int bb, int kvhh, int kk) {
-    const int64_t base = ((int64_t)bb * Hkv + kvhh) * M * D;
+    if constexpr (PAGED) {
+      // each lane looks up its row's page (table index clamped to the table);
+      // rows past the sequence's end may read another page's bytes, which are
+      // masked (K) or zeroed on conversion (V); out-of-range page ids read nothing
+      int pgl[kPieces8];
 #pragma unroll
-    for (int p = 0; p < kPieces8; ++p) {
-      const int u = p * kDecThreads + tid, row = u / kPR8;
-      const bool ok = kk + row < M;
-      const int64_t off = base + (int64_t)(kk + row) * D + 16 * (u % kPR8);
-      kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
-      vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < kPieces8; ++p) {
+        const int key = kk + (p * kDecThreads + tid) / kPR8;
+        const int e = min(key / pk.block_size, pk.max_blocks - 1);
+        pgl[p] = pk.block_table[(int64_t)bb * pk.max_blocks + e];
+      }
+#pragma unroll
+      for (int p = 0; p < kPieces8; ++p) {
+        const int u = p * kDecThreads + tid, key = kk + u / kPR8;
+        const bool ok = pgl[p] >= 0 && pgl[p] < pk.num_blocks;
+        const int64_t off = (int64_t)pgl[p] * pk.page_stride + (int64_t)kvhh * pk.head_stride +
+                            (int64_t)(key % pk.block_size) * pk.token_stride + 16 * (u % kPR8);
+        kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
+        vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int64_t base = ((int64_t)bb * Hkv + kvhh) * M * D;
+#pragma unroll
+      for (int p = 0; p < kPieces8; ++p) {
+        const int u = p * kDecThreads + tid, row = u / kPR8;
+        const bool ok = kk + row < M;
+        const int64_t off = base + (int64_t)(kk + row) * D + 16 * (u % kPR8);
+        kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
+        vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -378,7 +400,53 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     for (int key0 = c * chunk; key0 < c_end; key0 += kChunk) {
       const int len = min(kChunk, c_end - key0);
       const bool last = key0 + kChunk >= c_end;
-      if constexpr (PAGED) {
+      if constexpr (KV8) {
+        // FP8 KV: 16-byte pieces of E4M3 rows (consecutive threads read
+        // consecutive pieces), converted exactly to 16 bits in registers and
+        // written to the same swizzled layout; rows past M read as zeros
+        if (kv8_item != item || kv8_key0 != key0) load8(b, kvh, key0);
+        auto put = [&](uint32_t base, const uint4& w, int row, int pc8) {
+          const uint32_t* b4 = reinterpret_cast<const uint32_t*>(&w);
+          uint32_t h[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], true);
+            h[2 * t] = pack2<BF16>(lo[0], lo[1]);
+            h[2 * t + 1] = pack2<BF16>(hi[0], hi[1]);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int lc = 2 * pc8 + half;
+            *(lds_u32x4*)(uintptr_t)(base + (uint32_t)(row * D * 2 + ((lc ^ swz<D>(row)) << 4))) =
+                (u32x4){h[4 * half], h[4 * half + 1], h[4 * half + 2], h[4 * half + 3]};
+          }
+        };
+#pragma unroll
+        for (int p = 0; p < kPieces8; ++p) {
+          const int u = p * kDecThreads + tid;
+          const bool past = PAGED && key0 + u / kPR8 >= seq;  // a row past the sequence's end
+          put(k_lds, kr8[p], u / kPR8, u % kPR8);
+          put(v_lds, past ? make_uint4(0, 0, 0, 0) : vr8[p], u / kPR8, u % kPR8);
+        }
+        // prefetch the next sub-chunk, or the next item's first one
+        kv8_item = -1;
+        if (key0 + kChunk < c_end) {
+          kv8_item = item;
+          kv8_key0 = key0 + kChunk;
+          load8(b, kvh, kv8_key0);
+        } else if (item + (int)gridDim.x < n_items) {
+          const int n = item + (int)gridDim.x;
+          const int bkv_n = n / C / slices;
+          kv8_item = n;
+          kv8_key0 = (n % C) * chunk;
+          load8(bkv_n / Hkv, bkv_n % Hkv, kv8_key0);
+          if constexpr (PAGED) {
+            nx_item = n;
+            nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bkv_n / Hkv]);
+          }
+        }
+      } else if constexpr (PAGED) {
         // this wave's rows of instruction i: rg .. rg + kWaveRows - 1, of which
         // nv exist; page ids outside [0, num_blocks) read as no rows
         if (nx_item != item || nx_key0 != key0) load_pages(b, key0, pg);
@@ -412,47 +480,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bn]);
             load_pages(bn, nx_key0, pg);
           }
-        }
-      } else if constexpr (KV8) {
-        // FP8 KV: 16-byte pieces of E4M3 rows (consecutive threads read
-        // consecutive pieces), converted exactly to 16 bits in registers and
-        // written to the same swizzled layout; rows past M read as zeros
-        if (kv8_item != item || kv8_key0 != key0) load8(b, kvh, key0);
-        auto put = [&](uint32_t base, const uint4& w, int row, int pc8) {
-          const uint32_t* b4 = reinterpret_cast<const uint32_t*>(&w);
-          uint32_t h[8];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], true);
-            h[2 * t] = pack2<BF16>(lo[0], lo[1]);
-            h[2 * t + 1] = pack2<BF16>(hi[0], hi[1]);
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int lc = 2 * pc8 + half;
-            *(lds_u32x4*)(uintptr_t)(base + (uint32_t)(row * D * 2 + ((lc ^ swz<D>(row)) << 4))) =
-                (u32x4){h[4 * half], h[4 * half + 1], h[4 * half + 2], h[4 * half + 3]};
-          }
-        };
-#pragma unroll
-        for (int p = 0; p < kPieces8; ++p) {
-          const int u = p * kDecThreads + tid;
-          put(k_lds, kr8[p], u / kPR8, u % kPR8);
-          put(v_lds, vr8[p], u / kPR8, u % kPR8);
-        }
-        // prefetch the next sub-chunk, or the next item's first one
-        kv8_item = -1;
-        if (key0 + kChunk < c_end) {
-          kv8_item = item;
-          kv8_key0 = key0 + kChunk;
-          load8(b, kvh, kv8_key0);
-        } else if (item + (int)gridDim.x < n_items) {
-          const int n = item + (int)gridDim.x;
-          const int bkv_n = n / C / slices;
-          kv8_item = n;
-          kv8_key0 = (n % C) * chunk;
-          load8(bkv_n / Hkv, bkv_n % Hkv, kv8_key0);
         }
       } else {
 #pragma unroll
@@ -726,25 +753,28 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
                                  const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
                                  int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
                                  int64_t head_stride, float* o_part, float* lse_part, int B, int Hq, int Hkv,
-                                 int d, int chunk, bool bf16, float scale, hipStream_t stream) {
+                                 int d, int chunk, bool bf16, float scale, bool fp8, float k_scale,
+                                 float v_scale, hipStream_t stream) {
   const int M = max_blocks * block_size;  // longest sequence the table can describe
   const int C = (M + chunk - 1) / chunk;
-  const float sl2 = scale * kLog2e;
+  const float sl2 = scale * (fp8 ? k_scale : 1.f) * kLog2e;  // FP8: the scores carry k_scale
   const int group = Hq / Hkv;
   int g = std::min(group, kGqaCols);
   while (group % g != 0) --g;
   const int n_items = B * (Hq / g) * C;
   const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
-#define ATTN_PAGED_CASE(DD, BB)                                                                        \
-  if (d == DD && bf16 == BB) {                                                                         \
-    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, false>>(kDecThreads)); \
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+#define ATTN_PAGED_CASE(DD, BB, F8)                                                                    \
+  if (d == DD && bf16 == BB && fp8 == F8) {                                                            \
+    const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, F8>>(kDecThreads)); \
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true, F8>), dim3(grid), dim3(kDecThreads), 0, stream,  \
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, o_part,     \
-                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, 1.f);                               \
+                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, F8 ? v_scale : 1.f);            \
     return hipGetLastError();                                                                          \
   }
-  ATTN_PAGED_CASE(32, false) ATTN_PAGED_CASE(32, true) ATTN_PAGED_CASE(64, false) ATTN_PAGED_CASE(64, true)
-  ATTN_PAGED_CASE(128, false) ATTN_PAGED_CASE(128, true)
+  ATTN_PAGED_CASE(32, false, false) ATTN_PAGED_CASE(32, true, false) ATTN_PAGED_CASE(64, false, false)
+  ATTN_PAGED_CASE(64, true, false) ATTN_PAGED_CASE(128, false, false) ATTN_PAGED_CASE(128, true, false)
+  ATTN_PAGED_CASE(32, false, true) ATTN_PAGED_CASE(32, true, true) ATTN_PAGED_CASE(64, false, true)
+  ATTN_PAGED_CASE(64, true, true) ATTN_PAGED_CASE(128, false, true) ATTN_PAGED_CASE(128, true, true)
 #undef ATTN_PAGED_CASE
   return hipErrorInvalidValue;
 }

@@ -12,8 +12,8 @@ duration, measured with HIP events on the launch stream; the decode result is
 reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).  The
 ``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8, M=16384,
 d=128, bf16; K/V counted once per kv head), timed separately after the steps, and
-``decode_paged`` / ``decode_fp8kv`` the same workload's chunk kernel through the
-paged-KV and FP8-KV entry points.
+``decode_paged`` / ``decode_fp8kv`` / ``decode_paged_fp8kv`` the same workload's
+chunk kernel through the paged-KV, FP8-KV and paged FP8-KV entry points.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--prewarm-s 1.5] [--no-cpu-baseline]
 """
@@ -200,6 +200,20 @@ def paged_and_fp8_rates(attn, w, args, dev):
                            "value": round(nbytes8 / (ms8 * 1e-3) / 1e9, 1), "unit": "GB/s",
                            "frac": round(nbytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "chunk_ms": round(ms8, 4),
                            "kernel": "decode_gqa_mfma_kernel<128,bf16,fp8kv>"}
+    del sets8
+    sets8p = []
+    for _ in range(2):
+        kc = torch.randint(0, 126, (nb, bs, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+        vc = torch.randint(0, 126, (nb, bs, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+        table = torch.randperm(nb, generator=g).to(torch.int32).reshape(w.B, w.M // bs).to(dev)
+        sets8p.append((kc, vc, table))
+    ms8p = _time_chunk(lambda i: attn.attn_decode_paged_splitkv(q, sets8p[i % 2][0], sets8p[i % 2][1], sets8p[i % 2][2],
+                                                                lens, w.chunk, w.scale, o_part=o_part,
+                                                                lse_part=lse_part, k_scale=0.01, v_scale=0.01), args)
+    out["decode_paged_fp8kv"] = {"workload": w.desc + ", paged FP8 KV: 16-key token-major pages, shuffled",
+                                 "value": round(nbytes8 / (ms8p * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                 "frac": round(nbytes8 / (ms8p * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                 "chunk_ms": round(ms8p, 4), "kernel": "decode_gqa_mfma_kernel<128,bf16,paged,fp8kv>"}
     return out
 
 

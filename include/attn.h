@@ -17,6 +17,7 @@
  *   attn_decode_fp8kv_splitkv  the same partials with K and V stored as FP8 E4M3
  *                        codes and per-tensor scales (fp8 KV quantisation, listed as
  *                        future work on the "fmha sm120" page).
+ *   attn_decode_paged_fp8kv_splitkv  both: a paged cache of FP8 codes.
  *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
  *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
  *                        section 2.2, step 2, and section 6 "reduce kernel").
@@ -186,6 +187,17 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
                               const attn_paged_kv_t* pages, float* o_part, float* lse_part,
                               int B, int Hq, int Hkv, int d, int chunk_size, float scale,
                               attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_paged_fp8kv_splitkv - attn_decode_paged_splitkv over a paged cache
+ * of FP8 E4M3 codes with per-tensor scales (as attn_decode_fp8kv_splitkv): key
+ * and value elements are one byte, so the element strides are byte strides and
+ * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv.
+ */
+int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                    float k_scale, float v_scale, const attn_paged_kv_t* pages,
+                                    float* o_part, float* lse_part, int B, int Hq, int Hkv, int d,
+                                    int chunk_size, float scale, attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * attn_decode_fp8kv_splitkv - attn_decode_splitkv with K and V stored as FP8.

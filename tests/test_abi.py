@@ -27,7 +27,8 @@ def status_codes():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
-         "attn_decode_paged_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge", "attn_status_string"])
+         "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
+         "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -188,6 +189,26 @@ def fp8(**kw):
 ])
 def test_fp8kv_decode_rejects(kw, code):
     assert fp8(**kw) == code
+
+
+def paged8(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=0.01, vs=0.02, op=FAKE, lp=FAKE, B=2, Hq=8, Hkv=2, d=128, chunk=128,
+             scale=0.088, dtype=1, stream=None, bt=FAKE, sl=FAKE, nb=64, bs=16, mb=32, ps=16 * 2 * 128, ts=2 * 128,
+             hs=128)
+    a.update(kw)
+    pk = _lib.PagedKv(a["bt"], a["sl"], a["nb"], a["bs"], a["mb"], a["ps"], a["ts"], a["hs"])
+    return _lib.load().attn_decode_paged_fp8kv_splitkv(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], ctypes.byref(pk),
+                                                       a["op"], a["lp"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                                       a["chunk"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), -1), (dict(bt=None), -1), (dict(mb=0), -2), (dict(d=80), -3), (dict(chunk=64), -7),
+    (dict(ks=-0.5), -11), (dict(vs=float("nan")), -11),
+    (dict(hs=8), -12), (dict(ts=24), -12), (dict(bs=8), -12), (dict(vc=FAKE + 8), -10),
+])
+def test_paged_fp8kv_decode_rejects(kw, code):
+    assert paged8(**kw) == code
 
 
 def mrg(**kw):

@@ -386,6 +386,46 @@ def test_decode_paged(case):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
+PAGED_FP8_CASES = [
+    (3, 8, 2, (1, 200, 1000), 128, "bf16", 16, 128, False),
+    (2, 4, 4, (777, 64), 64, "f16", 64, 256, True),
+    (2, 16, 1, (130, 16), 32, "bf16", 32, 128, True),
+    (2, 32, 8, (5000, 4097), 128, "f16", 256, 512, False),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_FP8_CASES, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_decode_paged_fp8kv(case):
+    """Paged cache of E4M3 codes; the unowned rows hold NaN codes."""
+    B, Hq, Hkv, lens, d, dt, bs, chunk, head_major = case
+    say(f"case paged fp8 kv decode {case}")
+    q, kc, vc, _, _, table, sl = paged_inputs(B, Hq, Hkv, list(lens), d, dt, bs, seed=sum(lens) + 1,
+                                              head_major=head_major)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(3.0 / 448.0))
+    # clamp to the E4M3 range (beyond it the conversion gives NaN codes); the
+    # unowned rows keep their NaN, which clamp passes through
+    kc8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    view = (lambda t: t.transpose(1, 2)) if head_major else (lambda t: t)
+    scale = float(np.float32(d ** -0.5))
+    kd, vd = kc8.to(DEV), vc8.to(DEV)
+    o, lse, op, lp = attn().attn_decode_paged(q.to(DEV), view(kd), view(vd), table.to(DEV), sl.to(DEV), chunk, scale,
+                                              k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kdeq = oracle.e4m3_decode(view(kc8).numpy()) * ks
+    vdeq = oracle.e4m3_decode(view(vc8).numpy()) * vs
+    Or, Lr, OPr, LPr = oracle.paged_decode_ref(q, kdeq, vdeq, table.clamp(min=0), sl, scale, chunk)
+    OPg, LPg = f64(op), f64(lp)
+    full = np.isfinite(LPr)
+    assert np.array_equal(np.isfinite(LPg), full), "empty chunks must be exactly the chunks past each end"
+    assert np.all(OPg[~full] == 0.0)
+    errs = dict(o=maxerr(f64(o), Or), lse=maxerr(f64(lse), Lr),
+                o_part=maxerr(OPg[full], OPr[full]), lse_part=maxerr(LPg[full], LPr[full]))
+    say(f"  {case}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
+    assert errs["o"] <= TOL_O[dt] and errs["o_part"] <= TOL_O[dt], errs
+    assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
+
+
 def test_decode_paged_matches_contiguous():
     """One sequence in pages in order decodes like the contiguous decode."""
     say("case paged vs contiguous decode")
