@@ -292,6 +292,9 @@ DEC_SHAPES = [
     # larger MHA launches, one with a tail chunk
     (2, 8, 8, 16461, 64, "f16"),
     (1, 16, 16, 16384, 128, "bf16"),
+    # groups split over several 16-column slices: 32 = 2 x 16, 24 = 2 x 12
+    (1, 32, 1, 300, 128, "bf16"),
+    (2, 24, 1, 200, 64, "f16"),
     # head dim 32: VALU (small MHA), matrix-core (GQA and large MHA)
     (1, 4, 4, 300, 32, "f16"),
     (2, 16, 4, 1000, 32, "bf16"),
