@@ -298,17 +298,18 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
   // paged: the page ids of the next sub-chunk (and, across items, the next
   // sequence length) are loaded right after the current fetches are issued,
-  // so their latency hides behind those fetches.  Table reads are clamped to
-  // the table; entries past a sequence's end are read but never used.
+  // so their latency hides behind those fetches.  Lane i of one VGPR holds
+  // fetch instruction i's page (read out with v_readlane where it is used):
+  // kept in SGPRs the ids spilled, and each spill waited for its load at once.
+  // Table reads are clamped to the table; entries past a sequence's end are
+  // read but never used.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // keeps page descriptors scalar
   int nx_item = -1, nx_key0 = 0, nx_seq = 0;
-  int pg[kFetch];  // page ids of the current sub-chunk, then the prefetched ones
-  auto load_pages = [&](int bb, int kk, int (&pg)[kFetch]) {
-#pragma unroll
-    for (int i = 0; i < kFetch; ++i) {
-      const int e = min((kk + kRowsPerInst * i + wave_u * kWaveRows) / pk.block_size, pk.max_blocks - 1);
-      pg[i] = __builtin_amdgcn_readfirstlane(pk.block_table[(int64_t)bb * pk.max_blocks + e]);
-    }
+  int pgv = 0;  // lane i < kFetch: page id of fetch instruction i (current, then prefetched)
+  auto load_pages = [&](int bb, int kk, int& pv) {
+    const int i = min(lane, kFetch - 1);
+    const int e = min((kk + kRowsPerInst * i + wave_u * kWaveRows) / pk.block_size, pk.max_blocks - 1);
+    pv = pk.block_table[(int64_t)bb * pk.max_blocks + e];
   };
 
   // FP8 KV: each thread's 16-byte pieces of a 128-key sub-chunk; after the
@@ -449,12 +450,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       } else if constexpr (PAGED) {
         // this wave's rows of instruction i: rg .. rg + kWaveRows - 1, of which
         // nv exist; page ids outside [0, num_blocks) read as no rows
-        if (nx_item != item || nx_key0 != key0) load_pages(b, key0, pg);
+        if (nx_item != item || nx_key0 != key0) load_pages(b, key0, pgv);
 #pragma unroll
         for (int i = 0; i < kFetch; ++i) {
           const int rg = key0 + kRowsPerInst * i + wave_u * kWaveRows;
           int nv = min(kWaveRows, seq - rg);
-          int page = pg[i];
+          int page = __builtin_amdgcn_readlane(pgv, i);
           if (page < 0 || page >= pk.num_blocks) nv = 0;
           if (nv <= 0) page = 0;
           const int64_t off = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
@@ -469,7 +470,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           nx_item = item;
           nx_key0 = key0 + kChunk;
           nx_seq = seq;
-          load_pages(b, nx_key0, pg);
+          load_pages(b, nx_key0, pgv);
         } else {
           const int n = item + (int)gridDim.x;
           nx_item = -1;
@@ -478,7 +479,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             nx_item = n;
             nx_key0 = (n % C) * chunk;
             nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bn]);
-            load_pages(bn, nx_key0, pg);
+            load_pages(bn, nx_key0, pgv);
           }
         }
       } else {
