@@ -305,6 +305,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // read but never used.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // keeps page descriptors scalar
   int nx_item = -1, nx_key0 = 0, nx_seq = 0;
+  // a sequence's length through the scalar cache (the lengths are read-only
+  // here): a scalar load is waited for on its own counter, not behind the
+  // vector loads and fetches in flight
+  auto seq_len = [&](int bb) {
+    return ((const __attribute__((address_space(4))) int*)pk.seq_lens)[bb];
+  };
   int pgv = 0;  // lane i < kFetch: page id of fetch instruction i (current, then prefetched)
   auto load_pages = [&](int bb, int kk, int& pv) {
     const int i = min(lane, kFetch - 1);
@@ -312,46 +318,76 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     pv = pk.block_table[(int64_t)bb * pk.max_blocks + e];
   };
 
-  // FP8 KV: each thread's 16-byte pieces of a 128-key sub-chunk; after the
+  // FP8 KV: each thread's 16-byte pieces of a 128-key sub-chunk.  After the
   // current pieces are converted, the next sub-chunk's (or next item's first)
   // are loaded into the same registers, so that load overlaps this sub-chunk's
-  // products.  kv8_item / kv8_key0 name what the registers hold (-1: nothing).
+  // products.  kv8_item / kv8_key0 name what the registers hold (-1: nothing);
+  // bit p of kv8_ok says piece p is a row that exists (otherwise it was read
+  // from a safe address and is converted as zeros).
   constexpr int kPR8 = D / 16;                       // 16-byte pieces per FP8 row
   constexpr int kPieces8 = kChunk * kPR8 / kDecThreads;
   uint4 kr8[kPieces8], vr8[kPieces8];
   int kv8_item = -1, kv8_key0 = 0;
-  auto load8 = [&](int bb, int kvhh, int kk) {
-    if constexpr (PAGED) {
-      // each lane looks up its row's page (table index clamped to the table);
-      // rows past the sequence's end may read another page's bytes, which are
-      // masked (K) or zeroed on conversion (V); out-of-range page ids read nothing
-      int pgl[kPieces8];
+  uint32_t kv8_ok = 0;
+  // paged FP8: each lane's page id per piece for the fetch after the one in
+  // flight (pg_item / pg_key0 name it, -1: none), looked up right after that
+  // fetch is issued, so the table's latency overlaps the same products.  The
+  // guess ignores the sequence's length; when it turns out wrong the ids are
+  // looked up again.  Table reads are clamped to the table.
+  int pg8[kPieces8];
+  int pg_item = -1, pg_key0 = 0;
+  auto lookup8 = [&](int bb, int kk) {
 #pragma unroll
-      for (int p = 0; p < kPieces8; ++p) {
-        const int key = kk + (p * kDecThreads + tid) / kPR8;
-        const int e = min(key / pk.block_size, pk.max_blocks - 1);
-        pgl[p] = pk.block_table[(int64_t)bb * pk.max_blocks + e];
-      }
+    for (int p = 0; p < kPieces8; ++p) {
+      const int key = kk + (p * kDecThreads + tid) / kPR8;
+      const int e = min(key / pk.block_size, pk.max_blocks - 1);
+      pg8[p] = pk.block_table[(int64_t)bb * pk.max_blocks + e];
+    }
+  };
+  auto fetch8 = [&](int bb, int kvhh, int kk) {
+    const uint8_t* k8 = reinterpret_cast<const uint8_t*>(k);
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(v);
+    kv8_ok = 0;
+    if constexpr (PAGED) {
+      // a row past the sequence's end may read another page's bytes; put()
+      // zeroes it.  An out-of-range page id reads offset 0 (page 0 exists).
 #pragma unroll
       for (int p = 0; p < kPieces8; ++p) {
         const int u = p * kDecThreads + tid, key = kk + u / kPR8;
-        const bool ok = pgl[p] >= 0 && pgl[p] < pk.num_blocks;
-        const int64_t off = (int64_t)pgl[p] * pk.page_stride + (int64_t)kvhh * pk.head_stride +
-                            (int64_t)(key % pk.block_size) * pk.token_stride + 16 * (u % kPR8);
-        kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
-        vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
+        const bool ok = pg8[p] >= 0 && pg8[p] < pk.num_blocks;
+        const int64_t off = ok ? (int64_t)pg8[p] * pk.page_stride + (int64_t)kvhh * pk.head_stride +
+                                     (int64_t)(key % pk.block_size) * pk.token_stride + 16 * (u % kPR8)
+                               : 0;
+        kv8_ok |= (uint32_t)ok << p;
+        kr8[p] = load_stream8(k8 + off);
+        vr8[p] = load_stream8(v8 + off);
       }
     } else {
+      // rows past M read the slice's first row (M >= 1); put() zeroes them
       const int64_t base = ((int64_t)bb * Hkv + kvhh) * M * D;
 #pragma unroll
       for (int p = 0; p < kPieces8; ++p) {
         const int u = p * kDecThreads + tid, row = u / kPR8;
         const bool ok = kk + row < M;
-        const int64_t off = base + (int64_t)(kk + row) * D + 16 * (u % kPR8);
-        kr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(k) + off) : make_uint4(0, 0, 0, 0);
-        vr8[p] = ok ? load_stream8(reinterpret_cast<const uint8_t*>(v) + off) : make_uint4(0, 0, 0, 0);
+        const int64_t off = base + (ok ? (int64_t)(kk + row) * D + 16 * (u % kPR8) : 0);
+        kv8_ok |= (uint32_t)ok << p;
+        kr8[p] = load_stream8(k8 + off);
+        vr8[p] = load_stream8(v8 + off);
       }
     }
+  };
+
+  // FP8 KV: Q comes through registers as well, loaded together with the
+  // prefetch of its item's first sub-chunk, so its latency is hidden too.
+  // Thread tid holds LDS unit tid of the Q block (the layout of the Q fetch
+  // below): row tid / kU, logical chunk (tid % kU) ^ swz(row); rows >= G are 0.
+  uint4 q8 = make_uint4(0, 0, 0, 0);
+  int q8_item = -1;
+  auto loadq8 = [&](int bb, int hh0) {
+    const int rq = tid / kU, lc = (tid % kU) ^ swz<D>(rq);
+    q8 = make_uint4(0, 0, 0, 0);
+    if (tid < kGqaCols * kU && rq < G)
+      q8 = *reinterpret_cast<const uint4*>(q + ((int64_t)bb * Hq + hh0 + rq) * D + 8 * lc);
   };
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -362,7 +398,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int h0 = kvh * group + hs * G;  // first query head of this item
     int seq = M;  // keys of this sequence
     if constexpr (PAGED) {
-      seq = nx_item == item ? nx_seq : __builtin_amdgcn_readfirstlane(pk.seq_lens[b]);
+      seq = nx_item == item ? nx_seq : seq_len(b);
       seq = min(max(seq, 0), pk.max_blocks * pk.block_size);
       if (c * chunk >= seq) {
         // chunk past the sequence's end: O_c = 0, lse_c = -inf (no weight in the merge)
@@ -390,7 +426,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const i32x4 qdesc = make_desc(q + ((int64_t)b * Hq + h0) * D, D, G, D);
     const i32x4 kdesc = make_desc(k + slice, D, M, D);
     const i32x4 vdesc = make_desc(v + slice, D, M, D);
-    if (wave < kQInst) dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
+    if constexpr (KV8) {
+      if (q8_item != item) loadq8(b, h0);
+      if (tid < kGqaCols * kU) *(lds_u32x4*)(uintptr_t)(q_lds + (uint32_t)tid * 16u) = (u32x4){q8.x, q8.y, q8.z, q8.w};
+    } else if (wave < kQInst) {
+      dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
+    }
 
     // running state of head j across the sub-chunks: the reference max (log2
     // units, shared by all waves), this wave's sum and its O^T rows
@@ -405,7 +446,29 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         // FP8 KV: 16-byte pieces of E4M3 rows (consecutive threads read
         // consecutive pieces), converted exactly to 16 bits in registers and
         // written to the same swizzled layout; rows past M read as zeros
-        if (kv8_item != item || kv8_key0 != key0) load8(b, kvh, key0);
+        if (kv8_item != item || kv8_key0 != key0) {  // nothing in flight for this sub-chunk
+          if constexpr (PAGED) lookup8(b, key0);
+          fetch8(b, kvh, key0);
+        }
+        const uint32_t ok8 = kv8_ok;
+        // the next fetch: this item's next sub-chunk, or the next item's first
+        int nt_item = -1, nt_key0 = 0, nt_b = b, nt_kvh = kvh;
+        if (key0 + kChunk < c_end) {
+          nt_item = item;
+          nt_key0 = key0 + kChunk;
+        } else if (item + (int)gridDim.x < n_items) {
+          nt_item = item + (int)gridDim.x;
+          const int bkv_n = nt_item / C / slices;
+          nt_key0 = (nt_item % C) * chunk;
+          nt_b = bkv_n / Hkv;
+          nt_kvh = bkv_n % Hkv;
+        }
+        if constexpr (PAGED) {
+          if (nt_item >= 0 && nt_item != item) {
+            nx_item = nt_item;
+            nx_seq = seq_len(nt_b);
+          }
+        }
         auto put = [&](uint32_t base, const uint4& w, int row, int pc8) {
           const uint32_t* b4 = reinterpret_cast<const uint32_t*>(&w);
           uint32_t h[8];
@@ -423,28 +486,39 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 (u32x4){h[4 * half], h[4 * half + 1], h[4 * half + 2], h[4 * half + 3]};
           }
         };
+        const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int p = 0; p < kPieces8; ++p) {
           const int u = p * kDecThreads + tid;
-          const bool past = PAGED && key0 + u / kPR8 >= seq;  // a row past the sequence's end
-          put(k_lds, kr8[p], u / kPR8, u % kPR8);
-          put(v_lds, past ? make_uint4(0, 0, 0, 0) : vr8[p], u / kPR8, u % kPR8);
+          // a row that does not exist, or lies past the sequence's end
+          const bool bad = !((ok8 >> p) & 1u) || (PAGED && key0 + u / kPR8 >= seq);
+          put(k_lds, bad ? zero4 : kr8[p], u / kPR8, u % kPR8);
+          put(v_lds, bad ? zero4 : vr8[p], u / kPR8, u % kPR8);
         }
         // prefetch the next sub-chunk, or the next item's first one
-        kv8_item = -1;
-        if (key0 + kChunk < c_end) {
-          kv8_item = item;
-          kv8_key0 = key0 + kChunk;
-          load8(b, kvh, kv8_key0);
-        } else if (item + (int)gridDim.x < n_items) {
-          const int n = item + (int)gridDim.x;
-          const int bkv_n = n / C / slices;
-          kv8_item = n;
-          kv8_key0 = (n % C) * chunk;
-          load8(bkv_n / Hkv, bkv_n % Hkv, kv8_key0);
+        kv8_item = nt_item;
+        kv8_key0 = nt_key0;
+        if (nt_item >= 0) {
           if constexpr (PAGED) {
-            nx_item = n;
-            nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bkv_n / Hkv]);
+            if (pg_item != nt_item || pg_key0 != nt_key0) lookup8(nt_b, nt_key0);
+          }
+          if (nt_item != item) {
+            q8_item = nt_item;
+            loadq8(nt_b, nt_kvh * group + (nt_item / C) % slices * G);
+          }
+          fetch8(nt_b, nt_kvh, nt_key0);
+          if constexpr (PAGED) {
+            // guess the fetch after it and look up its pages now
+            pg_item = -1;
+            if (nt_key0 + kChunk < (nt_item % C + 1) * chunk) {
+              pg_item = nt_item;
+              pg_key0 = nt_key0 + kChunk;
+              lookup8(nt_b, pg_key0);
+            } else if (nt_item + (int)gridDim.x < n_items) {
+              pg_item = nt_item + (int)gridDim.x;
+              pg_key0 = (pg_item % C) * chunk;
+              lookup8(pg_item / C / slices / Hkv, pg_key0);
+            }
           }
         }
       } else if constexpr (PAGED) {
@@ -478,7 +552,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             const int bn = n / C / slices / Hkv;
             nx_item = n;
             nx_key0 = (n % C) * chunk;
-            nx_seq = __builtin_amdgcn_readfirstlane(pk.seq_lens[bn]);
+            nx_seq = seq_len(bn);
             load_pages(bn, nx_key0, pgv);
           }
         }
@@ -494,8 +568,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       }
       // paged: K and V of one instruction are issued together (each descriptor
       // lives briefly, and this measured faster than K first), so wait for both
-      if constexpr (PAGED) wait_tile_loads();
-      else if constexpr (KV8) wait_vm<2 * kPieces8>();  // Q landed; only the prefetch may be in flight
+      if constexpr (KV8) {
+        // nothing is fetched straight to LDS: the threads wrote Q, K and V
+      } else if constexpr (PAGED) wait_tile_loads();
       else wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
       __syncthreads();    // Q and K visible
 
