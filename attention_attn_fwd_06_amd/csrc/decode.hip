@@ -427,8 +427,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const i32x4 kdesc = make_desc(k + slice, D, M, D);
     const i32x4 vdesc = make_desc(v + slice, D, M, D);
     if constexpr (KV8) {
-      if (q8_item != item) loadq8(b, h0);
-      if (tid < kGqaCols * kU) *(lds_u32x4*)(uintptr_t)(q_lds + (uint32_t)tid * 16u) = (u32x4){q8.x, q8.y, q8.z, q8.w};
+      if (q8_item != item) loadq8(b, h0);  // written to LDS after the first sub-chunk's conversion
     } else if (wave < kQInst) {
       dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
     }
@@ -495,6 +494,8 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           put(k_lds, bad ? zero4 : kr8[p], u / kPR8, u % kPR8);
           put(v_lds, bad ? zero4 : vr8[p], u / kPR8, u % kPR8);
         }
+        if (key0 == c * chunk && tid < kGqaCols * kU)  // Q, before q8 is reloaded below
+          *(lds_u32x4*)(uintptr_t)(q_lds + (uint32_t)tid * 16u) = (u32x4){q8.x, q8.y, q8.z, q8.w};
         // prefetch the next sub-chunk, or the next item's first one
         kv8_item = nt_item;
         kv8_key0 = nt_key0;
