@@ -192,7 +192,10 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
  * attn_decode_paged_fp8kv_splitkv - attn_decode_paged_splitkv over a paged cache
  * of FP8 E4M3 codes with per-tensor scales (as attn_decode_fp8kv_splitkv): key
  * and value elements are one byte, so the element strides are byte strides and
- * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv.
+ * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv, except that
+ * in place of a row that does not exist (an out-of-range page id) the kernel
+ * reads 16 bytes at the start of the cache (page 0, which num_blocks >= 1
+ * guarantees) and discards them, so such rows still contribute no keys.
  */
 int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const void* v_cache,
                                     float k_scale, float v_scale, const attn_paged_kv_t* pages,
