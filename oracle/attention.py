@@ -158,11 +158,16 @@ def lse_merge_ref(o_part, lse_part):
     o_part [..., C, d], lse_part [..., C] -> O [..., d], lse [...]:
     g = max_c lse_c + ln sum_c exp(lse_c - max_c lse_c),
     w_c = exp(lse_c - g), O = sum_c w_c O_c, lse = g.
+    A row whose chunks are all empty (every lse_c = -inf: no key at all) has
+    no weight to spread: O = 0, lse = -inf, as for a row with no allowed key.
     """
     o_part, lse_part = _f64(o_part), _f64(lse_part)
     mx = np.max(lse_part, axis=-1, keepdims=True)
-    g = mx + np.log(np.sum(np.exp(lse_part - mx), axis=-1, keepdims=True))
-    w = np.exp(lse_part - g)                                  # [..., C]
+    empty = ~np.isfinite(mx)
+    mx_safe = np.where(empty, 0.0, mx)
+    with np.errstate(divide="ignore"):
+        g = np.where(empty, -np.inf, mx_safe + np.log(np.sum(np.exp(lse_part - mx_safe), axis=-1, keepdims=True)))
+    w = np.where(empty, 0.0, np.exp(lse_part - np.where(empty, 0.0, g)))    # [..., C]
     O = np.sum(w[..., None] * o_part, axis=-2)
     return O, g[..., 0]
 

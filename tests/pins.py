@@ -288,6 +288,13 @@ def check_merge_identities(ora):
     Om, Lm = ora.lse_merge_ref(o2[None], np.array([[0.3, 0.3]]))
     _close(Om[0], o2.mean(0), what="equal-weight merge")
     _close(Lm[0], 0.3 + math.log(2.0), what="equal-weight merge lse")
+    # a row with no key at all (every chunk empty): the empty sum, O = 0 and
+    # lse = -inf; a non-empty row next to it is unaffected
+    Oe, Le = ora.lse_merge_ref(np.stack([o2, o2]), np.array([[-np.inf, -np.inf], [0.3, -np.inf]]))
+    _close(Oe[0], np.zeros(4), tol=0.0, what="empty-row merge output")
+    assert Le[0] == -np.inf, f"empty-row merge lse {Le[0]}"
+    _close(Oe[1], o2[0], what="merge with one empty chunk")
+    _close(Le[1], 0.3, what="merge with one empty chunk lse")
 
 
 def check_two_keys_closed_form(ora):
@@ -344,6 +351,11 @@ def check_paged_decode_variable_lengths(ora):
     lens = np.array([1, 17, 40])
     O, L, op, lp = ora.paged_decode_ref(q, kc, vc, bt, lens, 0.7, 16)
     assert op.shape[2] == 3
+    # an empty sequence has no key: O = 0, lse = -inf (the empty sum)
+    Oz, Lz, opz, lpz = ora.paged_decode_ref(q, kc, vc, bt, np.array([0, 17, 40]), 0.7, 16)
+    _close(Oz[0], np.zeros((Hq, d)), tol=0.0, what="empty sequence output")
+    assert np.all(Lz[0] == -np.inf) and np.all(lpz[0] == -np.inf), "empty sequence lse"
+    _close(Oz[1:], O[1:], what="other sequences next to an empty one")
     for b, n in enumerate(lens):
         Or, Lr, opr, lpr = ora.decode_ref(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.7, 16)
         _close(O[b], Or[0], what=f"seq {b} output")
