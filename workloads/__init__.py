@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "prefill_inputs", "decode_inputs",
-    "make_inputs", "attn_flops", "decode_bytes", "torch_dtype",
+    "make_inputs", "attn_flops", "decode_bytes", "torch_dtype", "prefill_ramp_inputs",
 ]
 
 
@@ -102,6 +102,30 @@ def prefill_inputs(B, Hq, Hkv, N, M, d, dtype="f16", seed=0):
 def decode_inputs(B, Hq, Hkv, M, d, dtype="f16", seed=0):
     """q [B,Hq,d], k [B,Hkv,M,d], v [B,Hkv,M,d] on the CPU, rounded to ``dtype``."""
     return tuple(_draw([(B, Hq, d), (B, Hkv, M, d), (B, Hkv, M, d)], dtype, seed))
+
+
+def prefill_ramp_inputs(B, Hq, Hkv, N, M, d, dtype="f16", seed=0, a=4.0, slope=6.0, v_scale=0.25):
+    """Prefill inputs whose scores grow with the key index, so that a row's
+    maximum keeps rising from one block of keys to the next.
+
+    With u = (1, ..., 1) / sqrt(d) (a unit vector) and i.i.d. N(0, 1) draws
+    g_q, g_k, g_v (drawn in that order from the seeded generator):
+        q[b, i, h]  = g_q + a * u
+        k[b, j, kh] = g_k + slope * (j / 64) * u
+        v           = v_scale * g_v
+    so q.k_j carries a term a * slope * j / 64 that rises by a * slope per 64
+    keys; v is scaled down so that |O| stays well below 2.  Rounded to
+    ``dtype`` like the other inputs."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    gq = torch.randn((B, N, Hq, d), dtype=torch.float32, generator=g)
+    gk = torch.randn((B, M, Hkv, d), dtype=torch.float32, generator=g)
+    gv = torch.randn((B, M, Hkv, d), dtype=torch.float32, generator=g)
+    u = torch.full((d,), 1.0 / math.sqrt(d))
+    ramp = (slope * torch.arange(M, dtype=torch.float32) / 64.0)[None, :, None, None]
+    q = gq + a * u
+    k = gk + ramp * u
+    v = v_scale * gv
+    return tuple(x.to(torch_dtype(dtype)) for x in (q, k, v))
 
 
 def make_inputs(w: Workload, seed: int = 0):
