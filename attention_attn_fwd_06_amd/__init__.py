@@ -45,11 +45,56 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-def _check(t: torch.Tensor, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+# Argument checks.  The C ABI receives bare pointers and sizes and cannot see a
+# tensor's real extent, so every tensor is checked here against the shape,
+# dtype and layout that the sizes passed to the library imply; a mismatch
+# raises ValueError (TypeError for an unsupported dtype) before anything is
+# launched.  Shapes and dtypes are checked first, the device last.
+
+def _shape(t: torch.Tensor, name: str, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype(t: torch.Tensor, name: str, dtype):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _contig(t: torch.Tensor, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _rows_contig(t: torch.Tensor, name: str, dim: int):
+    if t.dim() != dim or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be {dim}-D with a contiguous last dimension")
+
+
+def _devices(*named):
+    """All given tensors (None entries skipped) on one GPU."""
+    dev = None
+    for t, name in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _check_f32(t, name, shape):
+    _shape(t, name, shape)
+    _dtype(t, name, torch.float32)
+    _contig(t, name)
+
+
+def _num_chunks(M: int, chunk_size: int) -> int:
+    if int(chunk_size) <= 0:
+        raise ValueError(f"chunk_size must be positive, got {chunk_size}")
+    return -(-M // int(chunk_size))
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None,
@@ -60,26 +105,31 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, 
     projection, or head-major tensors transposed to [B,N,H,d]) as long as the
     last dimension is contiguous; they then go through attn_fwd_strided."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        if not t.is_cuda:
-            raise ValueError(f"{n} must be a GPU tensor")
-        if t.dim() != 4 or t.stride(-1) != 1:
-            raise ValueError(f"{n} must be 4-D with a contiguous last dimension")
+        _rows_contig(t, n, 4)
+    dt = _dtype_code(q)
+    _dtype(k, "k", q.dtype)
+    _dtype(v, "v", q.dtype)
     B, N, Hq, d = q.shape
     M, Hkv = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, M, Hkv, d))
+    _shape(v, "v", k.shape)
+    if o is not None:
+        _rows_contig(o, "o", 4)
+        _shape(o, "o", q.shape)
+        _dtype(o, "o", q.dtype)
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq, N))
+    _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"))
     if scale is None:
         scale = d ** -0.5
     if o is None:
         o = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device)
-    elif not o.is_cuda or o.dim() != 4 or o.stride(-1) != 1:
-        raise ValueError("o must be a 4-D GPU tensor with a contiguous last dimension")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse")
     lib = _lib.load()
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None,
-            B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale), _dtype_code(q))
+            B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale), dt)
     if all(t.is_contiguous() for t in (q, k, v, o)):
         st = lib.attn_fwd(*args, _stream(stream))
         name = "attn_fwd"
@@ -99,26 +149,54 @@ def attn_decode_workspace_bytes(B: int, Hq: int, M: int, d: int, chunk_size: int
     return int(_lib.load().attn_decode_workspace_bytes(B, Hq, M, d, chunk_size))
 
 
-def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = None,
-                        o_part=None, lse_part=None, stream=None):
-    """q [B,Hq,d], k/v [B,Hkv,M,d] -> (o_part [B,Hq,C,d] fp32, lse_part [B,Hq,C] fp32)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n)
+def _decode_partials(q, o_part, lse_part, C):
+    """Checks (or allocates) the fp32 partials of a split-KV decode of q."""
     B, Hq, d = q.shape
-    Hkv, M = k.shape[1], k.shape[2]
-    C = -(-M // chunk_size)
-    if scale is None:
-        scale = d ** -0.5
+    if o_part is not None:
+        _check_f32(o_part, "o_part", (B, Hq, C, d))
+    if lse_part is not None:
+        _check_f32(lse_part, "lse_part", (B, Hq, C))
+    return o_part, lse_part
+
+
+def _alloc_partials(q, o_part, lse_part, C):
+    B, Hq, d = q.shape
     if o_part is None:
         o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    return o_part, lse_part
+
+
+def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = None,
+                        o_part=None, lse_part=None, stream=None):
+    """q [B,Hq,d], k/v [B,Hkv,M,d] -> (o_part [B,Hq,C,d] fp32, lse_part [B,Hq,C] fp32)."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, M, d]")
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, Hkv, M, d))
+    _shape(v, "v", k.shape)
+    _dtype(k, "k", q.dtype)
+    _dtype(v, "v", q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, n)
+    C = _num_chunks(M, chunk_size)
+    _decode_partials(q, o_part, lse_part, C)
+    _devices((q, "q"), (k, "k"), (v, "v"), (o_part, "o_part"), (lse_part, "lse_part"))
+    if scale is None:
+        scale = d ** -0.5
+    o_part, lse_part = _alloc_partials(q, o_part, lse_part, C)
     st = _lib.load().attn_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
                                          lse_part.data_ptr(), B, Hq, Hkv, M, d, chunk_size,
-                                         float(scale), _dtype_code(q), _stream(stream))
+                                         float(scale), dt, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_splitkv")
     return o_part, lse_part
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
@@ -134,46 +212,53 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
     C = ceil(max_blocks * block_size / chunk_size).  Caches of E4M3 codes
     (torch.float8_e4m3fn or uint8) take k_scale and v_scale (FP8 KV).
     """
-    _check(q, "q")
-    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"), (seq_lens, "seq_lens")):
-        if not t.is_cuda:
-            raise ValueError(f"{n} must be a GPU tensor")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
+    dt = _dtype_code(q)
+    _contig(q, "q")
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
-        if t.dim() != 4 or t.stride(-1) != 1:
-            raise ValueError(f"{n} must be a 4-D view with a contiguous last dimension")
+        _rows_contig(t, n, 4)
     if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must have the same shape and strides")
+    fp8 = k_cache.dtype in _FP8
+    if fp8:
+        if v_cache.dtype not in _FP8:
+            raise ValueError("k_cache holds E4M3 codes, so v_cache must too")
+        if k_scale is None or v_scale is None:
+            raise ValueError("FP8 caches need k_scale and v_scale")
+    else:
+        _dtype(k_cache, "k_cache", q.dtype)
+        _dtype(v_cache, "v_cache", q.dtype)
     for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens")):
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous int32 tensor")
     B, Hq, d = q.shape
     num_blocks, block_size, Hkv, dk = k_cache.shape
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks]")
     max_blocks = block_table.shape[1]
     if dk != d or tuple(block_table.shape) != (B, max_blocks) or tuple(seq_lens.shape) != (B,):
         raise ValueError("shape mismatch between q, the caches, block_table and seq_lens")
-    C = -(-(max_blocks * block_size) // chunk_size)
+    C = _num_chunks(max_blocks * block_size, chunk_size)
+    _decode_partials(q, o_part, lse_part, C)
+    _devices((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+             (seq_lens, "seq_lens"), (o_part, "o_part"), (lse_part, "lse_part"))
     if scale is None:
         scale = d ** -0.5
-    if o_part is None:
-        o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    o_part, lse_part = _alloc_partials(q, o_part, lse_part, C)
     pk = _lib.PagedKv(block_table.data_ptr(), seq_lens.data_ptr(), num_blocks, block_size, max_blocks,
                       k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
-    if k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
-        if k_scale is None or v_scale is None:
-            raise ValueError("FP8 caches need k_scale and v_scale")
+    if fp8:
         st = _lib.load().attn_decode_paged_fp8kv_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                                          float(k_scale), float(v_scale), ctypes.byref(pk),
                                                          o_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv, d,
-                                                         chunk_size, float(scale), _dtype_code(q), _stream(stream))
+                                                         chunk_size, float(scale), dt, _stream(stream))
         if st != 0:
             raise AttnError(st, "attn_decode_paged_fp8kv_splitkv")
         return o_part, lse_part
     st = _lib.load().attn_decode_paged_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                                ctypes.byref(pk), o_part.data_ptr(), lse_part.data_ptr(),
-                                               B, Hq, Hkv, d, chunk_size, float(scale), _dtype_code(q),
-                                               _stream(stream))
+                                               B, Hq, Hkv, d, chunk_size, float(scale), dt, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged_splitkv")
     return o_part, lse_part
@@ -183,23 +268,27 @@ def attn_decode_fp8kv_splitkv(q, k, v, k_scale: float, v_scale: float, chunk_siz
                               scale: float | None = None, o_part=None, lse_part=None, stream=None):
     """q [B,Hq,d] fp16/bf16; k, v [B,Hkv,M,d] E4M3 codes (torch.float8_e4m3fn or uint8);
     K = k_scale * e4m3(k), V = v_scale * e4m3(v).  Returns (o_part, lse_part)."""
-    _check(q, "q")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, M, d]")
+    dt = _dtype_code(q)
     for t, n in ((k, "k"), (v, "v")):
-        _check(t, n)
-        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        if t.dtype not in _FP8:
             raise TypeError(f"{n} must hold E4M3 codes (torch.float8_e4m3fn or uint8)")
     B, Hq, d = q.shape
     Hkv, M = k.shape[1], k.shape[2]
-    C = -(-M // chunk_size)
+    _shape(k, "k", (B, Hkv, M, d))
+    _shape(v, "v", k.shape)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, n)
+    C = _num_chunks(M, chunk_size)
+    _decode_partials(q, o_part, lse_part, C)
+    _devices((q, "q"), (k, "k"), (v, "v"), (o_part, "o_part"), (lse_part, "lse_part"))
     if scale is None:
         scale = d ** -0.5
-    if o_part is None:
-        o_part = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    o_part, lse_part = _alloc_partials(q, o_part, lse_part, C)
     st = _lib.load().attn_decode_fp8kv_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(k_scale),
                                                float(v_scale), o_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv,
-                                               M, d, chunk_size, float(scale), _dtype_code(q), _stream(stream))
+                                               M, d, chunk_size, float(scale), dt, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_fp8kv_splitkv")
     return o_part, lse_part
@@ -226,9 +315,21 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, chunk_size: in
 def lse_merge(o_part, lse_part, out_dtype=torch.float16, o=None, lse=None, return_lse: bool = True,
               stream=None):
     """o_part [B,Hq,C,d], lse_part [B,Hq,C] -> (o [B,Hq,d] out_dtype, lse [B,Hq] fp32 or None)."""
-    _check(o_part, "o_part")
-    _check(lse_part, "lse_part")
+    if o_part.dim() != 4:
+        raise ValueError("o_part must be [B, Hq, C, d]")
     B, Hq, C, d = o_part.shape
+    _check_f32(o_part, "o_part", (B, Hq, C, d))
+    _check_f32(lse_part, "lse_part", (B, Hq, C))
+    if o is not None:
+        _dtype_code(o)
+        _shape(o, "o", (B, Hq, d))
+        _contig(o, "o")
+    else:
+        if out_dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {out_dtype}; expected float16 or bfloat16")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq))
+    _devices((o_part, "o_part"), (lse_part, "lse_part"), (o, "o"), (lse, "lse"))
     if o is None:
         o = torch.empty((B, Hq, d), dtype=out_dtype, device=o_part.device)
     if lse is None and return_lse:

@@ -41,6 +41,16 @@ bool valid_dtype(int dt) { return dt == ATTN_F16 || dt == ATTN_BF16; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// Index ranges of the split-KV decode: a (batch, kv head) slice of K or V is
+// read through 32-bit offsets (up to one 128-key sub-chunk past M); the
+// partials and q are addressed with 64-bit offsets; the chunk items
+// (B * Hq * C at most) are counted in 32-bit integers; the merge grid has
+// B * Hq workgroups in one dimension.
+bool decode_too_large(int B, int Hq, int64_t M, int d, int chunk_size) {
+  const int64_t C = (M + chunk_size - 1) / chunk_size;
+  return (int64_t)B * Hq * C >= kMaxElems || (int64_t)B * Hq > 65535 || (M + kDecodeChunk) * d >= kMaxElems;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,14 +100,12 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
   // k and v share one token stride of at least d (key rows past M must lie
   // beyond the last key row, where the bounds-checked tile loads return zeros)
   if (st.k[1] != st.v[1] || st.k[1] < d) return ATTN_ERR_LAYOUT;
-  // largest element offset of each tensor (+ d), and the K/V buffer range
-  // ((M + 64) token rows, so that offsets of the rows past M never wrap)
-  auto extent = [&](const int64_t* t, int rows, int heads) {
-    return (int64_t)(B - 1) * t[0] + (int64_t)(rows - 1) * t[1] + (int64_t)(heads - 1) * t[2] + d;
-  };
-  if (extent(st.q, N, Hq) >= kMaxElems || extent(st.o, N, Hq) >= kMaxElems ||
-      extent(st.k, M, Hkv) >= kMaxElems || extent(st.v, M, Hkv) >= kMaxElems ||
-      (int64_t)(M + 64) * st.k[1] + d >= kMaxElems || (int64_t)B * Hq * ((N + 63) / 64) >= kMaxElems)
+  // q, o and lse are addressed with 64-bit offsets; the kernel reads one
+  // (batch, kv head) slice of K or V through a buffer descriptor with 32-bit
+  // byte offsets, up to one tile of 64 rows past M, so (M + 64) token rows
+  // must stay below 2^31 elements.  The grid holds B * Hq * ceil(N / 64)
+  // workgroups at most.
+  if ((int64_t)(M + 64) * st.k[1] + d >= kMaxElems || (int64_t)B * Hq * ((N + 63) / 64) >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
@@ -127,10 +135,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
-  const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
-  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535 ||
-      (int64_t)(M + kDecodeChunk) * d >= kMaxElems)
-    return ATTN_ERR_TOO_LARGE;
+  if (decode_too_large(B, Hq, M, d, chunk_size)) return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u))
     return ATTN_ERR_ALIGNMENT;
@@ -150,10 +155,7 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
   if (!std::isfinite(scale) || scale < 0.f || !std::isfinite(k_scale) || k_scale < 0.f || !std::isfinite(v_scale) ||
       v_scale < 0.f)
     return ATTN_ERR_SCALE;
-  const int64_t C = ((int64_t)M + chunk_size - 1) / chunk_size;
-  if ((int64_t)B * Hkv * M * d >= kMaxElems || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535 ||
-      (int64_t)(M + kDecodeChunk) * d >= kMaxElems)
-    return ATTN_ERR_TOO_LARGE;
+  if (decode_too_large(B, Hq, M, d, chunk_size)) return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u))
     return ATTN_ERR_ALIGNMENT;
@@ -189,9 +191,7 @@ int paged_decode(const void* q, const void* k_cache, const void* v_cache, const 
       15 * pk.token_stride + d >= kMaxElems)
     return ATTN_ERR_LAYOUT;
   const int64_t M = (int64_t)pk.max_blocks * pk.block_size;
-  const int64_t C = (M + chunk_size - 1) / chunk_size;
-  if (M >= ((int64_t)1 << 30) || (int64_t)B * Hq * C * d >= kMaxElems || (int64_t)B * Hq > 65535)
-    return ATTN_ERR_TOO_LARGE;
+  if (M >= ((int64_t)1 << 30) || decode_too_large(B, Hq, M, d, chunk_size)) return ATTN_ERR_TOO_LARGE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(o_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u) || (reinterpret_cast<uintptr_t>(pk.block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(pk.seq_lens) & 3u))
@@ -227,7 +227,7 @@ int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
   if (B <= 0 || Hq <= 0 || num_chunks <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
   if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(out_dtype)) return ATTN_ERR_DTYPE;
-  if ((int64_t)B * Hq * num_chunks * d >= kMaxElems || (int64_t)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
+  if ((int64_t)B * Hq * num_chunks >= kMaxElems || (int64_t)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||
       (reinterpret_cast<uintptr_t>(o) & 1u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_ALIGNMENT;

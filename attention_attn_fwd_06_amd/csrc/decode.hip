@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "launch.h"
 #include "lds_stage.h"
 
 namespace attn {
@@ -755,7 +756,9 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
     MergeState r = part[0][tid];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) r = merge_states(r, part[w][tid]);
-    const float inv = 1.f / r.s;
+    // a row whose chunks are all empty (an empty sequence) has no weight:
+    // O = 0 and lse = -inf
+    const float inv = r.s > 0.f ? 1.f / r.s : 0.f;
     const int d0 = blockIdx.y * (4 * QW) + tid * 4;
     const uint32_t w01 = pack2<BF16>(r.a[0] * inv, r.a[1] * inv);
     const uint32_t w23 = pack2<BF16>(r.a[2] * inv, r.a[3] * inv);
@@ -801,10 +804,9 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
 #define ATTN_GQA_CASE(DD, BB)                                                                          \
     if (d == DD && bf16 == BB) {                                                                       \
       const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, false>>(kDecThreads)); \
-      hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false, false>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+      return launch(&decode_gqa_mfma_kernel<DD, BB, false, false>, dim3(grid), dim3(kDecThreads), stream,  \
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,      \
-                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{}, 1.f);                                 \
-      return hipGetLastError();                                                                        \
+                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{}, 1.f);                                                                        \
     }
     ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
     ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)
@@ -815,10 +817,9 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
 #define ATTN_DEC_CASE(DD, BB)                                                                          \
   if (d == DD && bf16 == BB) {                                                                         \
     const int grid = std::min(n_items, resident_grid<decode_chunk_kernel<DD, BB>>(kDecThreads));    \
-    hipLaunchKernelGGL((decode_chunk_kernel<DD, BB>), dim3(grid), dim3(kDecThreads), 0, stream,     \
+    return launch(&decode_chunk_kernel<DD, BB>, dim3(grid), dim3(kDecThreads), stream,     \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,   \
-                       Hq, Hkv, M, C, n_items, sl2);                                                   \
-    return hipGetLastError();                                                                          \
+                       Hq, Hkv, M, C, n_items, sl2);                                                                          \
   }
   ATTN_DEC_CASE(32, false) ATTN_DEC_CASE(32, true)
   ATTN_DEC_CASE(64, false) ATTN_DEC_CASE(64, true) ATTN_DEC_CASE(128, false) ATTN_DEC_CASE(128, true)
@@ -843,10 +844,9 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
 #define ATTN_PAGED_CASE(DD, BB, F8)                                                                    \
   if (d == DD && bf16 == BB && fp8 == F8) {                                                            \
     const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, F8>>(kDecThreads)); \
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, true, F8>), dim3(grid), dim3(kDecThreads), 0, stream,  \
+    return launch(&decode_gqa_mfma_kernel<DD, BB, true, F8>, dim3(grid), dim3(kDecThreads), stream,  \
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, o_part,     \
-                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, F8 ? v_scale : 1.f);            \
-    return hipGetLastError();                                                                          \
+                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, F8 ? v_scale : 1.f);                                                                          \
   }
   ATTN_PAGED_CASE(32, false, false) ATTN_PAGED_CASE(32, true, false) ATTN_PAGED_CASE(64, false, false)
   ATTN_PAGED_CASE(64, true, false) ATTN_PAGED_CASE(128, false, false) ATTN_PAGED_CASE(128, true, false)
@@ -868,10 +868,9 @@ hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, fl
 #define ATTN_FP8_CASE(DD, BB)                                                                          \
   if (d == DD && bf16 == BB) {                                                                         \
     const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, true>>(kDecThreads)); \
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<DD, BB, false, true>), dim3(grid), dim3(kDecThreads), 0, stream, \
+    return launch(&decode_gqa_mfma_kernel<DD, BB, false, true>, dim3(grid), dim3(kDecThreads), stream, \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv,   \
-                       M, C, g, chunk, n_items, sl2, PagedKv{}, v_scale);                                      \
-    return hipGetLastError();                                                                          \
+                       M, C, g, chunk, n_items, sl2, PagedKv{}, v_scale);                                                                          \
   }
   ATTN_FP8_CASE(32, false) ATTN_FP8_CASE(32, true) ATTN_FP8_CASE(64, false) ATTN_FP8_CASE(64, true)
   ATTN_FP8_CASE(128, false) ATTN_FP8_CASE(128, true)
@@ -890,9 +889,8 @@ hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, f
   const dim3 grid(B * Hq, d / (4 * qw));
 #define ATTN_MERGE_CASE(DD, BB, QQ)                                                                  \
   if (d == DD && bf16 == BB && qw == QQ) {                                                           \
-    hipLaunchKernelGGL((lse_merge_kernel<DD, BB, QQ>), grid, dim3(kMergeThreads), 0, stream, o_part, \
-                       lse_part, (uint16_t*)o, lse, C);                                              \
-    return hipGetLastError();                                                                        \
+    return launch(&lse_merge_kernel<DD, BB, QQ>, grid, dim3(kMergeThreads), stream, o_part, \
+                       lse_part, (uint16_t*)o, lse, C);                                                                        \
   }
 #define ATTN_MERGE_QW(DD, BB) ATTN_MERGE_CASE(DD, BB, 4) ATTN_MERGE_CASE(DD, BB, 8) ATTN_MERGE_CASE(DD, BB, 16)
   ATTN_MERGE_CASE(32, false, 4) ATTN_MERGE_CASE(32, false, 8)

@@ -56,6 +56,7 @@
 
 #include "../../include/attn.h"
 #include "device_common.h"
+#include "launch.h"
 #include "lds_stage.h"
 
 namespace attn {
@@ -627,10 +628,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   while ((1 << pack_shift) < pack) ++pack_shift;
   const TileDecode td{fast_div((uint32_t)(group / pack)), fast_div((uint32_t)n_qtiles), fast_div((uint32_t)Hkv),
                       group, pack_shift};
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, M, Hq,
-                     Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, st, scale * kLog2e);
-  return hipGetLastError();
+  return launch(&prefill_fwd_kernel<D, BF16, CAUSAL>, dim3(total), dim3(kThreads), stream, q, k, v, o, lse, N, M,
+                Hq, Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, st, scale * kLog2e);
 }
 
 hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,

@@ -61,7 +61,7 @@ typedef enum {
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
   ATTN_ERR_CHUNK_SIZE = -7,     /* decode chunk size not a multiple of 128 or above 8192 */
-  ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (hipGetLastError) */
+  ATTN_ERR_LAUNCH = -8,         /* the HIP launch failed (the launch's own status) */
   ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
   ATTN_ERR_ALIGNMENT = -10,     /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_SCALE = -11,         /* scale is negative, infinite or NaN */
@@ -93,7 +93,9 @@ typedef struct {
  * key; for N == M this is the page's top-left mask.  Causal requires N <= M;
  * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
  * including the row maximum).  Requires d in {32, 64, 128}, Hq % Hkv == 0, a finite
- * scale >= 0, and B*(N+256)*Hq*d, B*(M+64)*Hkv*d below 2^31.
+ * scale >= 0, (M+64)*Hkv*d below 2^31 (one batch's K or V, read with 32-bit
+ * offsets) and B*Hq*ceil(N/64) below 2^31; q, o and lse have no size limit
+ * of their own (64-bit offsets).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
@@ -107,9 +109,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * [B, Hq, N] contiguous.  strides == NULL means the contiguous layouts.  Every
  * stride must be >= 0 and a multiple of 8 elements (so that every row of d
  * values starts 16-byte aligned), and k and v must share one token stride of at
- * least d (otherwise ATTN_ERR_LAYOUT).  The largest element offset of each tensor must
- * stay below 2^31, and (M + 64) times the k/v token stride below 2^31
- * (otherwise ATTN_ERR_TOO_LARGE).  Outputs must not overlap inputs or each other.
+ * least d (otherwise ATTN_ERR_LAYOUT).  (M + 64) times the k/v token stride must
+ * stay below 2^31 (otherwise ATTN_ERR_TOO_LARGE).  Outputs must not overlap inputs or each other.
  */
 int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
@@ -136,7 +137,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size);
  * lse_part = m_c + ln l_c ("CUDA Flash Decoding", section 2.2 step 1).  No mask.
  * Requires chunk_size a multiple of 128 and at most 8192 (longer chunks mean fewer
  * partials for lse_merge to read), d in {32, 64, 128}, Hq % Hkv == 0, a finite
- * scale >= 0, B*Hq <= 65535, and B*Hkv*M*d, B*Hq*C*d and (M + 128)*d below 2^31.
+ * scale >= 0, B*Hq <= 65535, B*Hq*C and (M + 128)*d below 2^31 (one (batch, kv
+ * head) slice of K or V is read with 32-bit offsets).
  */
 int attn_decode_splitkv(const void* q, const void* k, const void* v,
                         float* o_part, float* lse_part,
@@ -153,8 +155,15 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v,
  * {block_size*Hkv*d, Hkv*d, d}; [num_blocks, Hkv, block_size, d] head-major pages
  * {Hkv*block_size*d, d, block_size*d}.  Key t of sequence b is row
  * t % block_size of page block_table[b*max_blocks + t / block_size]; sequence b
- * holds seq_lens[b] keys (1 .. max_blocks*block_size).  block_table and seq_lens
- * are device memory, read by the kernel.
+ * holds seq_lens[b] keys (0 .. max_blocks*block_size; a length above that is
+ * taken as max_blocks*block_size, a negative one as 0).  A sequence of 0 keys
+ * has no chunk with a key: after lse_merge its o is 0 and its lse is -inf.
+ * The page ids of a sequence's first ceil(seq_lens[b] / block_size) table
+ * entries must lie in [0, num_blocks); entries past those are never used.  An
+ * id out of range is never dereferenced: its rows are taken as keys and values
+ * of all zeros (so they still enter the softmax, with score 0), which is the
+ * result of no valid cache.  block_table and seq_lens are device memory, read
+ * by the kernel.
  */
 typedef struct {
   const int32_t* block_table;   /* [B, max_blocks] page ids in [0, num_blocks) */
@@ -175,9 +184,7 @@ typedef struct {
  *
  * with C = ceil(max_blocks*block_size / chunk_size).  Sequence b's chunks are
  * those of attn_decode_splitkv on its keys; chunks past its end get o_part = 0
- * and lse_part = -inf, which lse_merge gives no weight.  Page ids outside
- * [0, num_blocks) and lengths outside [0, max_blocks*block_size] are clamped
- * to no keys rather than read.  Requires the attn_decode_splitkv conditions on
+ * and lse_part = -inf, which lse_merge gives no weight.  Requires the attn_decode_splitkv conditions on
  * B, Hq, Hkv, d, chunk_size and scale, block_size % 16 == 0, strides >= 0 and
  * multiples of 8 with 15*token_stride + d below 2^31 (else ATTN_ERR_LAYOUT),
  * and max_blocks*block_size below 2^30.  The workspace size is
@@ -192,10 +199,10 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
  * attn_decode_paged_fp8kv_splitkv - attn_decode_paged_splitkv over a paged cache
  * of FP8 E4M3 codes with per-tensor scales (as attn_decode_fp8kv_splitkv): key
  * and value elements are one byte, so the element strides are byte strides and
- * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv, except that
- * in place of a row that does not exist (an out-of-range page id) the kernel
- * reads 16 bytes at the start of the cache (page 0, which num_blocks >= 1
- * guarantees) and discards them, so such rows still contribute no keys.
+ * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv, including
+ * the zero rows in place of out-of-range page ids (for those the kernel reads
+ * 16 bytes at the start of the cache, page 0, which num_blocks >= 1
+ * guarantees, and discards them).
  */
 int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const void* v_cache,
                                     float k_scale, float v_scale, const attn_paged_kv_t* pages,
@@ -229,7 +236,9 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
  *
  * g = max_c lse_c + ln sum_c exp(lse_c - max_c lse_c), w_c = exp(lse_c - g),
  * o = sum_c w_c o_part[c], lse = g ("CUDA Flash Decoding", section 2.2 step 2).
- * Requires num_chunks >= 1 and d in {32, 64, 128}.
+ * A row whose lse_part are all -inf (no key at all, e.g. an empty paged
+ * sequence) gets o = 0 and lse = -inf.  Requires num_chunks >= 1, d in
+ * {32, 64, 128}, B*Hq <= 65535 and B*Hq*num_chunks below 2^31.
  */
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
               int B, int Hq, int num_chunks, int d, attn_dtype_t out_dtype,

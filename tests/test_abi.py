@@ -68,7 +68,8 @@ def fwd(**kw):
     (dict(Hq=6, Hkv=4), -5),
     (dict(causal=1, N=256, M=128), -6),
     (dict(scale=-0.5), -11), (dict(scale=float("inf")), -11), (dict(scale=float("nan")), -11),
-    (dict(B=1 << 12, N=1 << 12, Hq=1 << 4, d=128), -9),
+    (dict(B=1 << 14, Hq=1 << 12, Hkv=1, N=1 << 12), -9),   # grid of 2^32 workgroups
+    (dict(M=1 << 23, Hkv=2, d=128), -9),                 # one batch's K beyond 2^31 elements
     (dict(q=FAKE + 8), -10), (dict(o=FAKE + 2), -10), (dict(lse=FAKE + 2), -10),
 ])
 def test_attn_fwd_rejects(kw, code):
@@ -109,13 +110,18 @@ def _set(field, i, val):
     (_set("q", 1, -128), {}, -12), (_set("o", 2, 4), {}, -12), (_set("v", 0, 12), {}, -12),
     (_set("v", 1, 256), {}, -12),      # k and v token strides differ
     (_set("k", 1, 32), {}, -12),       # token stride below d (same for v)
-    (_set("q", 0, 1 << 31), {}, -9),   # largest q offset beyond 2^31 elements (needs B > 1)
     (None, dict(q=FAKE + 8), -10),
 ])
 def test_attn_fwd_strided_rejects(edit, kw, code):
-    if code == -9:
-        kw = dict(B=2)
     assert fwd_strided(edit, **kw) == code
+
+
+def test_attn_fwd_strided_kv_slice_too_large():
+    """(M + 64) token rows of the k/v token stride beyond 2^31 elements."""
+    def edit(st):
+        st.k[1] = 1 << 24
+        st.v[1] = 1 << 24
+    assert fwd_strided(edit) == -9
 
 
 def test_attn_fwd_strided_k_v_equal_small_token_stride_rejected():

@@ -215,6 +215,31 @@ def test_prefill_strided_layouts():
     assert maxerr(f64(o), Or) <= TOL_O["f16"]
 
 
+def test_prefill_q_beyond_2_31_elements():
+    """q and o of 2^31 elements (4 GiB each): rows past the 2^31st element
+    are read and written through 64-bit offsets.  Checked against the oracle
+    on the last rows of every head."""
+    B, N, Hq, Hkv, M, d = 1, 262144, 64, 1, 128, 128
+    say(f"case prefill q with {B * N * Hq * d} elements")
+    g = torch.Generator("cpu").manual_seed(31)
+    k = torch.randn((B, M, Hkv, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, M, Hkv, d), generator=g).to(torch.bfloat16)
+    q = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=DEV)
+    q.normal_(generator=torch.Generator(DEV).manual_seed(32))
+    scale = float(np.float32(d ** -0.5))
+    o, lse = attn().attn_fwd(q, k.to(DEV), v.to(DEV), causal=False, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.arange(N - 40, N)
+    qs = q[:, N - 40:].cpu()
+    Or, Lr = oracle.attn_ref(qs, k, v, scale, False)
+    eo = maxerr(f64(o[:, N - 40:]), Or)
+    el = maxerr(f64(lse[:, :, N - 40:]), Lr)
+    say(f"  last rows: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+    del q, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_prefill_deterministic():
     say("case prefill determinism")
     q, k, v = prefill_inputs(1, 8, 2, 520, 520, 128, "bf16", 5)
@@ -441,6 +466,63 @@ def test_decode_paged_fp8kv(case):
     say(f"  {case}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
     assert errs["o"] <= TOL_O[dt] and errs["o_part"] <= TOL_O[dt], errs
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8kv"])
+def test_decode_paged_invalid_page_and_empty_sequence(fp8):
+    """Sequence 0 is empty (o = 0, lse = -inf after the merge); sequence 2
+    has an out-of-range page id inside its length, whose rows the kernels
+    take as zero keys and values: the oracle sees the same cache with that
+    id pointing at a page of zeros."""
+    B, Hq, Hkv, d, bs, chunk = 3, 8, 2, 128, 16, 128
+    lens = [0, 200, 1000]
+    say(f"case paged decode, empty sequence and bad page id, fp8={fp8}")
+    q, kc, vc, kv_k, kv_v, table, sl = paged_inputs(B, Hq, Hkv, lens, d, "f16", bs, seed=77, head_major=False)
+    num_blocks = kc.shape[0]
+    table[2, 5] = num_blocks + 11          # inside sequence 2 (keys 80 .. 95)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(3.0 / 448.0))
+    if fp8:
+        kc = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        vc = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    scale = float(np.float32(d ** -0.5))
+    o, lse, op, lp = attn().attn_decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), sl.to(DEV), chunk,
+                                              scale, k_scale=ks if fp8 else None, v_scale=vs if fp8 else None)
+    torch.cuda.synchronize()
+    if fp8:
+        kref, vref = oracle.e4m3_decode(kc.numpy()) * ks, oracle.e4m3_decode(vc.numpy()) * vs
+    else:
+        kref, vref = f64(kc), f64(vc)
+    zero = np.zeros((1,) + kref.shape[1:])
+    kref, vref = np.concatenate([kref, zero]), np.concatenate([vref, zero])
+    tref = table.clone()
+    tref[2, 5] = num_blocks                # the appended page of zeros
+    Or, Lr, OPr, LPr = oracle.paged_decode_ref(q, kref, vref, tref.clamp(min=0), sl, scale, chunk)
+    Og, Lg = f64(o), f64(lse)
+    assert np.all(Og[0] == 0.0) and np.all(Lg[0] == -np.inf), "empty sequence"
+    assert np.all(Lr[0] == -np.inf)
+    eo, el = maxerr(Og[1:], Or[1:]), maxerr(Lg[1:], Lr[1:])
+    say(f"  o={eo:.3e} lse={el:.3e}")
+    assert eo <= TOL_O["f16"] and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_lse_merge_empty_rows(dt):
+    """Rows whose chunks are all -inf (no key) give o = 0 and lse = -inf."""
+    say(f"case lse_merge empty rows {dt}")
+    g = torch.Generator("cpu").manual_seed(5)
+    op = torch.randn((2, 3, 40, 128), generator=g) * 0.5
+    lp = torch.randn((2, 3, 40), generator=g) * 4.0
+    lp[0, 1] = float("-inf")
+    lp[1, 2, 7:] = float("-inf")
+    op[0, 1] = 0.0
+    o, lse = attn().lse_merge(op.to(DEV), lp.to(DEV), torch_dtype(dt))
+    torch.cuda.synchronize()
+    Or, Lr = oracle.lse_merge_ref(op, lp)
+    Og, Lg = f64(o), f64(lse)
+    assert np.all(Og[0, 1] == 0.0) and Lg[0, 1] == -np.inf
+    fin = np.isfinite(Lr)
+    assert np.array_equal(np.isfinite(Lg), fin)
+    assert maxerr(Og, Or) <= TOL_O[dt] and maxerr(Lg[fin], Lr[fin]) <= TOL_LSE
 
 
 def test_decode_paged_matches_contiguous():
