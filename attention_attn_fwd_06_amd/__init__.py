@@ -15,7 +15,8 @@ from . import _lib
 __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
-    "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv",
+    "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
+    "attn_decode_fused_workspace_bytes",
 ]
 
 ATTN_F16 = 0
@@ -194,6 +195,59 @@ def attn_decode_splitkv(q, k, v, chunk_size: int = 128, scale: float | None = No
     if st != 0:
         raise AttnError(st, "attn_decode_splitkv")
     return o_part, lse_part
+
+
+def attn_decode_fused_workspace_bytes(B: int, Hq: int, Hkv: int, M: int, d: int) -> int:
+    return int(_lib.load().attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
+
+
+def attn_decode_fused(q, k, v, scale: float | None = None, o=None, lse=None, return_lse: bool = True,
+                      workspace=None, stream=None):
+    """Split-KV decode end to end in one launch (partials and merge fused).
+
+    q [B,Hq,d], k/v [B,Hkv,M,d] -> (o [B,Hq,d], lse [B,Hq] fp32 or None).
+    ``workspace``: a uint8 GPU tensor of at least
+    attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d) bytes, zero-filled
+    before its first use (every completed call leaves its counters at zero);
+    by default a fresh zeroed one is allocated for the call."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, M, d]")
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, Hkv, M, d))
+    _shape(v, "v", k.shape)
+    _dtype(k, "k", q.dtype)
+    _dtype(v, "v", q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, n)
+    if o is not None:
+        _shape(o, "o", (B, Hq, d))
+        _dtype(o, "o", q.dtype)
+        _contig(o, "o")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq))
+    nbytes = attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d)
+    if workspace is not None:
+        _dtype(workspace, "workspace", torch.uint8)
+        _contig(workspace, "workspace")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (workspace, "workspace"))
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = _lib.load().attn_decode_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                                       workspace.numel(), B, Hq, Hkv, M, d, float(scale), dt, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fused")
+    return o, lse
 
 
 _FP8 = (torch.uint8, torch.float8_e4m3fn)

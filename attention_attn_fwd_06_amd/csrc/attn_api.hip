@@ -27,6 +27,11 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
 hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
                                  float* o_part, float* lse_part, int B, int Hq, int Hkv, int M, int d, int chunk,
                                  bool bf16, float scale, hipStream_t stream);
+hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, int B, int Hq, int Hkv, int M, int d, bool bf16, float scale,
+                                 hipStream_t stream);
+size_t fused_workspace_layout(int B, int Hq, int Hkv, int d, int S, size_t* off_lse, size_t* off_o);
+int fused_segment_cap(int B, int Hq, int Hkv, int M);
 }  // namespace attn
 
 namespace {
@@ -69,6 +74,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_TOO_LARGE: return "a size exceeds the supported index range";
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scales must be finite and >= 0";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than attn_decode_fused_workspace_bytes";
     case ATTN_ERR_LAYOUT:
       return "strides must be >= 0 and multiples of 8 elements (k and v: one token stride >= d; paged: "
              "block_size a multiple of 16, 15 * token_stride + d < 2^31)";
@@ -141,6 +147,31 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
     return ATTN_ERR_ALIGNMENT;
   return launch_status(attn::decode_dispatch(q, k, v, o_part, lse_part, B, Hq, Hkv, M, d, chunk_size,
                                              dtype == ATTN_BF16, scale, stream));
+}
+
+size_t attn_decode_fused_workspace_bytes(int B, int Hq, int Hkv, int M, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || Hq % Hkv != 0 || !valid_head_dim(d)) return 0;
+  return attn::fused_workspace_layout(B, Hq, Hkv, d, attn::fused_segment_cap(B, Hq, Hkv, M), nullptr, nullptr);
+}
+
+int attn_decode_fused(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int M, int d, float scale, attn_dtype_t dtype,
+                      hipStream_t stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  if (decode_too_large(B, Hq, M, d, kDecodeChunk)) return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(attn::decode_fused_dispatch(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, M, d,
+                                                   dtype == ATTN_BF16, scale, stream));
 }
 
 int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float k_scale, float v_scale,

@@ -222,6 +222,38 @@ void decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 //   KV8: K/V are FP8 E4M3 codes; k_scale is folded into scale_log2 by the
 // host and v_scale multiplies the stored partial.  With PAGED as well, each
 // lane looks up its own row's page.
+// (m, s, a[4]) merge of two running states, in log2 units: both rescaled to
+// the larger reference max.  A state with m = -inf (no chunk yet) is empty.
+struct MergeState {
+  float m, s, a[4];
+};
+// Adds one chunk (lse l2 in log2 units, normalised output ov) to a running
+// state: both rescaled to the larger reference max.  An empty state (m =
+// -inf) or an empty chunk (lse = -inf) has no weight, also when both are
+// empty.
+__device__ __forceinline__ void merge_chunk(MergeState& st, float l2, const float4& ov) {
+  const float mn = fmaxf(st.m, l2);
+  const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
+  const float w = l2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l2 - mn);
+  st.s = fmaf(st.s, r, w);
+  st.a[0] = fmaf(st.a[0], r, w * ov.x);
+  st.a[1] = fmaf(st.a[1], r, w * ov.y);
+  st.a[2] = fmaf(st.a[2], r, w * ov.z);
+  st.a[3] = fmaf(st.a[3], r, w * ov.w);
+  st.m = mn;
+}
+__device__ __forceinline__ MergeState merge_states(const MergeState& x, const MergeState& y) {
+  const float mm = fmaxf(x.m, y.m);
+  const float rx = (x.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x.m - mm);
+  const float ry = (y.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(y.m - mm);
+  MergeState r;
+  r.m = mm;
+  r.s = fmaf(x.s, rx, y.s * ry);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.a[c] = fmaf(x.a[c], rx, y.a[c] * ry);
+  return r;
+}
+
 constexpr int kGqaCols = 16;         // MFMA columns: query heads per item
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
@@ -234,15 +266,32 @@ struct PagedKv {
   int64_t page_stride, token_stride, head_stride;
   int num_blocks, block_size, max_blocks;
 };
+// Fused decode (split-KV with the merge inside the chunk kernel): an item is
+// (row, segment), a row being (batch, kv head, head slice) and a segment a run
+// of consecutive 128-key chunks of that row.  Each item leaves its
+// normalised partial and its log-sum-exp (log2 units) in seg_o / seg_lse; the
+// workgroup that finishes a row's last segment (a per-row counter, reset by
+// that workgroup) merges the row's partials into o and lse.  With one segment
+// per row the item writes o and lse directly.
+struct FusedOut {
+  float* seg_o;      // [rows, S, G, D] normalised segment outputs
+  float* seg_lse;    // [rows, S, G] segment log-sum-exp, log2 units
+  uint32_t* count;   // [rows] segments finished; 0 between calls
+  uint16_t* o;       // [B, Hq, D] final output (16-bit)
+  float* lse;        // [B, Hq] final log-sum-exp (natural log), or null
+  int n_chunks;      // 128-key chunks per row, ceil(M / 128)
+};
+
 constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
 constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
 
-template <int D, bool BF16, bool PAGED, bool KV8>
+template <int D, bool BF16, bool PAGED, bool KV8, bool FUSED = false>
 __global__ __launch_bounds__(kDecThreads)
 void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
-                            int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale) {
+                            int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale, FusedOut fo) {
+  static_assert(!FUSED || (!PAGED && !KV8), "the fused merge is built for contiguous 16-bit K/V");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
   constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
@@ -391,6 +440,88 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       q8 = *reinterpret_cast<const uint4*>(q + ((int64_t)bb * Hq + hh0 + rq) * D + 8 * lc);
   };
 
+  // Fused mode, after item (row, seg): with one segment per row, o and lse
+  // directly.  Otherwise the segment's partial goes to seg_o / seg_lse and the
+  // row's counter is incremented; the workgroup that brings it to C (the
+  // row's last segment) merges the row's partials ("CUDA Flash Decoding",
+  // section 2.2 step 2: w_s = exp(lse_s - logsumexp lse), o = sum_s w_s o_s)
+  // and resets the counter for the next call.
+  //   Visibility across the XCDs (each has its own L2): the partials are
+  // written and read with device-scope relaxed atomic stores and loads, which
+  // go through to the memory side instead of staying in an XCD's L2, and
+  // every thread waits for its stores to complete before the workgroup
+  // barrier that precedes the counter increment; the merging workgroup reads
+  // only after seeing the count.  A release/acquire fence pair would write
+  // back and invalidate the whole L2 in every wave instead (measured: it
+  // doubles the kernel's time).
+  __shared__ int fused_last;
+  auto fused_epilogue = [&](int row, int b, int h0, int seg, float lt, float m_ref, const f32x4 (&acc)[kDB]) {
+    if (C == 1) {
+      if (j < G) {
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          if (wave >= kPVWaves) break;
+          const f32x4 o4 = acc[db] * inv;
+          *reinterpret_cast<uint2*>(fo.o + ((int64_t)b * Hq + h0 + j) * D + 16 * (wave * kDB + db) + 4 * g) =
+              make_uint2(pack2<BF16>(o4[0], o4[1]), pack2<BF16>(o4[2], o4[3]));
+        }
+        if (wave == 0 && g == 0 && fo.lse != nullptr) fo.lse[(int64_t)b * Hq + h0 + j] = (m_ref + log2f(lt)) * kLn2;
+      }
+      return;
+    }
+    auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto get = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    if (j < G) {
+      const int64_t e = ((int64_t)row * C + seg) * G + j;
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        if (wave >= kPVWaves) break;
+        float* op = fo.seg_o + e * D + 16 * (wave * kDB + db) + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) put(op + r, acc[db][r] * inv);
+      }
+      if (wave == 0 && g == 0) put(fo.seg_lse + e, m_ref + log2f(lt));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0)
+      fused_last = __hip_atomic_fetch_add(fo.count + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)(C - 1);
+    __syncthreads();
+    if (!fused_last) return;
+    // (head, column quad) pairs, each merged over the row's C segments by SG
+    // threads (segments sg, sg + SG, ...); their states meet in LDS (the K
+    // buffer, free after the last sub-chunk's barriers)
+    constexpr int kQuads = D / 4;
+    const int pairs = G * kQuads;
+    const int SG = pairs >= kDecThreads ? 1 : min(16, kDecThreads / pairs);
+    MergeState* sts = reinterpret_cast<MergeState*>(kbuf);
+    for (int u = tid; u < pairs * SG; u += kDecThreads) {
+      const int p = u % pairs, sg = u / pairs, jj = p / kQuads, quad = p % kQuads;
+      MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+      for (int sgm = sg; sgm < C; sgm += SG) {
+        const int64_t e = ((int64_t)row * C + sgm) * G + jj;
+        const float* op = fo.seg_o + e * D + 4 * quad;
+        merge_chunk(st, get(fo.seg_lse + e), make_float4(get(op), get(op + 1), get(op + 2), get(op + 3)));
+      }
+      sts[u] = st;
+    }
+    __syncthreads();
+    for (int p = tid; p < pairs; p += kDecThreads) {
+      MergeState r = sts[p];
+      for (int sg = 1; sg < SG; ++sg) r = merge_states(r, sts[sg * pairs + p]);
+      const int jj = p / kQuads, quad = p % kQuads;
+      const float inv = r.s > 0.f ? 1.f / r.s : 0.f;
+      *reinterpret_cast<uint2*>(fo.o + ((int64_t)b * Hq + h0 + jj) * D + 4 * quad) =
+          make_uint2(pack2<BF16>(r.a[0] * inv, r.a[1] * inv), pack2<BF16>(r.a[2] * inv, r.a[3] * inv));
+      if (quad == 0 && fo.lse != nullptr) fo.lse[(int64_t)b * Hq + h0 + jj] = (r.m + log2f(r.s)) * kLn2;
+    }
+    if (tid == 0) __hip_atomic_store(fo.count + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int c = item % C;
     const int rest = item / C;
@@ -417,7 +548,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         continue;  // uniform over the workgroup; no LDS was touched
       }
     }
-    const int c_end = min(seq, (c + 1) * chunk);
+    // keys of this item: chunk c, or (fused) segment c of the row's chunks
+    const int k_begin = FUSED ? (int)((int64_t)c * fo.n_chunks / C) * kChunk : c * chunk;
+    const int c_end = FUSED ? min(M, (int)((int64_t)(c + 1) * fo.n_chunks / C) * kChunk) : min(seq, (c + 1) * chunk);
     const int64_t slice = PAGED ? 0 : ((int64_t)b * Hkv + kvh) * M * D;
 
     // Q rows h0 .. h0 + 15 (once per item), then per 128-key sub-chunk its K
@@ -439,7 +572,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     f32x4 oacc[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db) oacc[db] = (f32x4){};
-    for (int key0 = c * chunk; key0 < c_end; key0 += kChunk) {
+    for (int key0 = k_begin; key0 < c_end; key0 += kChunk) {
       const int len = min(kChunk, c_end - key0);
       const bool last = key0 + kChunk >= c_end;
       if constexpr (KV8) {
@@ -658,6 +791,11 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     float lt = red[1][0][j];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) lt += red[1][w][j];
+    if constexpr (FUSED) {
+      fused_epilogue(rest, b, h0, c, lt, m_run, oacc);
+      __syncthreads();  // Q, K, V, P, the sums and the merge states are refilled by the next item
+      continue;
+    }
     if (j < G) {
       const int64_t base = ((int64_t)b * Hq + h0 + j) * C + c;
 #pragma unroll
@@ -680,23 +818,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 }
 
 constexpr int kMergeThreads = 256;
-
-// (m, s, a[4]) merge of two running states, in log2 units: both rescaled to
-// the larger reference max.  A state with m = -inf (no chunk yet) is empty.
-struct MergeState {
-  float m, s, a[4];
-};
-__device__ __forceinline__ MergeState merge_states(const MergeState& x, const MergeState& y) {
-  const float mm = fmaxf(x.m, y.m);
-  const float rx = (x.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x.m - mm);
-  const float ry = (y.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(y.m - mm);
-  MergeState r;
-  r.m = mm;
-  r.s = fmaf(x.s, rx, y.s * ry);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) r.a[c] = fmaf(x.a[c], rx, y.a[c] * ry);
-  return r;
-}
 
 // One pass over the partials.  A workgroup covers one (batch, head) and QW
 // column quads (4*QW columns); thread t takes quad t % QW and chunk group
@@ -726,19 +847,7 @@ void lse_merge_kernel(const float* __restrict__ o_part, const float* __restrict_
   MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
   for (int c = grp; c < C; c += kGroups) {
-    const float l2 = lp[c] * kLog2e;
-    const float4 ov = *reinterpret_cast<const float4*>(op + (int64_t)c * D);
-    const float mn = fmaxf(st.m, l2);
-    // an empty state (m = -inf) or an empty chunk (lse = -inf) has no weight,
-    // also when both are empty (mn = -inf)
-    const float r = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mn);
-    const float w = l2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l2 - mn);
-    st.s = fmaf(st.s, r, w);
-    st.a[0] = fmaf(st.a[0], r, w * ov.x);
-    st.a[1] = fmaf(st.a[1], r, w * ov.y);
-    st.a[2] = fmaf(st.a[2], r, w * ov.z);
-    st.a[3] = fmaf(st.a[3], r, w * ov.w);
-    st.m = mn;
+    merge_chunk(st, lp[c] * kLog2e, *reinterpret_cast<const float4*>(op + (int64_t)c * D));
   }
   // lanes that share cq differ in the lane bits from log2(QW) up
 #pragma unroll
@@ -806,7 +915,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
       const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, false>>(kDecThreads)); \
       return launch(&decode_gqa_mfma_kernel<DD, BB, false, false>, dim3(grid), dim3(kDecThreads), stream,  \
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part,      \
-                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{}, 1.f);                                                                        \
+                         Hq, Hkv, M, C, g, chunk, n_items, sl2, PagedKv{}, 1.f, FusedOut{});                                                                        \
     }
     ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
     ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)
@@ -824,6 +933,83 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   ATTN_DEC_CASE(32, false) ATTN_DEC_CASE(32, true)
   ATTN_DEC_CASE(64, false) ATTN_DEC_CASE(64, true) ATTN_DEC_CASE(128, false) ATTN_DEC_CASE(128, true)
 #undef ATTN_DEC_CASE
+  return hipErrorInvalidValue;
+}
+
+// ---- fused decode: plan, workspace layout and launch ----
+
+constexpr int kFusedGridCap = 2048;  // most resident workgroups a plan assumes
+
+static int heads_per_item(int group) {
+  // the largest divisor of the group that fits the 16 MFMA columns
+  int g = std::min(group, kGqaCols);
+  while (group % g != 0) --g;
+  return g;
+}
+
+// Workspace of a fused decode with S segments per row: the per-row counters,
+// then seg_lse, then seg_o, each section starting at a multiple of 256 bytes.
+size_t fused_workspace_layout(int B, int Hq, int Hkv, int d, int S, size_t* off_lse, size_t* off_o) {
+  const int G = heads_per_item(Hq / Hkv);
+  const size_t rows = (size_t)B * (size_t)(Hq / G);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t cnt = up(rows * 4);
+  const size_t lse_bytes = up(rows * (size_t)S * G * 4);
+  if (off_lse) *off_lse = cnt;
+  if (off_o) *off_o = cnt + lse_bytes;
+  return cnt + lse_bytes + rows * (size_t)S * G * (size_t)d * 4;
+}
+
+// Largest segment count any launch may choose for these sizes (twice the
+// rows' share of the largest grid assumed, at most one segment per chunk):
+// the workspace is sized for it.
+int fused_segment_cap(int B, int Hq, int Hkv, int M) {
+  const int64_t rows = (int64_t)B * (Hq / heads_per_item(Hq / Hkv));
+  const int64_t chunks = ((int64_t)M + kChunk - 1) / kChunk;
+  return (int)std::min<int64_t>(chunks, 2 * ((kFusedGridCap + rows - 1) / rows));
+}
+
+// Segments per row: the S in [1, cap] that minimises the rounds of the
+// resident grid times the chunks of the longest segment (the smallest S on
+// a tie, so fewer partials to merge).
+static int fused_segments(int64_t rows, int64_t chunks, int64_t grid, int cap) {
+  int best = 1;
+  int64_t best_cost = ((rows + grid - 1) / grid) * chunks;
+  for (int S = 2; S <= cap; ++S) {
+    const int64_t cost = ((rows * S + grid - 1) / grid) * ((chunks + S - 1) / S);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
+
+hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, int B, int Hq, int Hkv, int M, int d, bool bf16, float scale,
+                                 hipStream_t stream) {
+  const int G = heads_per_item(Hq / Hkv);
+  const int64_t rows = (int64_t)B * (Hq / G);
+  const int chunks = (M + kChunk - 1) / kChunk;
+  const int cap = fused_segment_cap(B, Hq, Hkv, M);
+  const float sl2 = scale * kLog2e;
+#define ATTN_FUSED_CASE(DD, BB)                                                                              \
+  if (d == DD && bf16 == BB) {                                                                               \
+    auto* kern = &decode_gqa_mfma_kernel<DD, BB, false, false, true>;                                        \
+    const int resident = resident_grid<decode_gqa_mfma_kernel<DD, BB, false, false, true>>(kDecThreads);    \
+    const int S = fused_segments(rows, chunks, std::min(resident, kFusedGridCap), cap);                     \
+    size_t off_lse = 0, off_o = 0;                                                                           \
+    if (fused_workspace_layout(B, Hq, Hkv, DD, S, &off_lse, &off_o) > ws_bytes) return hipErrorInvalidValue; \
+    char* base = static_cast<char*>(ws);                                                                     \
+    const FusedOut fo{reinterpret_cast<float*>(base + off_o), reinterpret_cast<float*>(base + off_lse),      \
+                      reinterpret_cast<uint32_t*>(base), static_cast<uint16_t*>(o), lse, chunks};            \
+    const int n_items = (int)(rows * S);                                                                     \
+    return launch(kern, dim3(std::min(n_items, resident)), dim3(kDecThreads), stream, q, k, v,              \
+                  (float*)nullptr, (float*)nullptr, Hq, Hkv, M, S, G, kChunk, n_items, sl2, PagedKv{}, 1.f, fo); \
+  }
+  ATTN_FUSED_CASE(32, false) ATTN_FUSED_CASE(32, true) ATTN_FUSED_CASE(64, false)
+  ATTN_FUSED_CASE(64, true) ATTN_FUSED_CASE(128, false) ATTN_FUSED_CASE(128, true)
+#undef ATTN_FUSED_CASE
   return hipErrorInvalidValue;
 }
 
@@ -846,7 +1032,7 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
     const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, F8>>(kDecThreads)); \
     return launch(&decode_gqa_mfma_kernel<DD, BB, true, F8>, dim3(grid), dim3(kDecThreads), stream,  \
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, o_part,     \
-                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, F8 ? v_scale : 1.f);                                                                          \
+                       lse_part, Hq, Hkv, M, C, g, chunk, n_items, sl2, pk, F8 ? v_scale : 1.f, FusedOut{});                                                                          \
   }
   ATTN_PAGED_CASE(32, false, false) ATTN_PAGED_CASE(32, true, false) ATTN_PAGED_CASE(64, false, false)
   ATTN_PAGED_CASE(64, true, false) ATTN_PAGED_CASE(128, false, false) ATTN_PAGED_CASE(128, true, false)
@@ -870,7 +1056,7 @@ hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, fl
     const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, false, true>>(kDecThreads)); \
     return launch(&decode_gqa_mfma_kernel<DD, BB, false, true>, dim3(grid), dim3(kDecThreads), stream, \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv,   \
-                       M, C, g, chunk, n_items, sl2, PagedKv{}, v_scale);                                                                          \
+                       M, C, g, chunk, n_items, sl2, PagedKv{}, v_scale, FusedOut{});                                                                          \
   }
   ATTN_FP8_CASE(32, false) ATTN_FP8_CASE(32, true) ATTN_FP8_CASE(64, false) ATTN_FP8_CASE(64, true)
   ATTN_FP8_CASE(128, false) ATTN_FP8_CASE(128, true)

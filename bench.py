@@ -315,6 +315,11 @@ def main():
         for i in range(args.steps):
             chunk_only(i, c_events[i])
         torch.cuda.synchronize()
+        # the same decode in one launch (partials and merge fused)
+        ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d), dtype=torch.uint8,
+                         device=dev)
+        f_ms = _time_chunk(lambda i: attn.attn_decode_fused(dq, kv_sets[i % 2][0], kv_sets[i % 2][1], wd.scale, o=do_,
+                                                            lse=dlse, workspace=ws, stream=stream), args)
 
     out = {
         "metric": "attn fwd TFLOP/s & % MFMA peak (prefill); decode HBM GB/s & % peak",
@@ -345,6 +350,10 @@ def main():
                          "dtype": "f16", "chunk_merge_ms": round(d_ms, 4), "chunk_ms": round(c_ms, 4),
                          "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
                          "algorithmic_bytes": nbytes}
+        out["decode_fused"] = {"value": round(nbytes / (f_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "frac": round(nbytes / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "ms": round(f_ms, 4),
+                               "kernel": "decode_gqa_mfma_kernel<128,f16,fused>",
+                               "note": "partials of 128-key chunk runs and their merge in one launch"}
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                   "frac": round(chunk_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

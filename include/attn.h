@@ -18,6 +18,9 @@
  *                        codes and per-tensor scales (fp8 KV quantisation, listed as
  *                        future work on the "fmha sm120" page).
  *   attn_decode_paged_fp8kv_splitkv  both: a paged cache of FP8 codes.
+ *   attn_decode_fused    both Flash-Decoding steps in one launch, the merge done by the
+ *                        last workgroup of each row (a per-row counter in a caller-owned
+ *                        workspace).
  *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
  *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
  *                        section 2.2, step 2, and section 6 "reduce kernel").
@@ -65,8 +68,9 @@ typedef enum {
   ATTN_ERR_TOO_LARGE = -9,      /* a size exceeds the library's index range */
   ATTN_ERR_ALIGNMENT = -10,     /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_SCALE = -11,         /* scale is negative, infinite or NaN */
-  ATTN_ERR_LAYOUT = -12         /* strides: negative, not a multiple of 8 elements, or k and v
+  ATTN_ERR_LAYOUT = -12,        /* strides: negative, not a multiple of 8 elements, or k and v
                                    token strides differ or are below d */
+  ATTN_ERR_WORKSPACE = -13      /* workspace NULL, not 16-byte aligned, or too small */
 } attn_status_t;
 
 /*
@@ -144,6 +148,45 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v,
                         float* o_part, float* lse_part,
                         int B, int Hq, int Hkv, int M, int d, int chunk_size, float scale,
                         attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_fused_workspace_bytes - bytes of device workspace that
+ * attn_decode_fused needs for these sizes (0 for invalid sizes).  It holds one
+ * counter per (batch, kv head, head slice) and the fp32 partial output and
+ * log-sum-exp of every segment the launch may split the keys into.
+ */
+size_t attn_decode_fused_workspace_bytes(int B, int Hq, int Hkv, int M, int d);
+
+/*
+ * attn_decode_fused - split-KV decode end to end in one launch: the partials
+ * of attn_decode_splitkv and the merge of lse_merge ("CUDA Flash Decoding",
+ * section 2.2 steps 1 and 2; fusing the reduce into the chunk kernel is the
+ * page's section 8 lever of a last-block reduce).
+ *
+ *   q   [B, Hq, d]      dtype, read     o   [B, Hq, d]  dtype, written
+ *   k   [B, Hkv, M, d]  dtype, read     lse [B, Hq]     fp32, written (may be NULL)
+ *   v   [B, Hkv, M, d]  dtype, read
+ *
+ * The keys of each (batch, query head) are split into segments of whole
+ * 128-key chunks (the library picks how many from the sizes and the GPU, at
+ * most attn_decode_fused_workspace_bytes' worth); each segment's normalised
+ * output O_s and lse_s go to the workspace, and the workgroup that finishes a
+ * row's last segment merges them with w_s = exp(lse_s - logsumexp_s lse_s).
+ * The result is that of attn_decode_splitkv + lse_merge up to rounding.
+ *
+ * workspace: device memory of at least attn_decode_fused_workspace_bytes(B,
+ * Hq, Hkv, M, d) bytes, 16-byte aligned, owned by the caller.  Its counters
+ * must be zero before the first call (fill the buffer with zeros once); every
+ * call that completes leaves them zero again, so the same workspace serves
+ * any later call of any size that fits.  Calls that may run at the same time
+ * (other streams) need workspaces of their own.  Requires the conditions of
+ * attn_decode_splitkv for chunk_size 128 (else its status codes) and
+ * ATTN_ERR_WORKSPACE for a NULL, misaligned or short workspace.
+ */
+int attn_decode_fused(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int M, int d, float scale,
+                      attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * Paged KV cache for attn_decode_paged_splitkv (the "fmha sm120" page lists

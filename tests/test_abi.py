@@ -28,7 +28,7 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
          "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
-         "attn_status_string"])
+         "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -237,3 +237,33 @@ def test_workspace_bytes():
     assert lib.attn_decode_workspace_bytes(2, 8, 65536, 128, 128) == 2 * 8 * 512 * 129 * 4
     assert lib.attn_decode_workspace_bytes(1, 8, 513, 128, 128) == 1 * 8 * 5 * 129 * 4
     assert lib.attn_decode_workspace_bytes(0, 8, 512, 128, 128) == 0
+
+
+def fused(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30, B=2, Hq=8, Hkv=8, M=65536, d=128,
+             scale=0.088, dtype=0, stream=None)
+    a.update(kw)
+    return _lib.load().attn_decode_fused(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"],
+                                         a["Hq"], a["Hkv"], a["M"], a["d"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(M=0), -2), (dict(Hkv=0), -2), (dict(d=80), -3),
+    (dict(dtype=3), -4), (dict(Hq=8, Hkv=3), -5), (dict(scale=float("nan")), -11),
+    (dict(B=70000, Hq=1, Hkv=1), -9), (dict(M=1 << 24), -9),
+    (dict(o=FAKE + 8), -10), (dict(lse=FAKE + 1), -10),
+    (dict(ws=None), -13), (dict(ws=FAKE + 8), -13), (dict(wsb=100), -13),
+])
+def test_decode_fused_rejects(kw, code):
+    assert fused(**kw) == code
+
+
+def test_decode_fused_workspace_bytes():
+    lib = _lib.load()
+    # long decode workload: 16 rows of 512 chunks; at most 256 segments each,
+    # one fp32 output row of 128 and one lse per segment, plus the counters
+    n = lib.attn_decode_fused_workspace_bytes(2, 8, 8, 65536, 128)
+    assert n == 256 + 16 * 256 * 4 + 16 * 256 * 128 * 4
+    assert fused(wsb=n - 1) == -13
+    assert lib.attn_decode_fused_workspace_bytes(2, 8, 3, 100, 128) == 0
+    assert lib.attn_decode_fused_workspace_bytes(2, 8, 8, 100, 96) == 0

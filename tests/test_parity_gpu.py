@@ -582,6 +582,57 @@ def test_decode_fp8kv(case):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
+# fused decode (partials and merge in one launch): segments of 128-key chunks
+# merged by the last workgroup of each row
+FUSED_SHAPES = [
+    # B, Hq, Hkv, M, d, dtype
+    (1, 8, 8, 512, 128, "f16"),        # small decode workload
+    (2, 8, 8, 65536, 128, "f16"),      # long decode workload
+    (8, 32, 8, 16384, 128, "bf16"),    # grouped-query decode workload
+    (3, 16, 4, 4097, 64, "f16"),       # a one-key tail chunk
+    (2, 24, 8, 777, 128, "bf16"),      # groups of 3 heads
+    (1, 32, 1, 300, 128, "bf16"),      # a group split over two 16-head slices
+    (2, 16, 4, 1000, 32, "bf16"),
+    (64, 32, 32, 1000, 64, "f16"),     # more rows than the grid: one segment per row
+    (1, 1, 1, 1, 128, "f16"),          # a single key
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_fused(shape):
+    B, Hq, Hkv, M, d, dt = shape
+    say(f"case fused decode {shape}")
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=M + 3)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = attn().attn_decode_fused(q.to(DEV), k.to(DEV), v.to(DEV), scale)
+    torch.cuda.synchronize()
+    Or, Lr, _, _ = oracle.decode_ref(q, k, v, scale, 128)
+    eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+    say(f"  o={eo:.3e} lse={el:.3e}")
+    assert eo <= TOL_O[dt] and el <= TOL_LSE
+
+
+def test_decode_fused_workspace_reuse_and_determinism():
+    """One workspace serves calls of several sizes in a row (each completed
+    call leaves its counters at zero); repeated calls give identical bits."""
+    say("case fused decode workspace reuse")
+    shapes = [(2, 8, 8, 20000, 128, "f16"), (1, 16, 2, 3000, 64, "bf16"), (2, 8, 8, 20000, 128, "f16")]
+    need = max(attn().attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d) for B, Hq, Hkv, M, d, _ in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    outs = []
+    for i, (B, Hq, Hkv, M, d, dt) in enumerate(shapes):
+        q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=40 + (i % 2))
+        scale = float(np.float32(d ** -0.5))
+        o, lse = attn().attn_decode_fused(q.to(DEV), k.to(DEV), v.to(DEV), scale, workspace=ws)
+        torch.cuda.synchronize()
+        Or, Lr, _, _ = oracle.decode_ref(q, k, v, scale, 128)
+        assert maxerr(f64(o), Or) <= TOL_O[dt] and maxerr(f64(lse), Lr) <= TOL_LSE, i
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    n_cnt = 16 * 4  # the first 256 bytes hold the row counters of these shapes
+    assert int(ws[:n_cnt].count_nonzero()) == 0, "counters not reset"
+
+
 @pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
 def test_lse_merge_standalone(C, d, dt):
     say(f"case lse_merge C={C} d={d} {dt}")
