@@ -16,7 +16,7 @@ __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
     "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
-    "attn_decode_fused_workspace_bytes",
+    "attn_decode_fused_workspace_bytes", "attn_decode_fused_noalloc",
 ]
 
 ATTN_F16 = 0
@@ -247,6 +247,43 @@ def attn_decode_fused(q, k, v, scale: float | None = None, o=None, lse=None, ret
                                        workspace.numel(), B, Hq, Hkv, M, d, float(scale), dt, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_fused")
+    return o, lse
+
+
+def attn_decode_fused_noalloc(q, k, v, scale: float | None = None, o=None, lse=None, return_lse: bool = True,
+                              stream=None):
+    """attn_decode_fused on the library's static scratch (no workspace, no
+    device allocation by the library; o and lse are allocated here unless
+    given).  Calls that overlap on one GPU race."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, M, d]")
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, Hkv, M, d))
+    _shape(v, "v", k.shape)
+    _dtype(k, "k", q.dtype)
+    _dtype(v, "v", q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, n)
+    if o is not None:
+        _shape(o, "o", (B, Hq, d))
+        _dtype(o, "o", q.dtype)
+        _contig(o, "o")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq))
+    _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"))
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_decode_fused_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                               lse.data_ptr() if lse is not None else None, B, Hq, Hkv, M, d,
+                                               float(scale), dt, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fused_noalloc")
     return o, lse
 
 

@@ -32,6 +32,8 @@ hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, vo
                                  hipStream_t stream);
 size_t fused_workspace_layout(int B, int Hq, int Hkv, int d, int S, size_t* off_lse, size_t* off_o);
 int fused_segment_cap(int B, int Hq, int Hkv, int M);
+size_t scratch_capacity();
+void* scratch_address();
 }  // namespace attn
 
 namespace {
@@ -75,6 +77,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGNMENT: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scales must be finite and >= 0";
     case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than attn_decode_fused_workspace_bytes";
+    case ATTN_ERR_SCRATCH: return "the call needs more than the library's static scratch (16 MiB)";
     case ATTN_ERR_LAYOUT:
       return "strides must be >= 0 and multiples of 8 elements (k and v: one token stride >= d; paged: "
              "block_size a multiple of 16, 15 * token_stride + d < 2^31)";
@@ -171,6 +174,26 @@ int attn_decode_fused(const void* q, const void* k, const void* v, void* o, floa
       workspace_bytes < attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
     return ATTN_ERR_WORKSPACE;
   return launch_status(attn::decode_fused_dispatch(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, M, d,
+                                                   dtype == ATTN_BF16, scale, stream));
+}
+
+int attn_decode_fused_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                              int Hkv, int M, int d, float scale, attn_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+  if (decode_too_large(B, Hq, M, d, kDecodeChunk)) return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  // the same bound as a caller's workspace, so the outcome does not depend on the GPU
+  if (attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d) > attn::scratch_capacity()) return ATTN_ERR_SCRATCH;
+  void* ws = attn::scratch_address();
+  if (ws == nullptr) return ATTN_ERR_LAUNCH;
+  return launch_status(attn::decode_fused_dispatch(q, k, v, o, lse, ws, attn::scratch_capacity(), B, Hq, Hkv, M, d,
                                                    dtype == ATTN_BF16, scale, stream));
 }
 

@@ -33,6 +33,7 @@
 //    independent loads in flight per thread; the per-thread states of a
 //    column are combined by lane shuffles and one LDS step.
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -1011,6 +1012,38 @@ hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, vo
   ATTN_FUSED_CASE(64, true) ATTN_FUSED_CASE(128, false) ATTN_FUSED_CASE(128, true)
 #undef ATTN_FUSED_CASE
   return hipErrorInvalidValue;
+}
+
+// ---- fused decode without allocation: the library's static scratch ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the workspace of attn_decode_fused_noalloc is this array.  Each
+// GPU the library runs on holds its own copy until the process ends.  Its
+// row counters start at zero (the array is zero-initialised when the code
+// object is loaded) and every completed call sets them back to zero; the
+// partials are written before they are read in every call.  Calls that
+// overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t scratch_capacity() { return kScratchBytes; }
+
+// Device address of the current device's copy of the scratch array, looked
+// up once per device (with that device current) and kept; nullptr if the
+// lookup fails.  Host code passes this address, never the array's name.
+void* scratch_address() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void* v_cache,

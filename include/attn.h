@@ -70,7 +70,9 @@ typedef enum {
   ATTN_ERR_SCALE = -11,         /* scale is negative, infinite or NaN */
   ATTN_ERR_LAYOUT = -12,        /* strides: negative, not a multiple of 8 elements, or k and v
                                    token strides differ or are below d */
-  ATTN_ERR_WORKSPACE = -13      /* workspace NULL, not 16-byte aligned, or too small */
+  ATTN_ERR_WORKSPACE = -13,     /* workspace NULL, not 16-byte aligned, or too small */
+  ATTN_ERR_SCRATCH = -14        /* attn_decode_fused_noalloc: the sizes need more than the
+                                   library's static scratch */
 } attn_status_t;
 
 /*
@@ -187,6 +189,22 @@ int attn_decode_fused(const void* q, const void* k, const void* v, void* o, floa
                       void* workspace, size_t workspace_bytes,
                       int B, int Hq, int Hkv, int M, int d, float scale,
                       attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_fused_noalloc - attn_decode_fused without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The call
+ * allocates nothing: its workspace is a static 16 MiB device array of the
+ * library (one per GPU, held until the process ends), whose counters start
+ * at zero and are set back to zero by every completed call.  Same operation,
+ * arguments, outputs and status codes as attn_decode_fused, plus
+ * ATTN_ERR_SCRATCH when attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d)
+ * exceeds 16 MiB.  All calls on one GPU share the array: calls that may
+ * overlap on one GPU (several streams or threads) race and must not be made.
+ */
+int attn_decode_fused_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int M, int d, float scale,
+                              attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * Paged KV cache for attn_decode_paged_splitkv (the "fmha sm120" page lists

@@ -28,7 +28,8 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
          "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
-         "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused"])
+         "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused",
+         "attn_decode_fused_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -267,3 +268,21 @@ def test_decode_fused_workspace_bytes():
     assert fused(wsb=n - 1) == -13
     assert lib.attn_decode_fused_workspace_bytes(2, 8, 3, 100, 128) == 0
     assert lib.attn_decode_fused_workspace_bytes(2, 8, 8, 100, 96) == 0
+
+
+def noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, Hq=8, Hkv=8, M=65536, d=128, scale=0.088, dtype=0,
+             stream=None)
+    a.update(kw)
+    return _lib.load().attn_decode_fused_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                                 a["M"], a["d"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(M=0), -2), (dict(d=80), -3), (dict(dtype=3), -4),
+    (dict(Hq=8, Hkv=3), -5), (dict(scale=-1.0), -11), (dict(B=70000, Hq=1, Hkv=1), -9), (dict(o=FAKE + 8), -10),
+    # 64 rows of 16 heads, 512 chunks: 64 segments each need 33.8 MB of partials
+    (dict(B=64, Hq=16, Hkv=1), -14),
+])
+def test_decode_fused_noalloc_rejects(kw, code):
+    assert noalloc(**kw) == code
