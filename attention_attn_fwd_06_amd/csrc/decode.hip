@@ -493,12 +493,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     __syncthreads();
     if (!fused_last) return;
     // (head, column quad) pairs, each merged over the row's C segments by SG
-    // threads (segments sg, sg + SG, ...); their states meet in LDS (the K
-    // buffer, free after the last sub-chunk's barriers)
+    // threads (segments sg, sg + SG, ...); their states meet in LDS (the V
+    // buffer, free after the barrier above)
     constexpr int kQuads = D / 4;
     const int pairs = G * kQuads;
     const int SG = pairs >= kDecThreads ? 1 : min(16, kDecThreads / pairs);
-    MergeState* sts = reinterpret_cast<MergeState*>(kbuf);
+    MergeState* sts = reinterpret_cast<MergeState*>(vbuf);
     for (int u = tid; u < pairs * SG; u += kDecThreads) {
       const int p = u % pairs, sg = u / pairs, jj = p / kQuads, quad = p % kQuads;
       MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
@@ -521,6 +521,16 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       if (quad == 0 && fo.lse != nullptr) fo.lse[(int64_t)b * Hq + h0 + jj] = (r.m + log2f(r.s)) * kLn2;
     }
     if (tid == 0) __hip_atomic_store(fo.count + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // contiguous K/V: the item and first key of the K sub-chunk already
+  // fetched ahead (-1: none)
+  int pf_item = -1, pf_key0 = -1;
+  auto fetch_k = [&](const i32x4& desc, int kk) {
+#pragma unroll
+    for (int i = 0; i < kFetch; ++i)
+      dma16<true>(desc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+                  voff_lane + (uint32_t)(kk + kRowsPerInst * i) * (uint32_t)(D * 2));
   };
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -693,10 +703,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           }
         }
       } else {
-#pragma unroll
-        for (int i = 0; i < kFetch; ++i)
-          dma16<true>(kdesc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                      voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+        if (pf_item != item || pf_key0 != key0) fetch_k(kdesc, key0);
 #pragma unroll
         for (int i = 0; i < kFetch; ++i)
           dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
@@ -743,6 +750,18 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       if (g == 0) red[0][wave][j] = mx;
       if constexpr (!KV8) wait_tile_loads();  // this wave's part of the V sub-chunk is in LDS
       __syncthreads();    // V sub-chunk and the per-wave maxima visible
+      if constexpr (!PAGED && !KV8) {
+        // Every wave is done reading K: fetch the item's next sub-chunk of K
+        // now, so that the fetch overlaps this sub-chunk's softmax and P.V
+        // instead of following them.  (Fetching the next item's Q and first
+        // K here as well made the 128-key chunk kernel slower: 92.4 against
+        // 89-90 us on the long decode workload.)
+        if (!last) {
+          pf_item = item;
+          pf_key0 = key0 + kChunk;
+          fetch_k(kdesc, pf_key0);
+        }
+      }
       float m = m_run;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) m = fmaxf(m, red[0][w][j]);

@@ -9,11 +9,17 @@ already resident in HBM.  The decode rotates between two independent K/V sets
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 (4*B*Hq*N*M*d, halved for the causal mask) over the prefill kernel's average
 duration, measured with HIP events on the launch stream; the decode result is
-reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time).  The
-``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8, M=16384,
-d=128, bf16; K/V counted once per kv head), timed separately after the steps, and
-``decode_paged`` / ``decode_fp8kv`` / ``decode_paged_fp8kv`` the same workload's
-chunk kernel through the paged-KV, FP8-KV and paged FP8-KV entry points.
+reported in the ``decode`` object (GB/s of K+V+q+O over chunk + merge time) and
+``decode_fused`` (the same decode in one launch).  ``configs`` holds all five
+workloads (tiny MHA and small decode as latencies, the MHA fp16 d=64 prefill
+as TFLOP/s, the two headline workloads), each with the largest deviation from
+the CPU oracle over its whole output (checked after the timed region).  The
+``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8,
+M=16384, d=128, bf16; K/V counted once per kv head), and ``decode_paged`` /
+``decode_fp8kv`` / ``decode_paged_fp8kv`` the same workload's chunk kernel
+through the paged-KV, FP8-KV and paged FP8-KV entry points.  ``cpu_baseline``
+is the oracle timed on the host on the causal GQA prefill (all of it) and on
+the long decode.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--prewarm-s 1.5] [--no-cpu-baseline]
 """
@@ -36,6 +42,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
 PREFILL = "prefill_causal_gqa_bf16_d128"
 DECODE = "long_decode_fp16_d128"
 DECODE_GQA = "gqa_decode_bf16_d128"
+CONFIGS = {"C1": "tiny_mha_fp16_d64", "C2": "small_decode_fp16_d128", "C3": "prefill_mha_fp16_d64",
+           "C4": PREFILL, "C5": DECODE}
 KERNEL_SOURCES = {
     "prefill": ["attention_attn_fwd_06_amd/csrc/prefill_fwd.hip",
                 "attention_attn_fwd_06_amd/csrc/device_common.h",
@@ -72,35 +80,72 @@ def read_traffic(kind: str, workload: str):
         return None
 
 
-def cpu_baseline(budget_s: float = 15.0):
-    """The oracle, as it stands, on a bounded sample of the prefill workload:
-    whole (batch, head) problems of the causal GQA workload, timed on the host."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+
+def maxerr(a, b) -> float:
+    import numpy as np
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def oracle_checks(attn, dev, timing: bool):
+    """Each of the five workloads once more on the GPU (seed 0), compared with
+    the oracle over its whole output; the oracle runs on the causal GQA
+    prefill and the long decode are timed as the CPU baseline."""
+    import torch
 
     import oracle
-    from workloads import WORKLOADS, attn_flops, make_inputs
-    w = WORKLOADS[PREFILL]
-    q, k, v = make_inputs(w, 0)
-    g = w.Hq // w.Hkv
-    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    rng = np.random.default_rng(0)
-    rng.shuffle(pairs)
-    done, t0 = 0, time.perf_counter()
-    for b, h in pairs:
-        kh = h // g
-        oracle.attn_ref(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, kh:kh + 1], v[b:b + 1, :, kh:kh + 1],
-                        w.scale, w.causal)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = attn_flops(1, done, w.N, w.M, w.d, w.causal)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hq} (batch, head) problems of {w.name} "
-                      f"(full 4096x4096 S and P per problem, float64 numpy), {dt:.1f} s; "
-                      f"FLOPs credited with the causal-halved count"}
+    from workloads import WORKLOADS, attn_flops, decode_bytes, make_inputs
+    res, base = {}, {}
+    for key, name in CONFIGS.items():
+        w = WORKLOADS[name]
+        q, k, v = make_inputs(w, 0)
+        if w.kind == "prefill":
+            o, lse = attn.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal, scale=w.scale)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            Or, Lr = oracle.attn_ref(q, k, v, w.scale, w.causal)
+            dt = time.perf_counter() - t0
+            if name == PREFILL:
+                base["prefill"] = (attn_flops(w.B, w.Hq, w.N, w.M, w.d, w.causal) / dt / 1e12, dt)
+        else:
+            o, lse, _, _ = attn.attn_decode(q.to(dev), k.to(dev), v.to(dev), w.chunk, w.scale)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            Or, Lr, _, _ = oracle.decode_ref(q, k, v, w.scale, w.chunk)
+            dt = time.perf_counter() - t0
+            if name == DECODE:
+                base["decode"] = (decode_bytes(w.B, w.Hq, w.Hkv, w.M, w.d) / dt / 1e9, dt)
+        res[key] = {"max_dO": maxerr(o.float().cpu().double().numpy(), Or),
+                    "max_dlse": maxerr(lse.cpu().double().numpy(), Lr),
+                    "tol_O": 8e-3 if w.dtype == "bf16" else 2e-3, "tol_lse": 1e-3}
+        res[key]["within_tolerance"] = res[key]["max_dO"] <= res[key]["tol_O"] and \
+            res[key]["max_dlse"] <= res[key]["tol_lse"]
+    cpu = None
+    if timing:
+        threads = blas_threads()
+        pw, dw = WORKLOADS[PREFILL], WORKLOADS[DECODE]
+        cpu = {"value": base["prefill"][0], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0)),
+               "sample": f"the whole {pw.name} workload ({pw.B * pw.Hq} (batch, head) problems, full "
+                         f"{pw.N}x{pw.M} S and P each, float64 numpy), {base['prefill'][1]:.1f} s; FLOPs "
+                         f"credited with the causal-halved count",
+               "decode": {"value": base["decode"][0], "unit": "GB/s",
+                          "sample": f"the whole {dw.name} workload ({dw.B * dw.Hq * dw.num_chunks} chunk "
+                                    f"partials and their merge), {base['decode'][1]:.1f} s; bytes = K+V+q+O"}}
+    return res, cpu
 
 
 def gqa_decode_rate(attn, w, args, dev):
@@ -159,6 +204,49 @@ def _time_chunk(fn, args):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     return statistics.mean(a.elapsed_time(b) for a, b in ev)
+
+
+def small_and_mha_rates(attn, args, dev):
+    """The tiny MHA prefill and the small decode (latency-bound: microseconds
+    per call, HIP events around each call) and the MHA fp16 d=64 prefill
+    (TFLOP/s over its kernel time)."""
+    import torch
+    from workloads import WORKLOADS, attn_flops, make_inputs
+    stream = torch.cuda.current_stream()
+    out = {}
+    w1 = WORKLOADS[CONFIGS["C1"]]
+    q, k, v = (t.to(dev) for t in make_inputs(w1, args.seed))
+    o, lse = torch.empty_like(q), torch.empty((w1.B, w1.Hq, w1.N), dtype=torch.float32, device=dev)
+    us = 1e3 * _time_chunk(lambda i: attn.attn_fwd(q, k, v, causal=w1.causal, scale=w1.scale, o=o, lse=lse,
+                                                    stream=stream), args)
+    out["C1"] = {"workload": w1.desc, "us": round(us, 2), "kernel": "prefill_fwd_kernel<64,f16>"}
+    w2 = WORKLOADS[CONFIGS["C2"]]
+    q, k, v = (t.to(dev) for t in make_inputs(w2, args.seed))
+    op = torch.empty((w2.B, w2.Hq, w2.num_chunks, w2.d), dtype=torch.float32, device=dev)
+    lp = torch.empty((w2.B, w2.Hq, w2.num_chunks), dtype=torch.float32, device=dev)
+    o2 = torch.empty((w2.B, w2.Hq, w2.d), dtype=torch.float16, device=dev)
+    l2 = torch.empty((w2.B, w2.Hq), dtype=torch.float32, device=dev)
+
+    def two_launches(i):
+        attn.attn_decode_splitkv(q, k, v, w2.chunk, w2.scale, o_part=op, lse_part=lp, stream=stream)
+        attn.lse_merge(op, lp, o=o2, lse=l2, stream=stream)
+    us2 = 1e3 * _time_chunk(two_launches, args)
+    ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(w2.B, w2.Hq, w2.Hkv, w2.M, w2.d), dtype=torch.uint8,
+                     device=dev)
+    us2f = 1e3 * _time_chunk(lambda i: attn.attn_decode_fused(q, k, v, w2.scale, o=o2, lse=l2, workspace=ws,
+                                                              stream=stream), args)
+    out["C2"] = {"workload": w2.desc, "us_chunk_merge": round(us2, 2), "us_fused": round(us2f, 2)}
+    w3 = WORKLOADS[CONFIGS["C3"]]
+    q, k, v = (t.to(dev) for t in make_inputs(w3, args.seed))
+    o3 = torch.empty_like(q)
+    l3 = torch.empty((w3.B, w3.Hq, w3.N), dtype=torch.float32, device=dev)
+    ms3 = _time_chunk(lambda i: attn.attn_fwd(q, k, v, causal=w3.causal, scale=w3.scale, o=o3, lse=l3,
+                                               stream=stream), args)
+    tf3 = attn_flops(w3.B, w3.Hq, w3.N, w3.M, w3.d, w3.causal) / (ms3 * 1e-3) / 1e12
+    out["C3"] = {"workload": w3.desc, "ms": round(ms3, 4), "TFLOP/s": round(tf3, 2),
+                 "frac": round(tf3 / PEAK_BF16_TFLOPS, 4), "kernel": "prefill_fwd_kernel<64,f16>",
+                 "peak_note": "dense fp16 MFMA peak 2.5 PFLOP/s"}
+    return out
 
 
 def paged_and_fp8_rates(attn, w, args, dev):
@@ -226,8 +314,9 @@ def main():
                     help="seconds of untimed steps before the counted warm-up (clock ramp)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_gqa", "copy"], default=None,
-                    help="run one part only (for counter collection)")
+    ap.add_argument("--no-oracle", action="store_true", help="skip the oracle checks and the CPU baseline")
+    ap.add_argument("--only", choices=["prefill", "prefill_mha", "decode", "decode_fused", "decode_gqa", "copy"],
+                    default=None, help="run one part only (for counter collection)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
@@ -251,6 +340,26 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
+        return
+
+    if args.only == "prefill_mha":
+        # the MHA fp16 d=64 prefill alone (for counter collection)
+        w3 = WORKLOADS[CONFIGS["C3"]]
+        q, k, v = (t.to(dev) for t in make_inputs(w3, args.seed))
+        o3 = torch.empty_like(q)
+        ms3 = _time_chunk(lambda i: attn.attn_fwd(q, k, v, causal=w3.causal, scale=w3.scale, o=o3), args)
+        tf3 = attn_flops(w3.B, w3.Hq, w3.N, w3.M, w3.d, w3.causal) / (ms3 * 1e-3) / 1e12
+        print(json.dumps({"workload": w3.desc, "ms": round(ms3, 4), "TFLOP/s": round(tf3, 2)}), flush=True)
+        return
+    if args.only == "decode_fused":
+        # the fused long decode alone (for counter collection)
+        q, k0, v0 = (t.to(dev) for t in make_inputs(wd, args.seed))
+        _, k1, v1 = (t.to(dev) for t in make_inputs(wd, args.seed + 1))
+        ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d), dtype=torch.uint8,
+                         device=dev)
+        kv = [(k0, v0), (k1, v1)]
+        ms = _time_chunk(lambda i: attn.attn_decode_fused(q, kv[i % 2][0], kv[i % 2][1], wd.scale, workspace=ws), args)
+        print(json.dumps({"workload": wd.desc, "ms": round(ms, 4)}), flush=True)
         return
 
     do_p = args.only in (None, "prefill")
@@ -367,8 +476,21 @@ def main():
         out.update(paged_and_fp8_rates(attn, WORKLOADS[DECODE_GQA], args, dev))
         if args.only == "decode_gqa":
             out["value"], out["unit"], out["dtype"] = out["decode_gqa"]["value"], "GB/s", "bf16"
-    if args.only is None and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+    if args.only is None:
+        cfg = small_and_mha_rates(attn, args, dev)
+        cfg["C4"] = {"workload": wp.desc, "ms": out["prefill_ms"], "TFLOP/s": out["value"],
+                     "frac": out["roofline"]["frac"], "kernel": out["roofline"]["kernel"]}
+        cfg["C5"] = {"workload": wd.desc, "ms_chunk_merge": out["decode"]["chunk_merge_ms"],
+                     "GB/s": out["decode"]["value"], "frac": out["decode"]["frac"],
+                     "ms_fused": out["decode_fused"]["ms"], "GB/s_fused": out["decode_fused"]["value"],
+                     "frac_fused": out["decode_fused"]["frac"]}
+        if not args.no_oracle:
+            checks, cpu = oracle_checks(attn, dev, timing=not args.no_cpu_baseline)
+            for key, r in checks.items():
+                cfg[key].update(r)
+            if cpu is not None:
+                out["cpu_baseline"] = cpu
+        out["configs"] = cfg
     print(json.dumps(out), flush=True)
 
 
