@@ -227,6 +227,33 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const i32x4 vdesc = make_desc(v + b * st.v[0] + kvh * st.v[2], kv_row_stride, M, D);
   const uint32_t voff = F::voff_lane(wave, lane, kv_row_bytes);
 
+  // ---- Q^T operand: lane l of step t holds Q[qw + l%32][16t + 8g .. +7] ----
+  s16x8 qreg[kDT];
+
+  f32x16 acc_o[kDB];
+  float m_run = -INFINITY;  // running max of scale*log2e*s (the reference max)
+  float l_run = 0.f;        // running sum over this lane's keys
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
+
+  // causal: query i sees keys 0 .. i + causal_off (causal_off = M - N >= 0)
+  const int kv_end = CAUSAL ? min(M, q_start + rows + causal_off) : M;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  // last tile that holds a key <= some query of this wave
+  const int wave_tiles = CAUSAL ? min(n_tiles, (qlast + causal_off) / kBN + 1) : n_tiles;
+
+  // ---- prologue: K(0), V(0), K(1) to LDS, Q^T to registers; S(0) ----
+  // The tile fetches go out first, and the Q loads without a branch (a row
+  // past N loads row N-1, whose result is never stored), so that the wait
+  // for all of them starts as early as possible.
+  F::tile(kdesc, kbuf0, 0, wave, voff, kv_row_bytes);
+  F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
+  if (n_tiles > 1) F::tile(kdesc, kbuf0 + kTB, kBN, wave, voff, kv_row_bytes);
+  {
+    const uint16_t* qp = q + b * st.q[0] + (int64_t)min(qi, N - 1) * st.q[1] + h * st.q[2] + 8 * g;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t) qreg[t] = *reinterpret_cast<const s16x8*>(qp + 16 * t);
+  }
   // ---- per-lane LDS operand addresses ----
   LdsAddr<D> la;
   la.k_row = lds0 + (uint32_t)l32 * D * 2;
@@ -250,32 +277,6 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
   }
 
-  // ---- Q^T operand: lane l of step t holds Q[qw + l%32][16t + 8g .. +7] ----
-  s16x8 qreg[kDT];
-
-  f32x16 acc_o[kDB];
-  float m_run = -INFINITY;  // running max of scale*log2e*s (the reference max)
-  float l_run = 0.f;        // running sum over this lane's keys
-#pragma unroll
-  for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
-
-  // causal: query i sees keys 0 .. i + causal_off (causal_off = M - N >= 0)
-  const int kv_end = CAUSAL ? min(M, q_start + rows + causal_off) : M;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
-  // last tile that holds a key <= some query of this wave
-  const int wave_tiles = CAUSAL ? min(n_tiles, (qlast + causal_off) / kBN + 1) : n_tiles;
-
-  // ---- prologue: Q^T to registers, K(0), V(0), K(1) to LDS; S(0) ----
-  {
-    // rows past N are not read (their queries are never stored)
-    const uint16_t* qp = q + b * st.q[0] + (int64_t)qi * st.q[1] + h * st.q[2] + 8 * g;
-#pragma unroll
-    for (int t = 0; t < kDT; ++t)
-      qreg[t] = (qi < N) ? *reinterpret_cast<const s16x8*>(qp + 16 * t) : (s16x8){};
-  }
-  F::tile(kdesc, kbuf0, 0, wave, voff, kv_row_bytes);
-  F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
-  if (n_tiles > 1) F::tile(kdesc, kbuf0 + kTB, kBN, wave, voff, kv_row_bytes);
   wait_tile_loads();
   kv_barrier();
   f32x16 s_a[kKB], s_b[kKB];  // S of the current tile is always in s_a between steps

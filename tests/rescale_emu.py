@@ -66,10 +66,8 @@ def rescale_events(q, k, scale: float, causal: bool, margin: float = 0.05):
                 n_tiles = -(-kv_end // BN)
                 for qw in range(q_start, q_start + rows, WAVE_ROWS):
                     qi = np.arange(qw, qw + WAVE_ROWS)
-                    # rows past N hold q = 0 (their scores are 0, never stored)
-                    Qw = np.zeros((WAVE_ROWS, d))
-                    valid = qi < N
-                    Qw[valid] = q[b, qi[valid], h, :]
+                    # rows past N load row N-1 (their results are never stored)
+                    Qw = q[b, np.minimum(qi, N - 1), h, :]
                     S = Qw @ Kb.T                 # raw scores [32, M]
                     qlast = qw + WAVE_ROWS - 1
                     wave_tiles = min(n_tiles, (qlast + off) // BN + 1) if causal else n_tiles
