@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_decode_splitkv", "lse_merge",
+    "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_fwd_fp8qk", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
     "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
     "attn_decode_fused_workspace_bytes", "attn_decode_fused_noalloc",
@@ -21,6 +21,7 @@ __all__ = [
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
 _DTYPES = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 
 
@@ -143,6 +144,45 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, 
         name = "attn_fwd_strided"
     if st != 0:
         raise AttnError(st, name)
+    return o, lse
+
+
+def attn_fwd_fp8qk(q8, k8, v, q_scale: float, k_scale: float, causal: bool = False, scale: float | None = None,
+                   o=None, lse=None, return_lse: bool = True, stream=None):
+    """Prefill with Q and K as FP8 E4M3 codes (torch.float8_e4m3fn or uint8,
+    contiguous) and per-tensor scales: Q = q_scale * e4m3(q8), K = k_scale *
+    e4m3(k8).  q8 [B,N,Hq,d], k8 [B,M,Hkv,d], v [B,M,Hkv,d] fp16/bf16 ->
+    (o [B,N,Hq,d] v.dtype, lse [B,Hq,N] fp32 or None)."""
+    if q8.dim() != 4 or k8.dim() != 4 or v.dim() != 4:
+        raise ValueError("q8, k8 and v must be 4-D")
+    for t, n in ((q8, "q8"), (k8, "k8")):
+        if t.dtype not in _FP8:
+            raise TypeError(f"{n} must hold E4M3 codes (torch.float8_e4m3fn or uint8)")
+    dt = _dtype_code(v)
+    B, N, Hq, d = q8.shape
+    M, Hkv = k8.shape[1], k8.shape[2]
+    _shape(k8, "k8", (B, M, Hkv, d))
+    _shape(v, "v", k8.shape)
+    for t, n in ((q8, "q8"), (k8, "k8"), (v, "v")):
+        _contig(t, n)
+    if o is not None:
+        _shape(o, "o", (B, N, Hq, d))
+        _dtype(o, "o", v.dtype)
+        _contig(o, "o")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq, N))
+    _devices((q8, "q8"), (k8, "k8"), (v, "v"), (o, "o"), (lse, "lse"))
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty((B, N, Hq, d), dtype=v.dtype, device=v.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=v.device)
+    st = _lib.load().attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, float(q_scale), float(k_scale),
+                                    B, Hq, Hkv, N, M, d, int(bool(causal)), float(scale), dt, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8qk")
     return o, lse
 
 
@@ -285,9 +325,6 @@ def attn_decode_fused_noalloc(q, k, v, scale: float | None = None, o=None, lse=N
     if st != 0:
         raise AttnError(st, "attn_decode_fused_noalloc")
     return o, lse
-
-
-_FP8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,

@@ -30,6 +30,8 @@ SYMBOLS = {
                  + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "attn_fwd_strided": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 7
                          + [ctypes.c_float, ctypes.c_int, ctypes.POINTER(Strides), ctypes.c_void_p]),
+    "attn_fwd_fp8qk": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_float] * 2 + [ctypes.c_int] * 7
+                       + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
                             + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),

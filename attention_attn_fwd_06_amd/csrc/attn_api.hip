@@ -13,6 +13,9 @@ namespace attn {
 hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                             int Hq, int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
                             const attn_strides_t& st, hipStream_t stream);
+hipError_t prefill_fp8qk_dispatch(const void* q8, const void* k8, const void* v, void* o, float* lse, int B, int Hq,
+                                  int Hkv, int N, int M, int d, bool causal, bool bf16, float scale, float q_scale,
+                                  float k_scale, const attn_strides_t& st, hipStream_t stream);
 hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                            int B, int Hq, int Hkv, int M, int d, int chunk, bool bf16, float scale,
                            hipStream_t stream);
@@ -121,6 +124,30 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
     return ATTN_ERR_ALIGNMENT;
   return launch_status(attn::prefill_dispatch(q, k, v, o, lse, B, Hq, Hkv, N, M, d, causal != 0,
                                               dtype == ATTN_BF16, scale, st, stream));
+}
+
+int attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, float* lse, float q_scale, float k_scale,
+                   int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale, attn_dtype_t dtype,
+                   hipStream_t stream) {
+  if (!q8 || !k8 || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (causal && N > M) return ATTN_ERR_CAUSAL_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite(q_scale) || q_scale < 0.f || !std::isfinite(k_scale) ||
+      k_scale < 0.f)
+    return ATTN_ERR_SCALE;
+  const int64_t qn = (int64_t)Hq * d, kn = (int64_t)Hkv * d;
+  // contiguous layouts (element strides; the FP8 elements are bytes)
+  const attn_strides_t st{{N * qn, qn, d}, {M * kn, kn, d}, {M * kn, kn, d}, {N * qn, qn, d}};
+  if ((int64_t)(M + 64) * kn + d >= kMaxElems || (int64_t)B * Hq * ((N + 63) / 64) >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  return launch_status(attn::prefill_fp8qk_dispatch(q8, k8, v, o, lse, B, Hq, Hkv, N, M, d, causal != 0,
+                                                    dtype == ATTN_BF16, scale, q_scale, k_scale, st, stream));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,

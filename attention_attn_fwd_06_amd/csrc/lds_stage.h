@@ -42,6 +42,12 @@ __device__ __forceinline__ i32x4 make_desc(const uint16_t* base, int64_t row_str
   const uint64_t addr = (uint64_t)(uintptr_t)base;
   return (i32x4){(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
+// The same with the row stride and length in bytes (8-bit elements).
+__device__ __forceinline__ i32x4 make_desc_bytes(const uint8_t* base, int64_t row_stride_bytes, int M, int row_bytes) {
+  const int64_t bytes = (int64_t)(M - 1) * row_stride_bytes + row_bytes;
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  return (i32x4){(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
 // The same over M >= 0 rows: with M == 0 the size is 0 and every offset reads as zero.
 __device__ __forceinline__ i32x4 make_desc_rows(const uint16_t* base, int64_t row_stride, int M, int D) {
   const int64_t bytes = M > 0 ? ((int64_t)(M - 1) * row_stride + D) * 2 : 0;

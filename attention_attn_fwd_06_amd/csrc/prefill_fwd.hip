@@ -137,23 +137,60 @@ struct LdsAddr {
   uint32_t v[D / 32][2];  // lds base + V row/chunk offset for (d block, row half)
 };
 
+// Geometry of the S^T = K Q^T operands.  16-bit Q and K: one
+// v_mfma_f32_32x32x16 per 16 head-dim elements.  FP8 Q and K (QK8, E4M3 codes):
+// one v_mfma_f32_32x32x64_f8f6f4 per 64 head-dim bytes; a K row of D bytes is
+// stored, swizzled and fetched exactly like a 16-bit row of D / 2 elements,
+// and FP8 step u reads the two 16-byte chunks that the 16-bit kernel reads at
+// its steps 2u and 2u + 1 (so the conflict-free read pattern is the same).
+// The Q operand of a lane holds the same chunks of its query row in the same
+// order, so each contraction slot pairs equal head-dim indices of q and k.
+typedef short s16x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <int D, bool QK8>
+struct QkGeom {
+  static constexpr int kDK = QK8 ? D / 2 : D;          // K row in LDS as 16-bit elements
+  static constexpr int kSteps = QK8 ? D / 64 : D / 16;  // QK MFMAs per 32-key block
+  using Op = typename std::conditional<QK8, s16x16, s16x8>::type;  // Q or K operand of one MFMA
+};
+
+template <bool BF16, bool QK8, typename Op>
+__device__ __forceinline__ f32x16 qk_mfma(const Op& a, const Op& b, f32x16 c) {
+  if constexpr (QK8)
+    // format code 0 for both operands: FP8 E4M3; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                           c, 0, 0, 0, 0, 0, 0);
+  else
+    return mfma32x32x16<BF16>(a, b, c);
+}
+
+// K operand of QK step t at a K row address (k_row + k_tile + block offset,
+// with the per-lane chunk XOR kx): one 16-byte read, or two for FP8.
+template <int D, bool QK8>
+__device__ __forceinline__ typename QkGeom<D, QK8>::Op k_operand(uint32_t kx, uint32_t base, int t) {
+  if constexpr (QK8) {
+    const s16x8 lo = lds_read_b128(base + ((uint32_t)(64 * t) ^ kx));
+    const s16x8 hi = lds_read_b128(base + ((uint32_t)(64 * t + 32) ^ kx));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  } else {
+    return lds_read_b128(base + ((uint32_t)(32 * t) ^ kx));
+  }
+}
+
 // S^T[kb] = K(tile) Q^T for the wave's 32 queries (first tile, diagonal and
 // tail tiles).  qreg[t]: this lane's Q^T operand of contraction step t.
-template <int D, bool BF16>
+template <int D, bool BF16, bool QK8>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint32_t k_row, uint32_t kx,
-                                        const s16x8 (&qreg)[D / 16]) {
-  constexpr int kDT = D / 16;
+                                        const typename QkGeom<D, QK8>::Op (&qreg)[QkGeom<D, QK8>::kSteps]) {
+  using Gq = QkGeom<D, QK8>;
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
-  for (int t = 0; t < kDT; ++t) {
-    // k_row + (32t ^ kx): k_row is a multiple of 128 and 32t ^ kx < 128 * D / 64
-    const uint32_t row_t = k_row + ((uint32_t)(32 * t) ^ kx);
-    const s16x8 bq = qreg[t];
+  for (int t = 0; t < Gq::kSteps; ++t) {
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
-      const s16x8 a = lds_read_b128(row_t + k_tile + (uint32_t)(kb * 32 * D * 2));
-      s[kb] = mfma32x32x16<BF16>(a, bq, s[kb]);
+      const auto a = k_operand<D, QK8>(kx, k_row + k_tile + (uint32_t)(kb * 32 * Gq::kDK * 2), t);
+      s[kb] = qk_mfma<BF16, QK8>(a, qreg[t], s[kb]);
     }
   }
 }
@@ -175,21 +212,27 @@ struct TileDecode {
   int pack_shift;              // log2 of the query heads per workgroup
 };
 
-template <int D, bool BF16, bool CAUSAL>
+// QK8: q and k hold FP8 E4M3 codes (byte strides in st.q and st.k) and
+// scale_log2 carries their per-tensor scales; v and o are 16-bit.
+template <int D, bool BF16, bool CAUSAL, bool QK8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
-void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
                         int n_qtiles, int total, TileDecode td, int causal_off, attn_strides_t st,
                         float scale_log2) {
-  constexpr int kDT = D / 16;  // contraction steps of QK^T
+  using Gq = QkGeom<D, QK8>;
+  constexpr int kDT = Gq::kSteps;  // contraction steps of QK^T
   constexpr int kDB = D / 32;  // 32-row blocks of O^T
-  constexpr uint32_t kTB = kBN * D * 2;  // bytes of one K or V tile
+  constexpr uint32_t kTBK = kBN * Gq::kDK * 2;  // bytes of one K tile
+  constexpr uint32_t kTB = kBN * D * 2;         // bytes of one V tile
+  using FK = Fetch<Gq::kDK>;
   using F = Fetch<D>;
-  // LDS: K buffers 0, 1, V buffers 0, 1 (64 KB at d = 128).
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * kBN * D];
+  constexpr int kEB = QK8 ? 1 : 2;  // bytes per q or k element
+  // LDS: K buffers 0, 1, V buffers 0, 1 (64 KB at d = 128; 48 KB with FP8 K).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(2 * kTBK + 2 * kTB) / 2];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u16*)smem;
-  const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTB;
+  const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTBK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -221,14 +264,18 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int qi = qw + l32;             // this lane's query
 
   // element strides {batch, token, head}; k and v share their token stride
+  // (in elements; FP8 k elements are bytes)
   const int64_t kv_row_stride = st.k[1];
   const int kv_row_bytes = (int)(kv_row_stride * 2);
-  const i32x4 kdesc = make_desc(k + b * st.k[0] + kvh * st.k[2], kv_row_stride, M, D);
+  const int k_row_bytes = (int)(kv_row_stride * kEB);
+  const i32x4 kdesc = make_desc_bytes(static_cast<const uint8_t*>(k) + (b * st.k[0] + kvh * st.k[2]) * kEB,
+                                      k_row_bytes, M, D * kEB);
   const i32x4 vdesc = make_desc(v + b * st.v[0] + kvh * st.v[2], kv_row_stride, M, D);
   const uint32_t voff = F::voff_lane(wave, lane, kv_row_bytes);
+  const uint32_t voffk = QK8 ? FK::voff_lane(wave, lane, k_row_bytes) : voff;
 
   // ---- Q^T operand: lane l of step t holds Q[qw + l%32][16t + 8g .. +7] ----
-  s16x8 qreg[kDT];
+  typename Gq::Op qreg[kDT];
 
   f32x16 acc_o[kDB];
   float m_run = -INFINITY;  // running max of scale*log2e*s (the reference max)
@@ -246,18 +293,29 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // The tile fetches go out first, and the Q loads without a branch (a row
   // past N loads row N-1, whose result is never stored), so that the wait
   // for all of them starts as early as possible.
-  F::tile(kdesc, kbuf0, 0, wave, voff, kv_row_bytes);
+  FK::tile(kdesc, kbuf0, 0, wave, voffk, k_row_bytes);
   F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
-  if (n_tiles > 1) F::tile(kdesc, kbuf0 + kTB, kBN, wave, voff, kv_row_bytes);
+  if (n_tiles > 1) FK::tile(kdesc, kbuf0 + kTBK, kBN, wave, voffk, k_row_bytes);
   {
-    const uint16_t* qp = q + b * st.q[0] + (int64_t)min(qi, N - 1) * st.q[1] + h * st.q[2] + 8 * g;
+    // lane half g holds head-dim chunks 2t + g (16 bytes each) of step t
+    // (FP8: chunks 4t + g and 4t + 2 + g, as the K operand)
+    const uint8_t* qp = static_cast<const uint8_t*>(q) +
+                        (b * st.q[0] + (int64_t)min(qi, N - 1) * st.q[1] + h * st.q[2]) * kEB + 16 * g;
 #pragma unroll
-    for (int t = 0; t < kDT; ++t) qreg[t] = *reinterpret_cast<const s16x8*>(qp + 16 * t);
+    for (int t = 0; t < kDT; ++t) {
+      if constexpr (QK8) {
+        const s16x8 lo = *reinterpret_cast<const s16x8*>(qp + 64 * t);
+        const s16x8 hi = *reinterpret_cast<const s16x8*>(qp + 64 * t + 32);
+        qreg[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      } else {
+        qreg[t] = *reinterpret_cast<const s16x8*>(qp + 32 * t);
+      }
+    }
   }
   // ---- per-lane LDS operand addresses ----
   LdsAddr<D> la;
-  la.k_row = lds0 + (uint32_t)l32 * D * 2;
-  la.kx = (uint32_t)((g ^ swz<D>(l32)) << 4);
+  la.k_row = lds0 + (uint32_t)l32 * Gq::kDK * 2;
+  la.kx = (uint32_t)((g ^ swz<Gq::kDK>(l32)) << 4);
   {
     // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
     // of the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of
@@ -280,7 +338,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   wait_tile_loads();
   kv_barrier();
   f32x16 s_a[kKB], s_b[kKB];  // S of the current tile is always in s_a between steps
-  qk_tile<D, BF16>(s_a, 0, la.k_row, la.kx, qreg);
+  qk_tile<D, BF16, QK8>(s_a, 0, la.k_row, la.kx, qreg);
   kv_barrier();  // K buffer 0 is refilled in iteration 0
 
   // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks; v_tile
@@ -358,11 +416,11 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // bf16: P is split into hi + lo parts on the first tile
     constexpr bool kSplit = BF16 && kFirst;
     const uint32_t par = (uint32_t)(j & 1);
-    const uint32_t k_next = (1 - par) * kTB, v_cur = par * kTB;
+    const uint32_t k_next = (1 - par) * kTBK, v_cur = par * kTB;
     const int n0 = j * kBN;
-    if (j + 2 < n_tiles) F::tile(kdesc, kbuf0 + par * kTB, n0 + 2 * kBN, wave, voff, kv_row_bytes);
+    if (j + 2 < n_tiles) FK::tile(kdesc, kbuf0 + par * kTBK, n0 + 2 * kBN, wave, voffk, k_row_bytes);
     if (j + 1 < n_tiles) F::tile(vdesc, vbuf0 + (1 - par) * kTB, n0 + kBN, wave, voff, kv_row_bytes);
-    if (j + 1 < wave_tiles) qk_tile<D, BF16>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
+    if (j + 1 < wave_tiles) qk_tile<D, BF16, QK8>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
     if (j < wave_tiles) {
       const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw + causal_off) || (n0 + kBN > M);
       if (need_mask) {
@@ -441,10 +499,11 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const uint32_t kbase = opaque(la.k_row + k_next);
     constexpr int kNQ = 2 * kDT, kNP = 4 * kDB, kN = kNQ + kNP;
     constexpr int kL = 4;                  // MFMAs whose operands are read ahead
-    constexpr int kNF = 2 * F::kInst;      // tile fetch instructions per step
+    constexpr int kNF = F::kInst + FK::kInst;  // tile fetch instructions per step
     constexpr int kExpEnd = kNQ + 3 * kDB;  // first PV MFMA of the last k-step
-    static_assert(kNQ >= 2 * kNF, "fetch slots");
-    s16x8 qv[kDT], ka[kNQ], va[kNP], pb[4];
+    static_assert(kN >= 2 * kNF, "fetch slots");
+    typename Gq::Op qv[kDT], ka[kNQ];
+    s16x8 va[kNP], pb[4];
     float pe[4][8];
     float lsum = 0.f, mxn = -INFINITY;
     const float neg_m = (kFirst && m_run == -INFINITY) ? 0.f : -m_run;
@@ -453,8 +512,12 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       if (i < kNQ) {
         const int t = i >> 1, kb = i & 1;
         if (kb == 0) qv[t] = qreg[t];
-        const uint32_t row_t = xor_add(kx, (uint32_t)(32 * t), kbase);
-        ka[i] = lds_read_b128(row_t + (uint32_t)(kb * 32 * D * 2));
+        if constexpr (QK8) {
+          ka[i] = k_operand<D, QK8>(kx, kbase + (uint32_t)(kb * 32 * Gq::kDK * 2), t);
+        } else {
+          const uint32_t row_t = xor_add(kx, (uint32_t)(32 * t), kbase);
+          ka[i] = lds_read_b128(row_t + (uint32_t)(kb * 32 * D * 2));
+        }
       } else if (i < kN) {
         const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
         const uint32_t koff = v_cur + (uint32_t)(16 * ks * D * 2);  // keys 16 ks .. 16 ks + 15
@@ -485,7 +548,7 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       __builtin_amdgcn_sched_barrier(0);
       if (i < kNQ) {
         const int t = i >> 1, kb = i & 1;
-        s_next[kb] = mfma32x32x16<BF16>(ka[i], qv[t], t == 0 ? (f32x16){} : s_next[kb]);
+        s_next[kb] = qk_mfma<BF16, QK8>(ka[i], qv[t], t == 0 ? (f32x16){} : s_next[kb]);
       } else {
         const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
         acc_o[db] = mfma32x32x16<BF16>(va[pi], pb[ks], acc_o[db]);
@@ -516,21 +579,25 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   auto step_fast_p = [&](const int j, f32x16 (&s_cur)[kKB], f32x16 (&s_next)[kKB], float& mx, auto parity,
                          auto first) {
     constexpr int P = decltype(parity)::value;
-    const uint32_t k_fill = kbuf0 + P * kTB, v_fill = vbuf0 + (1 - P) * kTB;
+    const uint32_t k_fill = kbuf0 + P * kTBK, v_fill = vbuf0 + (1 - P) * kTB;
     const int n0 = j * kBN;
     // j + 1 < wave_tiles <= n_tiles, so V(j+1) exists; without a K(j+2) the K
-    // slots repeat the V(j+1) fetches (same bytes to the same place)
-    const bool has_k = j + 2 < n_tiles;
+    // slots repeat the V(j+1) fetches (same bytes to the same place).  With
+    // FP8 K (other fetch geometry) K(j+2) is fetched anyway: the K buffer is
+    // free, and rows past M read as zeros.
+    const bool has_k = QK8 || j + 2 < n_tiles;
     const i32x4 d2 = has_k ? kdesc : vdesc;
     const uint32_t l2 = has_k ? k_fill : v_fill;
     const int r2 = has_k ? n0 + 2 * kBN : n0 + kBN;
     auto fetch = [&](int i) {
       if (i < F::kInst)
         F::issue(vdesc, v_fill, n0 + kBN, i, wave, voff, kv_row_bytes);
+      else if constexpr (QK8)
+        FK::issue(kdesc, k_fill, n0 + 2 * kBN, i - F::kInst, wave, voffk, k_row_bytes);
       else
         F::issue(d2, l2, r2, i - F::kInst, wave, voff, kv_row_bytes);
     };
-    step_fast((1 - P) * kTB, P * kTB, s_cur, s_next, mx, fetch, first);
+    step_fast((1 - P) * kTBK, P * kTB, s_cur, s_next, mx, fetch, first);
     wait_tile_loads();
     kv_barrier();
   };
@@ -607,10 +674,10 @@ void prefill_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   if (lse != nullptr && g == 0 && qi < N) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
-// Host-side launcher (one instance per head dim, dtype and mask).
-template <int D, bool BF16, bool CAUSAL>
+// Host-side launcher (one instance per head dim, dtype, mask and Q/K format).
+template <int D, bool BF16, bool CAUSAL, bool QK8>
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          int Hkv, int N, int M, float scale, const attn_strides_t& st, hipStream_t stream) {
+                          int Hkv, int N, int M, float scale_log2, const attn_strides_t& st, hipStream_t stream) {
   // query heads per workgroup: the largest power of two that divides the GQA
   // group and leaves at least 64 rows (one K/V tile) per head
   const int group = Hq / Hkv;
@@ -629,15 +696,17 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
   while ((1 << pack_shift) < pack) ++pack_shift;
   const TileDecode td{fast_div((uint32_t)(group / pack)), fast_div((uint32_t)n_qtiles), fast_div((uint32_t)Hkv),
                       group, pack_shift};
-  return launch(&prefill_fwd_kernel<D, BF16, CAUSAL>, dim3(total), dim3(kThreads), stream, q, k, v, o, lse, N, M,
-                Hq, Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, st, scale * kLog2e);
+  return launch(&prefill_fwd_kernel<D, BF16, CAUSAL, QK8>, dim3(total), dim3(kThreads), stream, q, k, v, o, lse, N,
+                M, Hq, Hkv, n_qtiles, total, td, CAUSAL ? M - N : 0, st, scale_log2);
 }
 
 hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                             int Hkv, int N, int M, int d, bool causal, bool bf16, float scale,
                             const attn_strides_t& st, hipStream_t stream) {
+  const float sl2 = scale * kLog2e;
 #define ATTN_PREFILL_CASE(DD, BB, CC) \
-  if (d == DD && bf16 == BB && causal == CC) return launch_prefill<DD, BB, CC>(q, k, v, o, lse, B, Hq, Hkv, N, M, scale, st, stream);
+  if (d == DD && bf16 == BB && causal == CC) \
+    return launch_prefill<DD, BB, CC, false>(q, k, v, o, lse, B, Hq, Hkv, N, M, sl2, st, stream);
   ATTN_PREFILL_CASE(32, false, false)
   ATTN_PREFILL_CASE(32, false, true)
   ATTN_PREFILL_CASE(32, true, false)
@@ -651,6 +720,27 @@ hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o
   ATTN_PREFILL_CASE(128, true, false)
   ATTN_PREFILL_CASE(128, true, true)
 #undef ATTN_PREFILL_CASE
+  return hipErrorInvalidValue;
+}
+
+// Q and K as FP8 E4M3 codes with per-tensor scales: the scores are
+// scale * q_scale * k_scale * (codes' values), folded into one factor.
+hipError_t prefill_fp8qk_dispatch(const void* q8, const void* k8, const void* v, void* o, float* lse, int B, int Hq,
+                                  int Hkv, int N, int M, int d, bool causal, bool bf16, float scale, float q_scale,
+                                  float k_scale, const attn_strides_t& st, hipStream_t stream) {
+  const float sl2 = scale * q_scale * k_scale * kLog2e;
+#define ATTN_FP8QK_CASE(DD, BB, CC) \
+  if (d == DD && bf16 == BB && causal == CC) \
+    return launch_prefill<DD, BB, CC, true>(q8, k8, v, o, lse, B, Hq, Hkv, N, M, sl2, st, stream);
+  ATTN_FP8QK_CASE(64, false, false)
+  ATTN_FP8QK_CASE(64, false, true)
+  ATTN_FP8QK_CASE(64, true, false)
+  ATTN_FP8QK_CASE(64, true, true)
+  ATTN_FP8QK_CASE(128, false, false)
+  ATTN_FP8QK_CASE(128, false, true)
+  ATTN_FP8QK_CASE(128, true, false)
+  ATTN_FP8QK_CASE(128, true, true)
+#undef ATTN_FP8QK_CASE
   return hipErrorInvalidValue;
 }
 

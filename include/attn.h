@@ -7,6 +7,8 @@
  *                        and probability matrices never reach HBM ("fmha sm120: beyond
  *                        torch.sdpa", section 1 "flash attention" and section 2 "fmha
  *                        implementation").
+ *   attn_fwd_fp8qk       attn_fwd with Q and K as FP8 E4M3 codes and per-tensor scales
+ *                        (Q K^T on the FP8 matrix cores).
  *   attn_decode_splitkv  Flash-Decoding step 1: per-chunk partial outputs O_c and
  *                        log-sum-exp lse_c of a single query ("CUDA Flash Decoding",
  *                        section 2.2, step 1).
@@ -121,6 +123,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
                      attn_dtype_t dtype, const attn_strides_t* strides, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8qk - attn_fwd with Q and K given as FP8 E4M3 codes and one fp32
+ * scale each (fp8 attention, listed as future work on the "fmha sm120" page,
+ * which fixes no format; the format is the library's).
+ *
+ *   q8  [B, N, Hq, d]   E4M3 codes, read     o   [B, N, Hq, d]  dtype, written
+ *   k8  [B, M, Hkv, d]  E4M3 codes, read     lse [B, Hq, N]     fp32, written (may be NULL)
+ *   v   [B, M, Hkv, d]  dtype (fp16/bf16), read
+ *
+ * The queries and keys are Q = q_scale * e4m3(q8) and K = k_scale * e4m3(k8)
+ * (OCP E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 is NaN); the result is attn_fwd on Q, K and v:
+ * O = softmax(scale * Q K^T [+ causal mask]) V and its lse, with the masks,
+ * layouts, outputs and errors of attn_fwd.  Q K^T runs on the FP8 matrix
+ * cores (products of E4M3 values are exact, accumulation fp32); the softmax
+ * and P V are those of the 16-bit path.  Requires d in {64, 128} (else
+ * ATTN_ERR_HEAD_DIM) and finite scales >= 0 (else ATTN_ERR_SCALE).
+ */
+int attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, float* lse,
+                   float q_scale, float k_scale,
+                   int B, int Hq, int Hkv, int N, int M, int d, int causal, float scale,
+                   attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes - bytes of fp32 partials that one split-KV decode call

@@ -11,8 +11,8 @@ Every function here is pinned by tests outside this package (brute force on
 tiny inputs, a library special case, closed forms and invariants); there is no
 "parity unpinned" function.
 """
-from .attention import (attn_ref, decode_fp8kv_partials_ref, decode_fp8kv_ref, decode_partials_ref, decode_ref,
+from .attention import (attn_fp8qk_ref, attn_ref, decode_fp8kv_partials_ref, decode_fp8kv_ref, decode_partials_ref, decode_ref,
                         e4m3_decode, lse_merge_ref, paged_decode_partials_ref, paged_decode_ref)
 
 __all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref", "paged_decode_partials_ref",
-           "paged_decode_ref", "e4m3_decode", "decode_fp8kv_partials_ref", "decode_fp8kv_ref"]
+           "paged_decode_ref", "e4m3_decode", "decode_fp8kv_partials_ref", "decode_fp8kv_ref", "attn_fp8qk_ref"]

@@ -43,13 +43,17 @@ notes of the repository):
     the plain decode.  E4M3 (OCP "e4m3fn"): sign bit, 4 exponent bits with bias
     7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN;
     there are no infinities.
+  * FP8 attention (the same TODO item; no format on the pages): Q and K given
+    as E4M3 codes with one fp32 scale each, Q = q_scale * e4m3(q),
+    K = k_scale * e4m3(k), V in 16 bits; the result is the plain attention of
+    these values (the kernel's products of E4M3 values are exact).
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["attn_ref", "decode_partials_ref", "lse_merge_ref", "decode_ref", "paged_decode_partials_ref",
-           "paged_decode_ref", "e4m3_decode", "decode_fp8kv_partials_ref", "decode_fp8kv_ref"]
+           "paged_decode_ref", "e4m3_decode", "decode_fp8kv_partials_ref", "decode_fp8kv_ref", "attn_fp8qk_ref"]
 
 
 def _f64(x) -> np.ndarray:
@@ -244,3 +248,12 @@ def decode_fp8kv_ref(q, k_codes, v_codes, k_scale: float, v_scale: float, scale:
     o_part, lse_part = decode_fp8kv_partials_ref(q, k_codes, v_codes, k_scale, v_scale, scale, chunk)
     O, lse = lse_merge_ref(o_part, lse_part)
     return O, lse, o_part, lse_part
+
+
+def attn_fp8qk_ref(q_codes, k_codes, v, q_scale: float, k_scale: float, scale: float, causal: bool = False):
+    """Attention with Q and K given as E4M3 codes and fp32 scales: the
+    forward of Q = q_scale * e4m3(q_codes), K = k_scale * e4m3(k_codes) and V.
+    Returns (O, lse) as ``attn_ref``."""
+    q = e4m3_decode(q_codes) * float(np.float32(q_scale))
+    k = e4m3_decode(k_codes) * float(np.float32(k_scale))
+    return attn_ref(q, k, v, scale, causal)

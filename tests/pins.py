@@ -395,6 +395,30 @@ def check_fp8kv_decode_is_decode_of_scaled_values(ora):
     _close(op, opr, what="fp8 kv partials")
 
 
+def check_fp8qk_is_attention_of_scaled_values(ora):
+    """FP8 Q/K attention equals torch's float64 SDPA on torch's decoding of the
+    codes times the scales (causal GQA and non-causal MHA)."""
+    lib = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double()
+    g = np.random.default_rng(410)
+    for B, N, M, Hq, Hkv, d, causal in [(1, 9, 9, 4, 2, 8, True), (2, 5, 11, 2, 2, 6, False)]:
+        qc = g.integers(0, 256, (B, N, Hq, d)).astype(np.uint8)
+        kc = g.integers(0, 256, (B, M, Hkv, d)).astype(np.uint8)
+        qc[(qc & 0x7F) >= 0x60] &= 0x3F     # no NaN codes, moderate magnitudes
+        kc[(kc & 0x7F) >= 0x60] &= 0x3F
+        v = _rand((B, M, Hkv, d), 411)
+        qs, ks = float(np.float32(0.03)), float(np.float32(0.05))
+        O, L = ora.attn_fp8qk_ref(qc, kc, v, qs, ks, 0.7, causal)
+        qd, kd = (lib(qc) * qs).numpy(), (lib(kc) * ks).numpy()
+        _close(O, _sdpa(qd, kd, v, 0.7, causal), what=f"fp8 qk output {causal}")
+        # lse: torch's logsumexp of the masked scores of the decoded values
+        qt = torch.from_numpy(qd).permute(0, 2, 1, 3)
+        kt = torch.from_numpy(kd).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+        S = 0.7 * qt @ kt.transpose(-1, -2)
+        if causal:
+            S = S.masked_fill(torch.arange(M)[None, :] > torch.arange(N)[:, None] + (M - N), float("-inf"))
+        _close(L, torch.logsumexp(S, dim=-1).numpy(), what=f"fp8 qk lse {causal}")
+
+
 FAST_CHECKS = [
     check_brute_prefill_tiny, check_brute_decode_tiny, check_sdpa,
     check_identity_v_rows_are_probabilities, check_constant_v, check_single_key,
@@ -402,7 +426,7 @@ FAST_CHECKS = [
     check_gqa_is_repeated_mha, check_decode_is_single_query_attention,
     check_merge_identities, check_two_keys_closed_form, check_causal_chunk_is_tail_of_full,
     check_paged_decode_is_decode_of_gathered_keys, check_paged_decode_variable_lengths,
-    check_e4m3_decode, check_fp8kv_decode_is_decode_of_scaled_values,
+    check_e4m3_decode, check_fp8kv_decode_is_decode_of_scaled_values, check_fp8qk_is_attention_of_scaled_values,
 ]
 
 

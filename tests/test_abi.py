@@ -29,7 +29,7 @@ def test_header_declares_expected_api():
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
          "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
          "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused",
-         "attn_decode_fused_noalloc"])
+         "attn_decode_fused_noalloc", "attn_fwd_fp8qk"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -286,3 +286,20 @@ def noalloc(**kw):
 ])
 def test_decode_fused_noalloc_rejects(kw, code):
     assert noalloc(**kw) == code
+
+
+def fp8qk(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, qs=0.01, ks=0.02, B=1, Hq=4, Hkv=2, N=128, M=128, d=128,
+             causal=1, scale=0.088, dtype=1, stream=None)
+    a.update(kw)
+    return _lib.load().attn_fwd_fp8qk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["qs"], a["ks"], a["B"], a["Hq"],
+                                      a["Hkv"], a["N"], a["M"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(N=0), -2), (dict(d=32), -3), (dict(d=256), -3), (dict(dtype=4), -4),
+    (dict(Hq=6, Hkv=4), -5), (dict(causal=1, N=256, M=128), -6), (dict(qs=-1.0), -11), (dict(ks=float("nan")), -11),
+    (dict(scale=float("inf")), -11), (dict(M=1 << 23, Hkv=2), -9), (dict(k=FAKE + 8), -10), (dict(lse=FAKE + 2), -10),
+])
+def test_fwd_fp8qk_rejects(kw, code):
+    assert fp8qk(**kw) == code

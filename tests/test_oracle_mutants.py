@@ -45,6 +45,10 @@ MUTANTS = {
     "fp8kv_k_scale_dropped": ("k = e4m3_decode(k_codes) * float(np.float32(k_scale))", "k = e4m3_decode(k_codes)"),
     "fp8kv_scales_swapped": ("v = e4m3_decode(v_codes) * float(np.float32(v_scale))",
                              "v = e4m3_decode(v_codes) * float(np.float32(k_scale))"),
+    "fp8qk_q_scale_dropped": ("q = e4m3_decode(q_codes) * float(np.float32(q_scale))", "q = e4m3_decode(q_codes)"),
+    "fp8qk_k_scale_squared": ("k = e4m3_decode(k_codes) * float(np.float32(k_scale))",
+                              "k = e4m3_decode(k_codes) * float(np.float32(k_scale)) ** 2"),
+    "fp8qk_causal_dropped": ("return attn_ref(q, k, v, scale, causal)\n", "return attn_ref(q, k, v, scale, False)\n"),
 }
 
 

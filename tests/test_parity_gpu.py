@@ -16,7 +16,7 @@ import torch
 import oracle
 from tests.rescale_emu import rescale_events
 from tests.test_rescale_cases import RESCALE_CASES, rescale_case_inputs
-from workloads import WORKLOADS, decode_inputs, make_inputs, prefill_inputs, torch_dtype
+from workloads import WORKLOADS, decode_inputs, make_inputs, prefill_fp8qk_inputs, prefill_inputs, torch_dtype
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -165,6 +165,47 @@ def test_prefill_rescale_branch(case):
     assert ev["fast"] > 0 and ev["general"] > 0, ev
     say(f"  rescale events: steady-state {ev['fast']}, general {ev['general']}, largest jump {ev['max_jump']:.1f}")
     check_prefill(q, k, v, causal, scale, dt, label=f"rescale {case}")
+
+
+# FP8 Q and K (E4M3 codes, per-tensor scales), 16-bit V: the oracle is the
+# attention of the decoded values times the scales
+FP8QK_SHAPES = [
+    # B, N, M, Hq, Hkv, d, dtype (of v and o), causal
+    (1, 128, 128, 2, 2, 64, "f16", False),
+    (2, 300, 300, 8, 2, 128, "bf16", True),
+    (1, 257, 257, 6, 2, 64, "bf16", True),
+    (1, 200, 333, 4, 4, 128, "f16", False),
+    (2, 64, 200, 8, 2, 128, "bf16", True),
+    (1, 1, 1, 1, 1, 64, "f16", False),
+    (2, 1024, 1024, 8, 2, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("shape", FP8QK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_fp8qk(shape):
+    B, N, M, Hq, Hkv, d, dt, causal = shape
+    say(f"case fp8 qk prefill {shape}")
+    q8, k8, v, qs, ks = prefill_fp8qk_inputs(B, Hq, Hkv, N, M, d, dt, seed=N + M + d)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = attn().attn_fwd_fp8qk(q8.to(DEV), k8.to(DEV), v.to(DEV), qs, ks, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attn_fp8qk_ref(q8.numpy(), k8.numpy(), v, qs, ks, scale, causal)
+    eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+    say(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O[dt] and el <= TOL_LSE
+
+
+def test_prefill_fp8qk_causal_gqa_full_size_whole():
+    """The causal GQA d=128 workload's shape with FP8 Q and K, whole output."""
+    w = WORKLOADS["prefill_causal_gqa_bf16_d128"]
+    say("case fp8 qk prefill, causal GQA workload shape (whole output)")
+    q8, k8, v, qs, ks = prefill_fp8qk_inputs(w.B, w.Hq, w.Hkv, w.N, w.M, w.d, "bf16", seed=0)
+    o, lse = attn().attn_fwd_fp8qk(q8.to(DEV), k8.to(DEV), v.to(DEV), qs, ks, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attn_fp8qk_ref(q8.numpy(), k8.numpy(), v, qs, ks, w.scale, True)
+    eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+    say(f"  max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE
 
 
 def test_prefill_causal_chunk_matches_full_rows():

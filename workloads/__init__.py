@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "prefill_inputs", "decode_inputs",
-    "make_inputs", "attn_flops", "decode_bytes", "torch_dtype", "prefill_ramp_inputs",
+    "make_inputs", "attn_flops", "decode_bytes", "torch_dtype", "prefill_ramp_inputs", "prefill_fp8qk_inputs",
+    "e4m3_codes",
 ]
 
 
@@ -126,6 +127,29 @@ def prefill_ramp_inputs(B, Hq, Hkv, N, M, d, dtype="f16", seed=0, a=4.0, slope=6
     k = gk + ramp * u
     v = v_scale * gv
     return tuple(x.to(torch_dtype(dtype)) for x in (q, k, v))
+
+
+def e4m3_codes(x: torch.Tensor):
+    """Per-tensor quantisation to OCP FP8 E4M3 codes, as a caller would do it:
+    scale = max|x| / 448 (rounded to fp32), codes = round-to-nearest-even of
+    x / scale in E4M3 (torch's float8_e4m3fn conversion), as uint8.  Returns
+    (codes, scale)."""
+    scale = float(np.float32(float(x.abs().max()) / 448.0)) or 1.0
+    codes = (x.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def prefill_fp8qk_inputs(B, Hq, Hkv, N, M, d, dtype="bf16", seed=0):
+    """q, k, v drawn as ``prefill_inputs`` (float32 before rounding); q and k
+    quantised to E4M3 codes with per-tensor scales (``e4m3_codes``), v rounded
+    to ``dtype``.  Returns (q8, k8, v, q_scale, k_scale)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, N, Hq, d), dtype=torch.float32, generator=g)
+    k = torch.randn((B, M, Hkv, d), dtype=torch.float32, generator=g)
+    v = torch.randn((B, M, Hkv, d), dtype=torch.float32, generator=g)
+    q8, qs = e4m3_codes(q)
+    k8, ks = e4m3_codes(k)
+    return q8, k8, v.to(torch_dtype(dtype)), qs, ks
 
 
 def make_inputs(w: Workload, seed: int = 0):
