@@ -47,6 +47,7 @@ constexpr int kDecodeChunkMax = 8192;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
+bool valid_prefill_head_dim(int d) { return valid_head_dim(d) || d == 256; }
 bool valid_dtype(int dt) { return dt == ATTN_F16 || dt == ATTN_BF16; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
@@ -70,7 +71,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
     case ATTN_ERR_BAD_DIMENSION: return "a size argument is not positive";
-    case ATTN_ERR_HEAD_DIM: return "head dimension must be 32, 64 or 128";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (prefill: 32, 64, 128, 256; FP8 prefill: 64, 128; decode: 32, 64, 128)";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
     case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N <= M (bottom-right mask)";
@@ -93,7 +94,7 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
                      const attn_strides_t* strides, hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_prefill_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (causal && N > M) return ATTN_ERR_CAUSAL_SHAPE;

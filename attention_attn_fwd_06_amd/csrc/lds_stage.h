@@ -22,11 +22,14 @@ namespace attn {
 //    bit 2;
 //  d = 32 (64-byte rows, four per bank row): swz = (row/4)%4 permutes 0..3
 //    over the 4 rows of one residue mod 4 among 16 consecutive rows; 4
-//    consecutive rows fill one bank row whatever the swizzle.
+//    consecutive rows fill one bank row whatever the swizzle;
+//  d = 256 (512-byte rows, two bank rows each): the d = 128 swizzle on the
+//    low four chunk bits (a chunk's bank group is its index mod 16), so both
+//    reads see the same bank groups as at d = 128.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(D == 32 || D == 64 || D == 128, "head dims with a swizzle");
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dims with a swizzle");
+  if constexpr (D == 128 || D == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
   else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   else return (row >> 2) & 3;
 }

@@ -62,8 +62,12 @@
 namespace attn {
 
 constexpr int kBN = 64;            // keys per K/V tile
-constexpr int kWavesPerEU = 2;     // waves per SIMD
 constexpr int kWaves = 4;          // waves per workgroup
+// Waves per SIMD: two workgroups per CU (256 registers per wave), or at
+// d = 256 one (the wave needs more than 256 registers: 128 for O^T alone,
+// and the 128 KB of K/V tiles leave room for one workgroup per CU).
+template <int D>
+constexpr int waves_per_eu() { return D == 256 ? 1 : 2; }
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = kWaves * 32;   // queries per workgroup (32 per wave)
@@ -73,28 +77,37 @@ constexpr int kBM = kWaves * 32;   // queries per workgroup (32 per wave)
 // chunk that belongs at unit L (physical chunk pc of row r holds logical chunk
 // pc ^ swz<D>(r)).  Instruction i of wave w covers units (i*kWaves + w)*64 ..
 // +63, i.e. rows kRowsPerInst*i + (w*64 + L)/kU; the row-in-instruction part
-// and the chunk are per-lane constants (voff_lane below), since kRowsPerInst
-// is a multiple of the swizzle period (16 rows).
+// and the chunk are per-lane constants (voff_lane below).  When kRowsPerInst
+// is a multiple of the swizzle period (16 rows) one offset serves every
+// instruction; at d = 256 (8 rows per instruction index) odd instructions
+// take a second one.
 template <int D>
 struct Fetch {
   static constexpr int kU = D / 8;                          // 16-byte units per row
   static constexpr int kInst = kBN * kU / kThreads;         // instructions per wave per tile
   static constexpr int kRowsPerInst = kWaves * 64 / kU;     // rows covered by one instruction index
   static constexpr uint32_t kInstBytes = 64 * 16;           // LDS bytes written per instruction
+  static constexpr int kVar = (kInst == 1 || kRowsPerInst % 16 == 0) ? 1 : 16 / kRowsPerInst;
   static_assert(kBN * kU % kThreads == 0, "tile must split evenly over the workgroup");
-  static_assert(kInst == 1 || kRowsPerInst % 16 == 0, "swizzle must repeat across instructions");
-  // per-lane byte offset of instruction 0 relative to the tile's first row
-  static __device__ __forceinline__ uint32_t voff_lane(int wave, int lane, int row_stride_bytes) {
+  static_assert(kVar == 1 || 16 % kRowsPerInst == 0, "swizzle must repeat across instructions");
+  struct Voff {
+    uint32_t v[kVar];  // per-lane byte offsets of instructions 0 .. kVar-1 (then repeating)
+  };
+  static __device__ __forceinline__ Voff voff_lane(int wave, int lane, int row_stride_bytes) {
     const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
-    return (uint32_t)rl * (uint32_t)row_stride_bytes + (uint32_t)((pc ^ swz<D>(rl)) * 16);
+    Voff o;
+#pragma unroll
+    for (int x = 0; x < kVar; ++x)
+      o.v[x] = (uint32_t)rl * (uint32_t)row_stride_bytes + (uint32_t)((pc ^ swz<D>(rl + kRowsPerInst * x)) * 16);
+    return o;
   }
   // instruction i of the tile starting at key row n0, into the LDS tile at lds_tile
   static __device__ __forceinline__ void issue(i32x4 desc, uint32_t lds_tile, int n0, int i, int wave,
-                                               uint32_t voff, int row_stride_bytes) {
+                                               const Voff& voff, int row_stride_bytes) {
     dma16(desc, lds_tile + (uint32_t)(i * kWaves + wave) * kInstBytes,
-          voff + (uint32_t)(n0 + kRowsPerInst * i) * (uint32_t)row_stride_bytes);
+          voff.v[i % kVar] + (uint32_t)(n0 + kRowsPerInst * i) * (uint32_t)row_stride_bytes);
   }
-  static __device__ __forceinline__ void tile(i32x4 desc, uint32_t lds_tile, int n0, int wave, uint32_t voff,
+  static __device__ __forceinline__ void tile(i32x4 desc, uint32_t lds_tile, int n0, int wave, const Voff& voff,
                                               int row_stride_bytes) {
 #pragma unroll
     for (int i = 0; i < kInst; ++i) issue(desc, lds_tile, n0, i, wave, voff, row_stride_bytes);
@@ -215,7 +228,7 @@ struct TileDecode {
 // QK8: q and k hold FP8 E4M3 codes (byte strides in st.q and st.k) and
 // scale_log2 carries their per-tensor scales; v and o are 16-bit.
 template <int D, bool BF16, bool CAUSAL, bool QK8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>(), waves_per_eu<D>())))
 void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                         float* __restrict__ lse, int N, int M, int Hq, int Hkv,
@@ -271,8 +284,8 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   const i32x4 kdesc = make_desc_bytes(static_cast<const uint8_t*>(k) + (b * st.k[0] + kvh * st.k[2]) * kEB,
                                       k_row_bytes, M, D * kEB);
   const i32x4 vdesc = make_desc(v + b * st.v[0] + kvh * st.v[2], kv_row_stride, M, D);
-  const uint32_t voff = F::voff_lane(wave, lane, kv_row_bytes);
-  const uint32_t voffk = QK8 ? FK::voff_lane(wave, lane, k_row_bytes) : voff;
+  const auto voff = F::voff_lane(wave, lane, kv_row_bytes);
+  const auto voffk = FK::voff_lane(wave, lane, k_row_bytes);  // the same values without QK8
 
   // ---- Q^T operand: lane l of step t holds Q[qw + l%32][16t + 8g .. +7] ----
   typename Gq::Op qreg[kDT];
@@ -719,6 +732,10 @@ hipError_t prefill_dispatch(const void* q, const void* k, const void* v, void* o
   ATTN_PREFILL_CASE(128, false, true)
   ATTN_PREFILL_CASE(128, true, false)
   ATTN_PREFILL_CASE(128, true, true)
+  ATTN_PREFILL_CASE(256, false, false)
+  ATTN_PREFILL_CASE(256, false, true)
+  ATTN_PREFILL_CASE(256, true, false)
+  ATTN_PREFILL_CASE(256, true, true)
 #undef ATTN_PREFILL_CASE
   return hipErrorInvalidValue;
 }

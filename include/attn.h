@@ -61,7 +61,9 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL_POINTER = -1,   /* a required pointer is NULL */
   ATTN_ERR_BAD_DIMENSION = -2,  /* a size is <= 0 */
-  ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not in {32, 64, 128} */
+  ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not supported by the call (attn_fwd:
+                                   {32, 64, 128, 256}; attn_fwd_fp8qk: {64, 128}; decode and
+                                   merge: {32, 64, 128}) */
   ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
@@ -100,7 +102,7 @@ typedef struct {
  * of the key sequence (a chunk of a longer prefill), so the last query sees every
  * key; for N == M this is the page's top-left mask.  Causal requires N <= M;
  * O = softmax(S) V row by row, and lse[b,h,i] = ln sum_j exp(S_ij) (natural log,
- * including the row maximum).  Requires d in {32, 64, 128}, Hq % Hkv == 0, a finite
+ * including the row maximum).  Requires d in {32, 64, 128, 256}, Hq % Hkv == 0, a finite
  * scale >= 0, (M+64)*Hkv*d below 2^31 (one batch's K or V, read with 32-bit
  * offsets) and B*Hq*ceil(N/64) below 2^31; q, o and lse have no size limit
  * of their own (64-bit offsets).

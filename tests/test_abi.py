@@ -64,7 +64,7 @@ def fwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
     (dict(B=0), -2), (dict(Hq=-1), -2), (dict(Hkv=0), -2), (dict(N=0), -2), (dict(M=-5), -2), (dict(d=0), -2),
-    (dict(d=96), -3), (dict(d=256), -3), (dict(d=16), -3),
+    (dict(d=96), -3), (dict(d=512), -3), (dict(d=16), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4),
     (dict(Hq=6, Hkv=4), -5),
     (dict(causal=1, N=256, M=128), -6),
@@ -144,7 +144,7 @@ def dec(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1),
     (dict(M=0), -2), (dict(chunk=0), -2), (dict(B=-1), -2),
-    (dict(d=80), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
+    (dict(d=80), -3), (dict(d=256), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
     (dict(chunk=64), -7), (dict(chunk=192), -7), (dict(chunk=8320), -7),
     (dict(scale=-1.0), -11),
     (dict(B=70000, Hq=1, Hkv=1, M=128), -9),

@@ -108,6 +108,12 @@ SHAPES = [
     (2, 300, 300, 8, 2, 32, "bf16", True),
     (1, 70, 530, 4, 1, 32, "f16", True),
     (1, 1, 1, 1, 1, 32, "bf16", False),
+    # head dim 256 (one wave per SIMD, 128 KB of K/V tiles)
+    (1, 200, 333, 4, 4, 256, "f16", False),
+    (2, 300, 300, 8, 2, 256, "bf16", True),
+    (1, 64, 530, 4, 1, 256, "bf16", True),
+    (1, 1, 1, 1, 1, 256, "f16", True),
+    (1, 1024, 1024, 4, 2, 256, "bf16", True),
 ]
 
 
