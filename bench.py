@@ -47,10 +47,12 @@ CONFIGS = {"C1": "tiny_mha_fp16_d64", "C2": "small_decode_fp16_d128", "C3": "pre
 KERNEL_SOURCES = {
     "prefill": ["attention_attn_fwd_06_amd/csrc/prefill_fwd.hip",
                 "attention_attn_fwd_06_amd/csrc/device_common.h",
-                "attention_attn_fwd_06_amd/csrc/lds_stage.h"],
+                "attention_attn_fwd_06_amd/csrc/lds_stage.h",
+                "attention_attn_fwd_06_amd/csrc/launch.h"],
     "decode": ["attention_attn_fwd_06_amd/csrc/decode.hip",
                "attention_attn_fwd_06_amd/csrc/device_common.h",
-               "attention_attn_fwd_06_amd/csrc/lds_stage.h"],
+               "attention_attn_fwd_06_amd/csrc/lds_stage.h",
+               "attention_attn_fwd_06_amd/csrc/launch.h"],
 }
 
 
@@ -247,6 +249,26 @@ def small_and_mha_rates(attn, args, dev):
                  "frac": round(tf3 / PEAK_BF16_TFLOPS, 4), "kernel": "prefill_fwd_kernel<64,f16>",
                  "peak_note": "dense fp16 MFMA peak 2.5 PFLOP/s"}
     return out
+
+
+def fp8qk_rate(attn, args, dev):
+    """The causal GQA d=128 workload with Q and K as FP8 E4M3 codes (bf16 V):
+    TFLOP/s over the kernel time.  Half of the FLOPs (Q K^T) run on the FP8
+    matrix cores (5.0 PFLOP/s dense), half (P V) on the bf16 ones (2.5), so the
+    peak for this mix is 1 / (0.5 / 5.0 + 0.5 / 2.5) = 3.33 PFLOP/s."""
+    import torch
+    from workloads import WORKLOADS, attn_flops, prefill_fp8qk_inputs
+    w = WORKLOADS[PREFILL]
+    q8, k8, v, qs, ks = (t.to(dev) if hasattr(t, "to") else t for t in
+                         prefill_fp8qk_inputs(w.B, w.Hq, w.Hkv, w.N, w.M, w.d, "bf16", args.seed))
+    o = torch.empty((w.B, w.N, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    ms = _time_chunk(lambda i: attn.attn_fwd_fp8qk(q8, k8, v, qs, ks, causal=True, scale=w.scale, o=o, lse=lse), args)
+    tf = attn_flops(w.B, w.Hq, w.N, w.M, w.d, w.causal) / (ms * 1e-3) / 1e12
+    mixed_peak = 1.0 / (0.5 / 5000.0 + 0.5 / PEAK_BF16_TFLOPS)
+    return {"workload": w.desc.replace("bf16", "FP8 E4M3 Q/K, bf16 V"), "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "frac_of_mixed_peak": round(tf / mixed_peak, 4),
+            "kernel": "prefill_fwd_kernel<128,bf16,causal,fp8qk>"}
 
 
 def paged_and_fp8_rates(attn, w, args, dev):
@@ -478,6 +500,7 @@ def main():
             out["value"], out["unit"], out["dtype"] = out["decode_gqa"]["value"], "GB/s", "bf16"
     if args.only is None:
         cfg = small_and_mha_rates(attn, args, dev)
+        out["prefill_fp8qk"] = fp8qk_rate(attn, args, dev)
         cfg["C4"] = {"workload": wp.desc, "ms": out["prefill_ms"], "TFLOP/s": out["value"],
                      "frac": out["roofline"]["frac"], "kernel": out["roofline"]["kernel"]}
         cfg["C5"] = {"workload": wd.desc, "ms_chunk_merge": out["decode"]["chunk_merge_ms"],
