@@ -283,7 +283,30 @@ struct FusedOut {
   int n_chunks;      // 128-key chunks per row, ceil(M / 128)
 };
 
-constexpr int kPRow = kChunk + 8;    // P row stride in elements (16-byte pad)
+// LDS service model of gfx950 (measured with rocprofv3's SQ_LDS_BANK_CONFLICT
+// on single-wave probes): reads serve 256 bytes a cycle over 64 four-byte
+// banks, ds_read_b128 in four 16-lane groups (within each 32-lane half, the
+// 4-lane quads whose index has even, resp. odd, bit parity), ds_read_b64 and
+// ds_read_b64_tr_b16 in the two 32-lane halves; writes serve 128 bytes a cycle
+// over 32 banks, ds_write_b128 in groups of 8 consecutive lanes.  A group is
+// conflict-free when its lanes touch distinct banks (or the same address).
+//
+// P^T in LDS: per part (hi, lo) 16 rows (query heads) of 128 16-bit slots,
+// 256 bytes per row; 16-byte unit u of row j sits at unit u ^ j.  Slots
+// 32w .. 32w + 31 hold wave w's keys, in the order the P.V contraction uses:
+// slot 32w + 8 * perm4(g) + 4 kb + r holds key 32w + 16 kb + 4 g + r, so the
+// QK lane (j, g) writes its 8 values with one 16-byte store.
+constexpr int kPRow = kChunk;  // P row in 16-bit elements
+__device__ __forceinline__ int perm4(int g) { return ((g & 1) << 1) | (g >> 1); }  // swaps 1 and 2
+// Contraction chunk of QK step s for lane group g (16-byte chunks of d): both
+// operands read it, so any bijection is valid; this one makes the K and Q
+// reads (16 rows x 4 chunks, rows swizzled by swz<D>) conflict-free under the
+// ds_read_b128 lane groups.
+template <int D>
+__device__ __forceinline__ int qk_chunk(int s, int g) {
+  constexpr int kS = D / 32, kX = D == 32 ? 2 : (D == 64 ? 1 : 0);
+  return (kS * g + s) ^ ((g & 1) ? kX : 0);
+}
 constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
 
 template <int D, bool BF16, bool PAGED, bool KV8, bool FUSED = false>
@@ -332,20 +355,21 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       PAGED ? (uint32_t)((int64_t)(lane / kU) * pk.token_stride * 2) + (uint32_t)((pc ^ swz<D>(rl)) << 4) : 0u;
   // V^T operand: in each 16-lane group of a ds_read_b64_tr_b16, lane s
   // addresses V[K0 + s/4][D0 + 4*(s%4)], so lane i receives V[K0 + 0..3][D0 + i].
-  // Group g reads keys 32*ks + 8*g + 4*hh + 0..3 (k-step ks, half hh): slots
-  // 8g .. 8g + 7 of the k-step, the same key order the P^T read uses.
+  // Group g fills slots 8g .. 8g + 7 of k-step ks: keys 32 ks + 4 perm4(g) +
+  // 16 hh + 0..3 for half hh, the slot order of P^T.
   uint32_t va[kDB][2];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int row = 8 * g + 4 * hh + (j >> 2);
+      const int row = 4 * perm4(g) + 16 * hh + (j >> 2);
       const int col = 16 * (wave * kDB + db) + 4 * (j & 3);
       va[db][hh] = v_lds + (uint32_t)(row * D * 2 + ((((col >> 3) ^ swz<D>(row)) << 4) | ((col & 7) * 2)));
     }
   }
-  const uint32_t pa = p_lds + (uint32_t)((j * kPRow + 8 * g) * 2);               // P[j][32ks + 8g ..]
-  const uint32_t pw = p_lds + (uint32_t)((j * kPRow + 32 * wave + 4 * g) * 2);   // P[j][32w + 16kb + 4g ..]
+  // P^T row j: read unit 4 ks + g (slots 32ks + 8g ..), written unit 4 w + perm4(g)
+  const uint32_t p_row = p_lds + (uint32_t)(j * kPRow * 2);
+  const uint32_t pw = p_row + (uint32_t)(((4 * wave + perm4(g)) ^ j) << 4);
 
   // paged: the page ids of the next sub-chunk (and, across items, the next
   // sequence length) are loaded right after the current fetches are issued,
@@ -377,6 +401,12 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // from a safe address and is converted as zeros).
   constexpr int kPR8 = D / 16;                       // 16-byte pieces per FP8 row
   constexpr int kPieces8 = kChunk * kPR8 / kDecThreads;
+  // Piece u of a sub-chunk is piece u % kPR8 of row piece_row(u): the row
+  // index u / kPR8 with bit 2 flipped when bit 2 of u is set.  Each group of 8
+  // consecutive lanes (one ds_write_b128 cycle) then writes two rows whose
+  // swizzles differ in their low bit, so its 16-byte units land on 8 distinct
+  // bank groups; a wave's 64 pieces still cover whole consecutive rows.
+  auto piece_row = [](int u) { return (u / kPR8) ^ (((u >> 2) & 1) << 2); };
   uint4 kr8[kPieces8], vr8[kPieces8];
   int kv8_item = -1, kv8_key0 = 0;
   uint32_t kv8_ok = 0;
@@ -390,7 +420,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   auto lookup8 = [&](int bb, int kk) {
 #pragma unroll
     for (int p = 0; p < kPieces8; ++p) {
-      const int key = kk + (p * kDecThreads + tid) / kPR8;
+      const int key = kk + piece_row(p * kDecThreads + tid);
       const int e = min(key / pk.block_size, pk.max_blocks - 1);
       pg8[p] = pk.block_table[(int64_t)bb * pk.max_blocks + e];
     }
@@ -404,7 +434,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       // zeroes it.  An out-of-range page id reads offset 0 (page 0 exists).
 #pragma unroll
       for (int p = 0; p < kPieces8; ++p) {
-        const int u = p * kDecThreads + tid, key = kk + u / kPR8;
+        const int u = p * kDecThreads + tid, key = kk + piece_row(u);
         const bool ok = pg8[p] >= 0 && pg8[p] < pk.num_blocks;
         const int64_t off = ok ? (int64_t)pg8[p] * pk.page_stride + (int64_t)kvhh * pk.head_stride +
                                      (int64_t)(key % pk.block_size) * pk.token_stride + 16 * (u % kPR8)
@@ -418,7 +448,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       const int64_t base = ((int64_t)bb * Hkv + kvhh) * M * D;
 #pragma unroll
       for (int p = 0; p < kPieces8; ++p) {
-        const int u = p * kDecThreads + tid, row = u / kPR8;
+        const int u = p * kDecThreads + tid, row = piece_row(u);
         const bool ok = kk + row < M;
         const int64_t off = base + (ok ? (int64_t)(kk + row) * D + 16 * (u % kPR8) : 0);
         kv8_ok |= (uint32_t)ok << p;
@@ -613,7 +643,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             nx_seq = seq_len(nt_b);
           }
         }
-        auto put = [&](uint32_t base, const uint4& w, int row, int pc8) {
+        // u: the piece's index in the sub-chunk
+        auto put = [&](uint32_t base, const uint4& w, int u) {
+          const int row = piece_row(u), pc8 = u % kPR8;
           const uint32_t* b4 = reinterpret_cast<const uint32_t*>(&w);
           uint32_t h[8];
 #pragma unroll
@@ -635,9 +667,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         for (int p = 0; p < kPieces8; ++p) {
           const int u = p * kDecThreads + tid;
           // a row that does not exist, or lies past the sequence's end
-          const bool bad = !((ok8 >> p) & 1u) || (PAGED && key0 + u / kPR8 >= seq);
-          put(k_lds, bad ? zero4 : kr8[p], u / kPR8, u % kPR8);
-          put(v_lds, bad ? zero4 : vr8[p], u / kPR8, u % kPR8);
+          const bool bad = !((ok8 >> p) & 1u) || (PAGED && key0 + piece_row(u) >= seq);
+          put(k_lds, bad ? zero4 : kr8[p], u);
+          put(v_lds, bad ? zero4 : vr8[p], u);
         }
         if (key0 == c * chunk && tid < kGqaCols * kU)  // Q, before q8 is reloaded below
           *(lds_u32x4*)(uintptr_t)(q_lds + (uint32_t)tid * 16u) = (u32x4){q8.x, q8.y, q8.z, q8.w};
@@ -717,13 +749,13 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       else wait_vm<kFetch>();  // this wave's Q and K fetches have landed (V may not)
       __syncthreads();    // Q and K visible
 
-      // A operand of S^T: K row 32w + 16kb + j, d = 32s + 8g .. +7; B operand:
-      // q of head h0 + j, same d.  Logical chunk 4s + g of a row whose swizzle
-      // is swz(j) (rows of a 16-row block share their low four bits with j).
+      // A operand of S^T: K row 32w + 16kb + j, d chunk qk_chunk(s, g); B
+      // operand: q of head h0 + j, same d.  The row's swizzle is swz(j) (rows
+      // of a 16-row block share their low four bits with j).
       s16x8 ka[2][kS], qb[kS];
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
-        const uint32_t cx = (uint32_t)(((4 * s + g) ^ swz<D>(j)) << 4);
+        const uint32_t cx = (uint32_t)((qk_chunk<D>(s, g) ^ swz<D>(j)) << 4);
         qb[s] = lds_read_b128(q_lds + (uint32_t)(j * D * 2) + cx);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -769,6 +801,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       m_run = m;
 
       float lsum = 0.f;
+      uint32_t pwh[4], pwl[4];  // this lane's 8 P slots, hi and lo parts
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float p[4];
@@ -779,11 +812,13 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         }
         const uint32_t h01 = pack2<BF16>(p[0], p[1]), h23 = pack2<BF16>(p[2], p[3]);
         const f32x2 r01 = unpack2<BF16>(h01), r23 = unpack2<BF16>(h23);
-        const uint32_t l01 = pack2<BF16>(p[0] - r01[0], p[1] - r01[1]);
-        const uint32_t l23 = pack2<BF16>(p[2] - r23[0], p[3] - r23[1]);
-        lds_write_b64(pw + 32u * kb, (u32x2){h01, h23});
-        lds_write_b64(pw + kPBytes + 32u * kb, (u32x2){l01, l23});
+        pwh[2 * kb] = h01;
+        pwh[2 * kb + 1] = h23;
+        pwl[2 * kb] = pack2<BF16>(p[0] - r01[0], p[1] - r01[1]);
+        pwl[2 * kb + 1] = pack2<BF16>(p[2] - r23[0], p[3] - r23[1]);
       }
+      *(lds_u32x4*)(uintptr_t)pw = (u32x4){pwh[0], pwh[1], pwh[2], pwh[3]};
+      *(lds_u32x4*)(uintptr_t)(pw + kPBytes) = (u32x4){pwl[0], pwl[1], pwl[2], pwl[3]};
       lsum += __shfl_xor(lsum, 16);
       lsum = sum_xor32(lsum);
       l_w = fmaf(l_w, alpha, lsum);
@@ -795,8 +830,9 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks) {
         if (wave >= kPVWaves) break;
-        const s16x8 ph = lds_read_b128(pa + 64u * ks);
-        const s16x8 pl = lds_read_b128(pa + kPBytes + 64u * ks);
+        const uint32_t pr = p_row + (uint32_t)(((4 * ks + g) ^ j) << 4);
+        const s16x8 ph = lds_read_b128(pr);
+        const s16x8 pl = lds_read_b128(pr + kPBytes);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const s16x4 lo = lds_read_tr16_b64(va[db][0] + (uint32_t)(32 * ks * D * 2));
