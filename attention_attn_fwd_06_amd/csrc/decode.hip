@@ -283,6 +283,18 @@ struct FusedOut {
   int n_chunks;      // 128-key chunks per row, ceil(M / 128)
 };
 
+// Two E4M3 codes (bytes 0, 1 of w, or 2, 3 with HI) to two 16-bit values in
+// one instruction.  The scale operand is 1: every E4M3 value (normal,
+// subnormal or zero) is exact in fp16 and in bf16, so the result is the exact
+// decode; NaN codes give NaN.
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_16(uint32_t w) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.f, HI));
+}
+
 // LDS service model of gfx950 (measured with rocprofv3's SQ_LDS_BANK_CONFLICT
 // on single-wave probes): reads serve 256 bytes a cycle over 64 four-byte
 // banks, ds_read_b128 in four 16-lane groups (within each 32-lane half, the
@@ -650,10 +662,8 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           uint32_t h[8];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b4[t], true);
-            h[2 * t] = pack2<BF16>(lo[0], lo[1]);
-            h[2 * t + 1] = pack2<BF16>(hi[0], hi[1]);
+            h[2 * t] = e4m3x2_to_16<BF16, false>(b4[t]);
+            h[2 * t + 1] = e4m3x2_to_16<BF16, true>(b4[t]);
           }
 #pragma unroll
           for (int half = 0; half < 2; ++half) {

@@ -167,7 +167,7 @@ def lse_merge_ref(o_part, lse_part):
     """
     o_part, lse_part = _f64(o_part), _f64(lse_part)
     mx = np.max(lse_part, axis=-1, keepdims=True)
-    empty = ~np.isfinite(mx)
+    empty = mx == -np.inf           # all partials -inf: no key (NaN partials stay NaN)
     mx_safe = np.where(empty, 0.0, mx)
     with np.errstate(divide="ignore"):
         g = np.where(empty, -np.inf, mx_safe + np.log(np.sum(np.exp(lse_part - mx_safe), axis=-1, keepdims=True)))

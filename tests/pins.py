@@ -295,6 +295,10 @@ def check_merge_identities(ora):
     assert Le[0] == -np.inf, f"empty-row merge lse {Le[0]}"
     _close(Oe[1], o2[0], what="merge with one empty chunk")
     _close(Le[1], 0.3, what="merge with one empty chunk lse")
+    # a NaN partial is not an empty row: NaN propagates to O and lse
+    with np.errstate(invalid="ignore"):
+        On, Ln = ora.lse_merge_ref(o2[None], np.array([[np.nan, -np.inf]]))
+    assert np.isnan(Ln[0]) and np.all(np.isnan(On[0])), f"NaN partial merged as {On[0]}, {Ln[0]}"
 
 
 def check_two_keys_closed_form(ora):

@@ -33,7 +33,8 @@ MUTANTS = {
                              "s = (k[b, kh, lo:hi, :] @ q[b, h, :])"),
     "merge_weights_unnormalised": ("np.exp(lse_part - np.where(empty, 0.0, g))", "np.exp(lse_part - mx_safe)"),
     "merge_lse_without_max": ("mx_safe + np.log(np.sum(", "np.log(np.sum("),
-    "merge_empty_row_nan": ("empty = ~np.isfinite(mx)", "empty = np.zeros_like(mx, dtype=bool)"),
+    "merge_empty_row_nan": ("empty = mx == -np.inf", "empty = np.zeros_like(mx, dtype=bool)"),
+    "merge_nan_row_as_empty": ("empty = mx == -np.inf", "empty = ~np.isfinite(mx)"),
     "merge_plain_average": ("O = np.sum(w[..., None] * o_part, axis=-2)", "O = np.mean(o_part, axis=-2)"),
     "paged_row_shifted": ("pages, rows = bt[b, t // bs], t % bs", "pages, rows = bt[b, t // bs], (t + 1) % bs"),
     "paged_page_in_order": ("pages, rows = bt[b, t // bs], t % bs", "pages, rows = t // bs, t % bs"),

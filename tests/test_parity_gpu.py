@@ -629,6 +629,38 @@ def test_decode_fp8kv(case):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_decode_fp8kv_every_code(dt):
+    """Every E4M3 code through the kernel's conversion, exactly: one key per
+    sequence, so o = v_scale * e4m3(v) (each code is exact in 16 bits) and,
+    with one-hot queries, lse = scale * k_scale * e4m3(k) of one column.  NaN
+    codes (S.1111.111) give NaN where the oracle's arithmetic does: a NaN in
+    V only in its column, a NaN anywhere in a key row in every head's score."""
+    say(f"case fp8 kv decode, every code, {dt}")
+    B, Hq, d = 16, 16, 128
+    codes = np.arange(256, dtype=np.uint8)
+    vc = np.stack([np.roll(codes, -d * b)[:d] for b in range(B)]).reshape(B, 1, 1, d)
+    kc = np.zeros((B, 1, 1, d), np.uint8)
+    for b in range(B):
+        kc[b, 0, 0, :16] = codes[16 * b:16 * b + 16]     # head h reads column h
+    q = torch.zeros((B, Hq, d), dtype=torch_dtype(dt))
+    for h in range(Hq):
+        q[:, h, h] = 1.0
+    ks, vs, scale = 0.5, 1.0, 0.125
+    o, lse, op, lp = attn().attn_decode_fp8kv(q.to(DEV), torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                                              ks, vs, 128, scale)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        Or, Lr, _, _ = oracle.decode_fp8kv_ref(q, kc, vc, ks, vs, scale, 128)
+    O, L = f64(o), f64(lse)
+    assert np.array_equal(np.isnan(O), np.isnan(Or)) and np.array_equal(np.isnan(L), np.isnan(Lr))
+    assert np.isnan(Lr).sum() == 2 * Hq and np.isnan(Or).sum() == 2 * Hq * d + (B - 2) * Hq   # the pins above
+    fin = ~np.isnan(Or)
+    assert np.array_equal(O[fin], Or[fin])                # exact: e4m3 values are 16-bit values
+    ok = ~np.isnan(Lr)
+    assert np.max(np.abs(L[ok] - Lr[ok])) <= 1e-6 * np.max(np.abs(Lr[ok]))
+
+
 # fused decode (partials and merge in one launch): segments of 128-key chunks
 # merged by the last workgroup of each row
 FUSED_SHAPES = [
