@@ -182,12 +182,19 @@ def gqa_decode_rate(attn, w, args, dev):
     torch.cuda.synchronize()
     c_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
     cm_ms = statistics.mean(e[0].elapsed_time(e[2]) for e in events)
+    # the same decode in one launch (partials of 128-key chunk runs and their merge)
+    ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(w.B, w.Hq, w.Hkv, w.M, w.d), dtype=torch.uint8,
+                     device=dev)
+    f_ms = _time_chunk(lambda i: attn.attn_decode_fused(q, kv[i % 2][0], kv[i % 2][1], w.scale, o=o, lse=lse,
+                                                        workspace=ws), args)
     nbytes = decode_bytes(w.B, w.Hq, w.Hkv, w.M, w.d)
     chunk_bytes = nbytes - w.B * w.Hq * w.d * 2
     gbps = nbytes / (cm_ms * 1e-3) / 1e9
+    f_gbps = nbytes / (f_ms * 1e-3) / 1e9
     return {"workload": w.desc, "value": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "chunk_merge_ms": round(cm_ms, 4), "chunk_ms": round(c_ms, 4),
             "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
+            "fused_ms": round(f_ms, 4), "fused_GBps": round(f_gbps, 1), "fused_frac": round(f_gbps / PEAK_HBM_GBPS, 4),
             "kernel": "decode_gqa_mfma_kernel<128,bf16>", "algorithmic_bytes": nbytes,
             "bytes_note": "K and V counted once per kv head"}
 
