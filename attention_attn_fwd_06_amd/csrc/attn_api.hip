@@ -48,6 +48,8 @@ constexpr int kDecodeChunkMax = 8192;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
 bool valid_prefill_head_dim(int d) { return valid_head_dim(d) || d == 256; }
+// the 16-bit decode, its merge and the fused decode (the FP8-KV decode keeps valid_head_dim)
+bool valid_decode_head_dim(int d) { return valid_head_dim(d) || d == 256; }
 bool valid_dtype(int dt) { return dt == ATTN_F16 || dt == ATTN_BF16; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
@@ -71,7 +73,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
     case ATTN_ERR_BAD_DIMENSION: return "a size argument is not positive";
-    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (prefill: 32, 64, 128, 256; FP8 prefill: 64, 128; decode: 32, 64, 128)";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (prefill and 16-bit decode: 32, 64, 128, 256; FP8 prefill: 64, 128; FP8-KV decode: 32, 64, 128)";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
     case ATTN_ERR_GQA_GROUPS: return "Hq must be a multiple of Hkv";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires N <= M (bottom-right mask)";
@@ -167,7 +169,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
                         hipStream_t stream) {
   if (!q || !k || !v || !o_part || !lse_part) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || chunk_size <= 0) return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_decode_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
@@ -181,7 +183,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, float* o_pa
 }
 
 size_t attn_decode_fused_workspace_bytes(int B, int Hq, int Hkv, int M, int d) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || Hq % Hkv != 0 || !valid_head_dim(d)) return 0;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0 || Hq % Hkv != 0 || !valid_decode_head_dim(d)) return 0;
   return attn::fused_workspace_layout(B, Hq, Hkv, d, attn::fused_segment_cap(B, Hq, Hkv, M), nullptr, nullptr);
 }
 
@@ -190,7 +192,7 @@ int attn_decode_fused(const void* q, const void* k, const void* v, void* o, floa
                       hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_decode_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
@@ -209,7 +211,7 @@ int attn_decode_fused_noalloc(const void* q, const void* k, const void* v, void*
                               int Hkv, int M, int d, float scale, attn_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_decode_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
@@ -259,7 +261,7 @@ int paged_decode(const void* q, const void* k_cache, const void* v_cache, const 
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || chunk_size <= 0 || pk.num_blocks <= 0 || pk.block_size <= 0 ||
       pk.max_blocks <= 0)
     return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (fp8 ? !valid_head_dim(d) : !valid_decode_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
   if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
   if (chunk_size % kDecodeChunk != 0 || chunk_size > kDecodeChunkMax) return ATTN_ERR_CHUNK_SIZE;
@@ -307,7 +309,7 @@ int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
               int d, attn_dtype_t out_dtype, hipStream_t stream) {
   if (!o_part || !lse_part || !o) return ATTN_ERR_NULL_POINTER;
   if (B <= 0 || Hq <= 0 || num_chunks <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
-  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_decode_head_dim(d)) return ATTN_ERR_HEAD_DIM;
   if (!valid_dtype(out_dtype)) return ATTN_ERR_DTYPE;
   if ((int64_t)B * Hq * num_chunks >= kMaxElems || (int64_t)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
   if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) ||

@@ -316,7 +316,7 @@ __device__ __forceinline__ int perm4(int g) { return ((g & 1) << 1) | (g >> 1); 
 // ds_read_b128 lane groups.
 template <int D>
 __device__ __forceinline__ int qk_chunk(int s, int g) {
-  constexpr int kS = D / 32, kX = D == 32 ? 2 : (D == 64 ? 1 : 0);
+  constexpr int kS = D / 32, kX = D == 32 ? 2 : (D == 64 ? 1 : 0);  // d = 128, 256: kX = 0
   return (kS * g + s) ^ ((g & 1) ? kX : 0);
 }
 constexpr int kMfmaMinItems = 2048;  // MHA chunk items from which the MFMA kernel is used
@@ -328,6 +328,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
                             int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale, FusedOut fo) {
   static_assert(!FUSED || (!PAGED && !KV8), "the fused merge is built for contiguous 16-bit K/V");
+  static_assert(!KV8 || D <= 128, "FP8 K/V: head dims up to 128");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
   constexpr int kDB = D / 16 >= kWaves ? D / 16 / kWaves : 1;  // 16-row d blocks per wave
@@ -336,7 +337,10 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   constexpr int kRowsPerInst = kDecThreads / kU;    // rows per fetch instruction index
   constexpr int kFetch = kChunk / kRowsPerInst;     // fetch instructions per wave
   constexpr uint32_t kPBytes = kGqaCols * kPRow * 2;  // one P part
-  static_assert(kRowsPerInst % 16 == 0, "swizzle must repeat across fetch instructions");
+  // the swizzle repeats every 16 rows: with 8 rows per fetch instruction
+  // (d = 256) the odd instructions take the lane offsets of rows 8 .. 15
+  static_assert(kRowsPerInst % 16 == 0 || kRowsPerInst == 8, "rows per fetch instruction");
+  constexpr bool kOddRows = kRowsPerInst == 8;
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf[kChunk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf[kChunk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t qbuf[kGqaCols * D];
@@ -354,17 +358,22 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
   // K/V fetch: instruction i of wave w fills LDS units (i*kWaves + w)*64 +
   // lane, i.e. row kRowsPerInst*i + rl, physical 16-byte chunk pc (holding
-  // logical chunk pc ^ swz(row)).  The Q fetch (16 rows) uses instruction 0 of
-  // the first kQInst waves.
+  // logical chunk pc ^ swz(row)).  The Q fetch (16 rows) takes kQInst
+  // instructions the same way: instruction 0 of the first kQInst waves, or
+  // (d = 256) instructions 0 and 1 of every wave.
   constexpr int kQInst = kGqaCols * kU / 64;
   const int rl = (wave * 64 + lane) / kU, pc = lane % kU;
   const uint32_t voff_lane = (uint32_t)(rl * D * 2 + ((pc ^ swz<D>(rl)) << 4));
+  const uint32_t voff_odd = (uint32_t)(rl * D * 2 + ((pc ^ swz<D>(rl + 8)) << 4));  // rows 8 .. 15 (d = 256)
+  auto voff_inst = [&](int i) { return (kOddRows && (i & 1)) ? voff_odd : voff_lane; };
   // paged: a wave's fetch instruction covers kWaveRows consecutive key rows
   // (4, 8 or 16), which never straddle a page (block_size % 16 == 0), so each
   // instruction gets its own page descriptor and the lanes offset into it
   constexpr int kWaveRows = 64 / kU;
   const uint32_t voff_paged =
       PAGED ? (uint32_t)((int64_t)(lane / kU) * pk.token_stride * 2) + (uint32_t)((pc ^ swz<D>(rl)) << 4) : 0u;
+  const uint32_t voff_paged_odd =
+      PAGED ? (uint32_t)((int64_t)(lane / kU) * pk.token_stride * 2) + (uint32_t)((pc ^ swz<D>(rl + 8)) << 4) : 0u;
   // V^T operand: in each 16-lane group of a ds_read_b64_tr_b16, lane s
   // addresses V[K0 + s/4][D0 + 4*(s%4)], so lane i receives V[K0 + 0..3][D0 + i].
   // Group g fills slots 8g .. 8g + 7 of k-step ks: keys 32 ks + 4 perm4(g) +
@@ -572,7 +581,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < kFetch; ++i)
       dma16<true>(desc, k_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                  voff_lane + (uint32_t)(kk + kRowsPerInst * i) * (uint32_t)(D * 2));
+                  voff_inst(i) + (uint32_t)(kk + kRowsPerInst * i) * (uint32_t)(D * 2));
   };
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -615,6 +624,11 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const i32x4 vdesc = make_desc(v + slice, D, M, D);
     if constexpr (KV8) {
       if (q8_item != item) loadq8(b, h0);  // written to LDS after the first sub-chunk's conversion
+    } else if constexpr (kQInst > kWaves) {
+#pragma unroll
+      for (int i = 0; i < kQInst / kWaves; ++i)
+        dma16(qdesc, q_lds + (uint32_t)(i * kWaves + wave) * 1024u,
+              voff_inst(i) + (uint32_t)(kRowsPerInst * i) * (uint32_t)(D * 2));
     } else if (wave < kQInst) {
       dma16(qdesc, q_lds + (uint32_t)wave * 1024u, voff_lane);
     }
@@ -722,10 +736,11 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           if (nv <= 0) page = 0;
           const int64_t off = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
                               (int64_t)(rg % pk.block_size) * pk.token_stride;
+          const uint32_t vo = (kOddRows && (i & 1)) ? voff_paged_odd : voff_paged;
           dma16<true>(make_desc_rows(k + off, pk.token_stride, max(nv, 0), D),
-                      k_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
+                      k_lds + (uint32_t)(i * kWaves + wave) * 1024u, vo);
           dma16<true>(make_desc_rows(v + off, pk.token_stride, max(nv, 0), D),
-                      v_lds + (uint32_t)(i * kWaves + wave) * 1024u, voff_paged);
+                      v_lds + (uint32_t)(i * kWaves + wave) * 1024u, vo);
         }
         // prefetch the next sub-chunk's page ids (the next item's, with its length)
         if (key0 + kChunk < c_end) {
@@ -749,7 +764,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int i = 0; i < kFetch; ++i)
           dma16<true>(vdesc, v_lds + (uint32_t)(i * kWaves + wave) * 1024u,
-                      voff_lane + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
+                      voff_inst(i) + (uint32_t)(key0 + kRowsPerInst * i) * (uint32_t)(D * 2));
       }
       // paged: K and V of one instruction are issued together (each descriptor
       // lives briefly, and this measured faster than K first), so wait for both
@@ -970,7 +985,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
   // (K/V read once per kv head), and so do large MHA launches; a small MHA
   // launch (a few rounds of items) finishes sooner on the VALU kernel's
   // shorter per-item path.
-  if (group >= 2 || chunk != kChunk || (int64_t)B * Hq * C >= kMfmaMinItems) {
+  if (group >= 2 || chunk != kChunk || (int64_t)B * Hq * C >= kMfmaMinItems || d == 256) {
     // query heads per item: the largest divisor of the group that fits the
     // 16 MFMA columns
     int g = std::min(group, kGqaCols);
@@ -985,6 +1000,7 @@ hipError_t decode_dispatch(const void* q, const void* k, const void* v, float* o
     }
     ATTN_GQA_CASE(32, false) ATTN_GQA_CASE(32, true)
     ATTN_GQA_CASE(64, false) ATTN_GQA_CASE(64, true) ATTN_GQA_CASE(128, false) ATTN_GQA_CASE(128, true)
+    ATTN_GQA_CASE(256, false) ATTN_GQA_CASE(256, true)
 #undef ATTN_GQA_CASE
     return hipErrorInvalidValue;
   }
@@ -1075,6 +1091,7 @@ hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, vo
   }
   ATTN_FUSED_CASE(32, false) ATTN_FUSED_CASE(32, true) ATTN_FUSED_CASE(64, false)
   ATTN_FUSED_CASE(64, true) ATTN_FUSED_CASE(128, false) ATTN_FUSED_CASE(128, true)
+  ATTN_FUSED_CASE(256, false) ATTN_FUSED_CASE(256, true)
 #undef ATTN_FUSED_CASE
   return hipErrorInvalidValue;
 }
@@ -1134,6 +1151,7 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
   }
   ATTN_PAGED_CASE(32, false, false) ATTN_PAGED_CASE(32, true, false) ATTN_PAGED_CASE(64, false, false)
   ATTN_PAGED_CASE(64, true, false) ATTN_PAGED_CASE(128, false, false) ATTN_PAGED_CASE(128, true, false)
+  ATTN_PAGED_CASE(256, false, false) ATTN_PAGED_CASE(256, true, false)
   ATTN_PAGED_CASE(32, false, true) ATTN_PAGED_CASE(32, true, true) ATTN_PAGED_CASE(64, false, true)
   ATTN_PAGED_CASE(64, true, true) ATTN_PAGED_CASE(128, false, true) ATTN_PAGED_CASE(128, true, true)
 #undef ATTN_PAGED_CASE
@@ -1185,6 +1203,8 @@ hipError_t merge_dispatch(const float* o_part, const float* lse_part, void* o, f
   ATTN_MERGE_QW(128, true)
   ATTN_MERGE_CASE(128, false, 32)
   ATTN_MERGE_CASE(128, true, 32)
+  ATTN_MERGE_QW(256, false) ATTN_MERGE_CASE(256, false, 32)
+  ATTN_MERGE_QW(256, true) ATTN_MERGE_CASE(256, true, 32)
 #undef ATTN_MERGE_QW
 #undef ATTN_MERGE_CASE
   return hipErrorInvalidValue;

@@ -62,8 +62,9 @@ typedef enum {
   ATTN_ERR_NULL_POINTER = -1,   /* a required pointer is NULL */
   ATTN_ERR_BAD_DIMENSION = -2,  /* a size is <= 0 */
   ATTN_ERR_HEAD_DIM = -3,       /* head dimension d not supported by the call (attn_fwd:
-                                   {32, 64, 128, 256}; attn_fwd_fp8qk: {64, 128}; decode and
-                                   merge: {32, 64, 128}) */
+                                   {32, 64, 128, 256}; attn_fwd_fp8qk: {64, 128}; 16-bit
+                                   decode, fused decode and merge: {32, 64, 128, 256};
+                                   FP8-KV decode: {32, 64, 128}) */
   ATTN_ERR_DTYPE = -4,          /* dtype not an attn_dtype_t value */
   ATTN_ERR_GQA_GROUPS = -5,     /* Hq is not a multiple of Hkv */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal requested with N > M */
@@ -169,7 +170,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int M, int d, int chunk_size);
  * p_j = exp(s_j - m_c), l_c = sum p_j, o_part = (sum_j p_j v_j) / l_c (normalised),
  * lse_part = m_c + ln l_c ("CUDA Flash Decoding", section 2.2 step 1).  No mask.
  * Requires chunk_size a multiple of 128 and at most 8192 (longer chunks mean fewer
- * partials for lse_merge to read), d in {32, 64, 128}, Hq % Hkv == 0, a finite
+ * partials for lse_merge to read), d in {32, 64, 128, 256}, Hq % Hkv == 0, a finite
  * scale >= 0, B*Hq <= 65535, B*Hq*C and (M + 128)*d below 2^31 (one (batch, kv
  * head) slice of K or V is read with 32-bit offsets).
  */
@@ -287,7 +288,8 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
  * attn_decode_paged_fp8kv_splitkv - attn_decode_paged_splitkv over a paged cache
  * of FP8 E4M3 codes with per-tensor scales (as attn_decode_fp8kv_splitkv): key
  * and value elements are one byte, so the element strides are byte strides and
- * must be multiples of 16.  Otherwise as attn_decode_paged_splitkv, including
+ * must be multiples of 16, and d in {32, 64, 128}.  Otherwise as
+ * attn_decode_paged_splitkv, including
  * the zero rows in place of out-of-range page ids (for those the kernel reads
  * 16 bytes at the start of the cache, page 0, which num_blocks >= 1
  * guarantees, and discards them).
@@ -309,7 +311,8 @@ int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const vo
  * future work and fixes no format).  Codes are converted exactly to dtype
  * inside the kernel; the products and sums are those of attn_decode_splitkv.
  * NaN codes (S.1111.111) give NaN.  Requires the attn_decode_splitkv
- * conditions and finite scales >= 0 (else ATTN_ERR_SCALE).
+ * conditions with d in {32, 64, 128} (else ATTN_ERR_HEAD_DIM) and finite
+ * scales >= 0 (else ATTN_ERR_SCALE).
  */
 int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float k_scale, float v_scale,
                               float* o_part, float* lse_part,
@@ -326,7 +329,7 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
  * o = sum_c w_c o_part[c], lse = g ("CUDA Flash Decoding", section 2.2 step 2).
  * A row whose lse_part are all -inf (no key at all, e.g. an empty paged
  * sequence) gets o = 0 and lse = -inf.  Requires num_chunks >= 1, d in
- * {32, 64, 128}, B*Hq <= 65535 and B*Hq*num_chunks below 2^31.
+ * {32, 64, 128, 256}, B*Hq <= 65535 and B*Hq*num_chunks below 2^31.
  */
 int lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
               int B, int Hq, int num_chunks, int d, attn_dtype_t out_dtype,

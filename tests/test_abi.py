@@ -144,7 +144,7 @@ def dec(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(op=None), -1), (dict(lp=None), -1),
     (dict(M=0), -2), (dict(chunk=0), -2), (dict(B=-1), -2),
-    (dict(d=80), -3), (dict(d=256), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
+    (dict(d=80), -3), (dict(d=512), -3), (dict(dtype=7), -4), (dict(Hq=8, Hkv=3), -5),
     (dict(chunk=64), -7), (dict(chunk=192), -7), (dict(chunk=8320), -7),
     (dict(scale=-1.0), -11),
     (dict(B=70000, Hq=1, Hkv=1, M=128), -9),
@@ -190,7 +190,8 @@ def fp8(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(k=None), -1), (dict(lp=None), -1), (dict(M=0), -2), (dict(d=48), -3), (dict(dtype=5), -4),
+    (dict(k=None), -1), (dict(lp=None), -1), (dict(M=0), -2), (dict(d=48), -3), (dict(d=256), -3),
+    (dict(dtype=5), -4),
     (dict(Hq=6, Hkv=4), -5), (dict(chunk=96), -7), (dict(ks=-1.0), -11), (dict(vs=float("inf")), -11),
     (dict(ks=float("nan")), -11), (dict(B=70000, Hq=1, Hkv=1), -9), (dict(v=FAKE + 8), -10),
 ])
@@ -210,8 +211,8 @@ def paged8(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(kc=None), -1), (dict(bt=None), -1), (dict(mb=0), -2), (dict(d=80), -3), (dict(chunk=64), -7),
-    (dict(ks=-0.5), -11), (dict(vs=float("nan")), -11),
+    (dict(kc=None), -1), (dict(bt=None), -1), (dict(mb=0), -2), (dict(d=80), -3), (dict(d=256), -3),
+    (dict(chunk=64), -7), (dict(ks=-0.5), -11), (dict(vs=float("nan")), -11),
     (dict(hs=8), -12), (dict(ts=24), -12), (dict(bs=8), -12), (dict(vc=FAKE + 8), -10),
 ])
 def test_paged_fp8kv_decode_rejects(kw, code):
@@ -238,6 +239,9 @@ def test_workspace_bytes():
     assert lib.attn_decode_workspace_bytes(2, 8, 65536, 128, 128) == 2 * 8 * 512 * 129 * 4
     assert lib.attn_decode_workspace_bytes(1, 8, 513, 128, 128) == 1 * 8 * 5 * 129 * 4
     assert lib.attn_decode_workspace_bytes(0, 8, 512, 128, 128) == 0
+    # head dim 256 (16-bit decode, fused decode, merge)
+    assert lib.attn_decode_workspace_bytes(1, 4, 300, 256, 128) == 1 * 4 * 3 * 257 * 4
+    assert lib.attn_decode_fused_workspace_bytes(2, 16, 4, 1000, 256) > 0
 
 
 def fused(**kw):

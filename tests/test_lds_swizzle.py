@@ -143,16 +143,16 @@ def perm4(g):
 
 
 def qk_chunk(D, s, g):
-    kS, kX = D // 32, {32: 2, 64: 1, 128: 0}[D]
+    kS, kX = D // 32, {32: 2, 64: 1, 128: 0, 256: 0}[D]
     return (kS * g + s) ^ (kX if g & 1 else 0)
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_decode_qk_chunk_map_is_a_bijection(D):
     assert sorted(qk_chunk(D, s, g) for s in range(D // 32) for g in range(4)) == list(range(D // 8))
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_decode_k_and_q_operand_reads(D):
     # 16x16x32 MFMA: lane (j = l%16, g = l/16) reads row 32w + 16kb + j (Q: row j),
     # logical chunk qk_chunk(s, g)
@@ -163,7 +163,7 @@ def test_decode_k_and_q_operand_reads(D):
                                                    for l in range(64)])
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_decode_v_transposed_reads(D):
     # lane s of group g addresses row 32ks + 4 perm4(g) + 16hh + s/4, column 16*blk + 4(s%4)
     for ks in range(4):

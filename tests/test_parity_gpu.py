@@ -385,6 +385,11 @@ DEC_SHAPES = [
     (1, 4, 4, 300, 32, "f16"),
     (2, 16, 4, 1000, 32, "bf16"),
     (4, 8, 8, 8200, 32, "f16"),
+    # head dim 256 (matrix-core kernel for every launch; 8-row fetch instructions)
+    (1, 4, 4, 300, 256, "f16"),
+    (2, 16, 4, 1000, 256, "bf16"),
+    (1, 8, 8, 2100, 256, "bf16"),
+    (1, 24, 8, 777, 256, "f16"),
 ]
 
 
@@ -401,7 +406,7 @@ def test_decode_shapes(shape):
 @pytest.mark.parametrize("shape", [(1, 8, 2, 1000, 128, "bf16", 256), (2, 4, 4, 3000, 64, "f16", 512),
                                    (1, 16, 2, 777, 128, "f16", 1024), (1, 4, 1, 9000, 64, "bf16", 8192),
                                    (2, 8, 8, 2049, 128, "f16", 384), (1, 32, 4, 130, 128, "bf16", 8192),
-                                   (1, 8, 2, 2000, 32, "bf16", 512)],
+                                   (1, 8, 2, 2000, 32, "bf16", 512), (1, 8, 2, 1000, 256, "bf16", 512)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_decode_chunk_sizes(shape):
     B, Hq, Hkv, M, d, dt, chunk = shape
@@ -449,6 +454,8 @@ PAGED_CASES = [
     (2, 16, 1, (130, 16), 32, "bf16", 32, 128, True),
     (1, 2, 1, (2048,), 128, "f16", 128, 128, False),
     (2, 12, 4, (300, 2000), 64, "bf16", 48, 1024, False),
+    (2, 8, 2, (300, 1000), 256, "bf16", 16, 128, False),
+    (1, 4, 1, (777,), 256, "f16", 64, 256, True),
 ]
 
 
@@ -674,6 +681,8 @@ FUSED_SHAPES = [
     (2, 16, 4, 1000, 32, "bf16"),
     (64, 32, 32, 1000, 64, "f16"),     # more rows than the grid: one segment per row
     (1, 1, 1, 1, 128, "f16"),          # a single key
+    (2, 16, 4, 1000, 256, "bf16"),     # head dim 256
+    (1, 8, 8, 4097, 256, "f16"),
 ]
 
 
@@ -712,7 +721,8 @@ def test_decode_fused_workspace_reuse_and_determinism():
     assert int(ws[:n_cnt].count_nonzero()) == 0, "counters not reset"
 
 
-@pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16")])
+@pytest.mark.parametrize("C,d,dt", [(1, 128, "f16"), (3, 64, "bf16"), (600, 128, "f16"), (37, 64, "f16"),
+                                    (3, 256, "bf16")])
 def test_lse_merge_standalone(C, d, dt):
     say(f"case lse_merge C={C} d={d} {dt}")
     g = torch.Generator("cpu").manual_seed(C)
@@ -726,12 +736,14 @@ def test_lse_merge_standalone(C, d, dt):
 
 
 # (batch, head) counts that select every column width of the merge workgroup:
-# 4*QW columns per workgroup, QW in {4, 8, 16, 32} (d = 128), {4, 8, 16} (d = 64)
+# 4*QW columns per workgroup, QW in {4, 8, 16, 32} (d = 128, 256), {4, 8, 16} (d = 64)
 # and {4, 8} (d = 32)
 @pytest.mark.parametrize("B,Hq,C,d,dt", [(4, 32, 50, 128, "bf16"), (8, 32, 7, 128, "f16"),
                                          (16, 32, 3, 128, "bf16"), (8, 32, 20, 64, "f16"),
                                          (16, 32, 5, 64, "bf16"), (3, 5, 130, 64, "bf16"),
-                                         (2, 3, 40, 32, "f16"), (16, 32, 9, 32, "bf16")])
+                                         (2, 3, 40, 32, "f16"), (16, 32, 9, 32, "bf16"),
+                                         (8, 32, 7, 256, "f16"), (4, 32, 9, 256, "bf16"),
+                                         (2, 32, 11, 256, "f16"), (2, 3, 40, 256, "bf16")])
 def test_lse_merge_column_widths(B, Hq, C, d, dt):
     say(f"case lse_merge B={B} Hq={Hq} C={C} d={d} {dt}")
     g = torch.Generator("cpu").manual_seed(B * 1000 + C)
