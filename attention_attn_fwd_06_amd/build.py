@@ -21,6 +21,11 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops stay disabled (hipcc -O3 would otherwise form them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the prefill's fully unrolled step at head dim 256 (64 MFMA slots) is larger
+    # than the default limit for `#pragma unroll`; left rolled, its register
+    # arrays are indexed at run time and spill to scratch (2 KB per lane, 50x
+    # slower).  The other kernels compile to the same code either way.
+    "-mllvm", "-pragma-unroll-threshold=100000",
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["attn_api.hip", "prefill_fwd.hip", "decode.hip"]
