@@ -15,7 +15,7 @@ from . import _lib
 __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_fwd_fp8qk", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
-    "attn_decode_paged", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
+    "attn_decode_paged", "attn_decode_paged_fused", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
     "attn_decode_fused_workspace_bytes", "attn_decode_fused_noalloc",
 ]
 
@@ -327,19 +327,9 @@ def attn_decode_fused_noalloc(q, k, v, scale: float | None = None, o=None, lse=N
     return o, lse
 
 
-def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
-                              scale: float | None = None, o_part=None, lse_part=None, stream=None,
-                              k_scale: float | None = None, v_scale: float | None = None):
-    """Split-KV decode partials over a paged KV cache.
-
-    q [B,Hq,d]; k_cache, v_cache: views [num_blocks, block_size, Hkv, d] with a
-    contiguous last dimension (token-major pages as they are, head-major pages
-    [num_blocks, Hkv, block_size, d] passed as ``.transpose(1, 2)``), both with
-    the same strides; block_table [B, max_blocks] int32; seq_lens [B] int32.
-    Returns (o_part [B,Hq,C,d], lse_part [B,Hq,C]) with
-    C = ceil(max_blocks * block_size / chunk_size).  Caches of E4M3 codes
-    (torch.float8_e4m3fn or uint8) take k_scale and v_scale (FP8 KV).
-    """
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens):
+    """Checks of a paged call's inputs; returns (dtype code, B, Hq, d,
+    num_blocks, block_size, Hkv, max_blocks)."""
     if q.dim() != 3:
         raise ValueError("q must be [B, Hq, d]")
     dt = _dtype_code(q)
@@ -348,12 +338,9 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
         _rows_contig(t, n, 4)
     if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must have the same shape and strides")
-    fp8 = k_cache.dtype in _FP8
-    if fp8:
+    if k_cache.dtype in _FP8:
         if v_cache.dtype not in _FP8:
             raise ValueError("k_cache holds E4M3 codes, so v_cache must too")
-        if k_scale is None or v_scale is None:
-            raise ValueError("FP8 caches need k_scale and v_scale")
     else:
         _dtype(k_cache, "k_cache", q.dtype)
         _dtype(v_cache, "v_cache", q.dtype)
@@ -367,6 +354,26 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
     max_blocks = block_table.shape[1]
     if dk != d or tuple(block_table.shape) != (B, max_blocks) or tuple(seq_lens.shape) != (B,):
         raise ValueError("shape mismatch between q, the caches, block_table and seq_lens")
+    return dt, B, Hq, d, num_blocks, block_size, Hkv, max_blocks
+
+
+def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_size: int = 128,
+                              scale: float | None = None, o_part=None, lse_part=None, stream=None,
+                              k_scale: float | None = None, v_scale: float | None = None):
+    """Split-KV decode partials over a paged KV cache.
+
+    q [B,Hq,d]; k_cache, v_cache: views [num_blocks, block_size, Hkv, d] with a
+    contiguous last dimension (token-major pages as they are, head-major pages
+    [num_blocks, Hkv, block_size, d] passed as ``.transpose(1, 2)``), both with
+    the same strides; block_table [B, max_blocks] int32; seq_lens [B] int32.
+    Returns (o_part [B,Hq,C,d], lse_part [B,Hq,C]) with
+    C = ceil(max_blocks * block_size / chunk_size).  Caches of E4M3 codes
+    (torch.float8_e4m3fn or uint8) take k_scale and v_scale (FP8 KV).
+    """
+    fp8 = k_cache.dtype in _FP8
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("FP8 caches need k_scale and v_scale")
+    dt, B, Hq, d, num_blocks, block_size, Hkv, max_blocks = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
     C = _num_chunks(max_blocks * block_size, chunk_size)
     _decode_partials(q, o_part, lse_part, C)
     _devices((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
@@ -390,6 +397,52 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
     if st != 0:
         raise AttnError(st, "attn_decode_paged_splitkv")
     return o_part, lse_part
+
+
+def attn_decode_paged_fused(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None, o=None,
+                            lse=None, return_lse: bool = True, workspace=None, stream=None):
+    """Split-KV decode over a paged KV cache in one launch (partials of
+    128-key chunk runs and their merge fused).
+
+    q [B,Hq,d]; k_cache, v_cache, block_table, seq_lens as in
+    attn_decode_paged_splitkv (16-bit caches).  Returns (o [B,Hq,d], lse
+    [B,Hq] fp32 or None).  ``workspace``: a uint8 GPU tensor of at least
+    attn_decode_fused_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, d)
+    bytes, zero-filled before its first use; by default a fresh zeroed one."""
+    if k_cache.dtype in _FP8:
+        raise TypeError("the fused paged decode takes 16-bit caches")
+    dt, B, Hq, d, num_blocks, block_size, Hkv, max_blocks = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
+    if o is not None:
+        _shape(o, "o", (B, Hq, d))
+        _dtype(o, "o", q.dtype)
+        _contig(o, "o")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq))
+    nbytes = attn_decode_fused_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, d)
+    if workspace is not None:
+        _dtype(workspace, "workspace", torch.uint8)
+        _contig(workspace, "workspace")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    _devices((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+             (seq_lens, "seq_lens"), (o, "o"), (lse, "lse"), (workspace, "workspace"))
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    pk = _lib.PagedKv(block_table.data_ptr(), seq_lens.data_ptr(), num_blocks, block_size, max_blocks,
+                      k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    st = _lib.load().attn_decode_paged_fused(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(pk),
+                                             o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                             workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, d, float(scale), dt,
+                                             _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_fused")
+    return o, lse
 
 
 def attn_decode_fp8kv_splitkv(q, k, v, k_scale: float, v_scale: float, chunk_size: int = 128,

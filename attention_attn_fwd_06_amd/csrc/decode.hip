@@ -327,7 +327,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
                             int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale, FusedOut fo) {
-  static_assert(!FUSED || (!PAGED && !KV8), "the fused merge is built for contiguous 16-bit K/V");
+  static_assert(!FUSED || !KV8, "the fused merge is built for 16-bit K/V");
   static_assert(!KV8 || D <= 128, "FP8 K/V: head dims up to 128");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
@@ -508,9 +508,13 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   // doubles the kernel's time).
   __shared__ int fused_last;
   auto fused_epilogue = [&](int row, int b, int h0, int seg, float lt, float m_ref, const f32x4 (&acc)[kDB]) {
+    // lt == 0: a segment (or row) with no key (past a paged sequence's end):
+    // O = 0 and lse = -inf, which the merge gives no weight
+    const bool has = !(lt == 0.f);
+    const float inv = has ? 1.f / lt : 0.f;
+    const float l2 = has ? m_ref + log2f(lt) : -INFINITY;
     if (C == 1) {
       if (j < G) {
-        const float inv = 1.f / lt;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           if (wave >= kPVWaves) break;
@@ -518,7 +522,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           *reinterpret_cast<uint2*>(fo.o + ((int64_t)b * Hq + h0 + j) * D + 16 * (wave * kDB + db) + 4 * g) =
               make_uint2(pack2<BF16>(o4[0], o4[1]), pack2<BF16>(o4[2], o4[3]));
         }
-        if (wave == 0 && g == 0 && fo.lse != nullptr) fo.lse[(int64_t)b * Hq + h0 + j] = (m_ref + log2f(lt)) * kLn2;
+        if (wave == 0 && g == 0 && fo.lse != nullptr) fo.lse[(int64_t)b * Hq + h0 + j] = l2 * kLn2;
       }
       return;
     }
@@ -526,7 +530,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     auto get = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     if (j < G) {
       const int64_t e = ((int64_t)row * C + seg) * G + j;
-      const float inv = 1.f / lt;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         if (wave >= kPVWaves) break;
@@ -534,7 +537,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r) put(op + r, acc[db][r] * inv);
       }
-      if (wave == 0 && g == 0) put(fo.seg_lse + e, m_ref + log2f(lt));
+      if (wave == 0 && g == 0) put(fo.seg_lse + e, l2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
     __syncthreads();
@@ -594,7 +597,17 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     if constexpr (PAGED) {
       seq = nx_item == item ? nx_seq : seq_len(b);
       seq = min(max(seq, 0), pk.max_blocks * pk.block_size);
-      if (c * chunk >= seq) {
+      if constexpr (FUSED) {
+        if ((int)((int64_t)c * fo.n_chunks / C) * kChunk >= seq) {
+          // a segment past the sequence's end still counts towards its row
+          f32x4 zero[kDB];
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) zero[db] = (f32x4){};
+          fused_epilogue(rest, b, h0, c, 0.f, -INFINITY, zero);
+          __syncthreads();  // the merge states are refilled by the next item
+          continue;
+        }
+      } else if (c * chunk >= seq) {
         // chunk past the sequence's end: O_c = 0, lse_c = -inf (no weight in the merge)
         if (j < G) {
           const int64_t base = ((int64_t)b * Hq + h0 + j) * C + c;
@@ -612,7 +625,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     }
     // keys of this item: chunk c, or (fused) segment c of the row's chunks
     const int k_begin = FUSED ? (int)((int64_t)c * fo.n_chunks / C) * kChunk : c * chunk;
-    const int c_end = FUSED ? min(M, (int)((int64_t)(c + 1) * fo.n_chunks / C) * kChunk) : min(seq, (c + 1) * chunk);
+    const int c_end = FUSED ? min(seq, (int)((int64_t)(c + 1) * fo.n_chunks / C) * kChunk) : min(seq, (c + 1) * chunk);
     const int64_t slice = PAGED ? 0 : ((int64_t)b * Hkv + kvh) * M * D;
 
     // Q rows h0 .. h0 + 15 (once per item), then per 128-key sub-chunk its K
@@ -754,7 +767,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           if (n < n_items) {
             const int bn = n / C / slices / Hkv;
             nx_item = n;
-            nx_key0 = (n % C) * chunk;
+            nx_key0 = FUSED ? (int)((int64_t)(n % C) * fo.n_chunks / C) * kChunk : (n % C) * chunk;
             nx_seq = seq_len(bn);
             load_pages(bn, nx_key0, pgv);
           }
@@ -1093,6 +1106,42 @@ hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, vo
   ATTN_FUSED_CASE(64, true) ATTN_FUSED_CASE(128, false) ATTN_FUSED_CASE(128, true)
   ATTN_FUSED_CASE(256, false) ATTN_FUSED_CASE(256, true)
 #undef ATTN_FUSED_CASE
+  return hipErrorInvalidValue;
+}
+
+// Fused decode over a paged cache: rows of the longest sequence the table can
+// describe (max_blocks * block_size keys) split into segments as in the
+// contiguous case; segments past a row's sequence end count as empty.
+hipError_t decode_paged_fused_dispatch(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
+                                       int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
+                                       int64_t head_stride, void* o, float* lse, void* ws, size_t ws_bytes, int B,
+                                       int Hq, int Hkv, int d, bool bf16, float scale, hipStream_t stream) {
+  const int M = max_blocks * block_size;
+  const int G = heads_per_item(Hq / Hkv);
+  const int64_t rows = (int64_t)B * (Hq / G);
+  const int chunks = (M + kChunk - 1) / kChunk;
+  const int cap = fused_segment_cap(B, Hq, Hkv, M);
+  const float sl2 = scale * kLog2e;
+  const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
+#define ATTN_PFUSED_CASE(DD, BB)                                                                             \
+  if (d == DD && bf16 == BB) {                                                                               \
+    auto* kern = &decode_gqa_mfma_kernel<DD, BB, true, false, true>;                                         \
+    const int resident = resident_grid<decode_gqa_mfma_kernel<DD, BB, true, false, true>>(kDecThreads);     \
+    const int S = fused_segments(rows, chunks, std::min(resident, kFusedGridCap), cap);                     \
+    size_t off_lse = 0, off_o = 0;                                                                           \
+    if (fused_workspace_layout(B, Hq, Hkv, DD, S, &off_lse, &off_o) > ws_bytes) return hipErrorInvalidValue; \
+    char* base = static_cast<char*>(ws);                                                                     \
+    const FusedOut fo{reinterpret_cast<float*>(base + off_o), reinterpret_cast<float*>(base + off_lse),      \
+                      reinterpret_cast<uint32_t*>(base), static_cast<uint16_t*>(o), lse, chunks};            \
+    const int n_items = (int)(rows * S);                                                                     \
+    return launch(kern, dim3(std::min(n_items, resident)), dim3(kDecThreads), stream, q, k_cache, v_cache,  \
+                  (float*)nullptr, (float*)nullptr, Hq, Hkv, M, S, G, kChunk, n_items, sl2, pk, 1.f, fo);   \
+  }
+  ATTN_PFUSED_CASE(32, false) ATTN_PFUSED_CASE(32, true) ATTN_PFUSED_CASE(64, false)
+  ATTN_PFUSED_CASE(64, true) ATTN_PFUSED_CASE(128, false) ATTN_PFUSED_CASE(128, true)
+  ATTN_PFUSED_CASE(256, false) ATTN_PFUSED_CASE(256, true)
+#undef ATTN_PFUSED_CASE
   return hipErrorInvalidValue;
 }
 

@@ -285,6 +285,31 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
                               attn_dtype_t dtype, hipStream_t stream);
 
 /*
+ * attn_decode_paged_fused - attn_decode_paged_splitkv at chunk size 128 and
+ * lse_merge in one launch (the paged counterpart of attn_decode_fused).
+ *
+ *   q        [B, Hq, d]  dtype, read      o   [B, Hq, d]  dtype, written
+ *   k_cache, v_cache     dtype, read      lse [B, Hq]     fp32, written (may be NULL)
+ *                        (layout in attn_paged_kv_t)
+ *
+ * The keys of sequence b (see attn_paged_kv_t) are split into segments of
+ * whole 128-key chunks of the longest sequence the table can describe
+ * (max_blocks*block_size keys); segments past the sequence's end have no key
+ * and no weight, and a sequence of 0 keys gets o = 0 and lse = -inf.  The
+ * result is that of attn_decode_paged_splitkv + lse_merge up to rounding.
+ * workspace: at least attn_decode_fused_workspace_bytes(B, Hq, Hkv,
+ * max_blocks*block_size, d) bytes, 16-byte aligned, with the conventions of
+ * attn_decode_fused (its counters zero before the first call and left zero
+ * by every completed call; calls that may run at the same time need
+ * workspaces of their own).  Requires the attn_decode_paged_splitkv
+ * conditions at chunk size 128, a 16-byte aligned o, and ATTN_ERR_WORKSPACE
+ * for a NULL, misaligned or short workspace.
+ */
+int attn_decode_paged_fused(const void* q, const void* k_cache, const void* v_cache, const attn_paged_kv_t* pages,
+                            void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                            int d, float scale, attn_dtype_t dtype, hipStream_t stream);
+
+/*
  * attn_decode_paged_fp8kv_splitkv - attn_decode_paged_splitkv over a paged cache
  * of FP8 E4M3 codes with per-tensor scales (as attn_decode_fp8kv_splitkv): key
  * and value elements are one byte, so the element strides are byte strides and

@@ -29,7 +29,7 @@ def test_header_declares_expected_api():
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
          "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
          "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused",
-         "attn_decode_fused_noalloc", "attn_fwd_fp8qk"])
+         "attn_decode_fused_noalloc", "attn_fwd_fp8qk", "attn_decode_paged_fused"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -272,6 +272,35 @@ def test_decode_fused_workspace_bytes():
     assert fused(wsb=n - 1) == -13
     assert lib.attn_decode_fused_workspace_bytes(2, 8, 3, 100, 128) == 0
     assert lib.attn_decode_fused_workspace_bytes(2, 8, 8, 100, 96) == 0
+
+
+def pfused(**kw):
+    """attn_decode_paged_fused with a page table whose pointers are fake."""
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30, B=2, Hq=8, Hkv=2, d=128, scale=0.088,
+             dtype=1, stream=None, bt=FAKE, sl=FAKE, nb=64, bs=16, mb=32, ps=16 * 2 * 128, ts=2 * 128, hs=128,
+             pages=True)
+    a.update(kw)
+    pk = _lib.PagedKv(a["bt"], a["sl"], a["nb"], a["bs"], a["mb"], a["ps"], a["ts"], a["hs"])
+    return _lib.load().attn_decode_paged_fused(a["q"], a["kc"], a["vc"], ctypes.byref(pk) if a["pages"] else None,
+                                               a["o"], a["lse"], a["ws"], a["wsb"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                               a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(pages=False), -1), (dict(sl=None), -1),
+    (dict(B=0), -2), (dict(bs=0), -2), (dict(d=80), -3), (dict(dtype=2), -4), (dict(Hq=8, Hkv=3), -5),
+    (dict(scale=-1.0), -11), (dict(bs=24), -12), (dict(ts=-8), -12),
+    (dict(o=FAKE + 8), -10), (dict(lse=FAKE + 1), -10), (dict(vc=FAKE + 8), -10),
+    (dict(ws=None), -13), (dict(ws=FAKE + 8), -13), (dict(wsb=100), -13),
+])
+def test_decode_paged_fused_rejects(kw, code):
+    assert pfused(**kw) == code
+
+
+def test_decode_paged_fused_workspace_is_that_of_the_longest_sequence():
+    lib = _lib.load()
+    n = lib.attn_decode_fused_workspace_bytes(2, 8, 2, 32 * 16, 128)
+    assert n > 0 and pfused(wsb=n - 1) == -13
 
 
 def noalloc(**kw):

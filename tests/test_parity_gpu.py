@@ -482,6 +482,63 @@ def test_decode_paged(case):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
+# the paged decode in one launch: the same cases (any chunk size runs as 128-key
+# chunks), an empty sequence, a bad page id inside a sequence, head dim 256
+PAGED_FUSED_CASES = [c for c in PAGED_CASES] + [
+    (4, 16, 4, (0, 1, 4096, 700), 128, "bf16", 16, 128, False),
+    (8, 8, 8, (3000,) * 8, 64, "f16", 32, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_FUSED_CASES, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_decode_paged_fused(case):
+    B, Hq, Hkv, lens, d, dt, bs, _, head_major = case
+    say(f"case paged fused decode {case}")
+    q, kc, vc, kv_k, kv_v, table, sl = paged_inputs(B, Hq, Hkv, list(lens), d, dt, bs, seed=sum(lens) + 1,
+                                                    head_major=head_major)
+    scale = float(np.float32(d ** -0.5))
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    kvk_d = kd.transpose(1, 2) if head_major else kd
+    kvv_d = vd.transpose(1, 2) if head_major else vd
+    ws = torch.zeros(attn().attn_decode_fused_workspace_bytes(B, Hq, Hkv, table.shape[1] * bs, d), dtype=torch.uint8,
+                     device=DEV)
+    for rep in range(2):       # the second call reuses the workspace (its counters reset themselves)
+        o, lse = attn().attn_decode_paged_fused(q.to(DEV), kvk_d, kvv_d, table.to(DEV), sl.to(DEV), scale,
+                                                workspace=ws)
+        torch.cuda.synchronize()
+        Or, Lr, _, _ = oracle.paged_decode_ref(q, kv_k, kv_v, table.clamp(min=0), sl, scale, 128)
+        Og, Lg = f64(o), f64(lse)
+        empty = np.asarray(lens) == 0
+        assert np.all(Og[empty] == 0.0) and np.all(Lg[empty] == -np.inf), "empty sequence"
+        eo, el = maxerr(Og[~empty], Or[~empty]), maxerr(Lg[~empty], Lr[~empty])
+        say(f"  call {rep}: o={eo:.3e} lse={el:.3e}")
+        assert eo <= TOL_O[dt] and el <= TOL_LSE
+    assert torch.count_nonzero(ws[:256]).item() == 0, "row counters left non-zero"
+
+
+def test_decode_paged_fused_bad_page_id():
+    """A page id out of range inside a sequence reads as keys and values of
+    zeros, as in the two-launch paged decode."""
+    B, Hq, Hkv, d, bs = 3, 8, 2, 128, 16
+    lens = [5, 200, 1000]
+    say("case paged fused decode, bad page id")
+    q, kc, vc, kv_k, kv_v, table, sl = paged_inputs(B, Hq, Hkv, lens, d, "f16", bs, seed=78, head_major=False)
+    num_blocks = kc.shape[0]
+    table[2, 5] = num_blocks + 11
+    scale = float(np.float32(d ** -0.5))
+    o, lse = attn().attn_decode_paged_fused(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), sl.to(DEV), scale)
+    torch.cuda.synchronize()
+    kref, vref = f64(kc), f64(vc)
+    zero = np.zeros((1,) + kref.shape[1:])
+    kref, vref = np.concatenate([kref, zero]), np.concatenate([vref, zero])
+    tref = table.clone()
+    tref[2, 5] = num_blocks
+    Or, Lr, _, _ = oracle.paged_decode_ref(q, kref, vref, tref.clamp(min=0), sl, scale, 128)
+    eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+    say(f"  o={eo:.3e} lse={el:.3e}")
+    assert eo <= TOL_O["f16"] and el <= TOL_LSE
+
+
 PAGED_FP8_CASES = [
     (3, 8, 2, (1, 200, 1000), 128, "bf16", 16, 128, False),
     (2, 4, 4, (777, 64), 64, "f16", 64, 256, True),
