@@ -19,7 +19,7 @@ the CPU oracle over its whole output (checked after the timed region).  The
 ``decode_gqa`` object reports a grouped-query decode (B=8, Hq=32, Hkv=8,
 M=16384, d=128, bf16; K/V counted once per kv head; two launches and one), and ``decode_paged`` /
 ``decode_fp8kv`` / ``decode_paged_fp8kv`` the same workload's chunk kernel
-through the paged-KV, FP8-KV and paged FP8-KV entry points.  ``cpu_baseline``
+through the paged-KV (two launches and one), FP8-KV and paged FP8-KV entry points.  ``cpu_baseline``
 is the oracle timed on the host on the causal GQA prefill (all of it) and on
 the long decode.
 
@@ -304,9 +304,18 @@ def paged_and_fp8_rates(attn, w, args, dev):
     ms = _time_chunk(lambda i: attn.attn_decode_paged_splitkv(q, sets[i % 2][0], sets[i % 2][1], sets[i % 2][2], lens,
                                                               w.chunk, w.scale, o_part=o_part, lse_part=lse_part), args)
     nbytes = 2.0 * w.B * w.Hkv * w.M * w.d * 2 + w.B * w.Hq * w.d * 2
+    # the same paged decode in one launch (partials and merge fused)
+    ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(w.B, w.Hq, w.Hkv, w.M, w.d), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    ms_f = _time_chunk(lambda i: attn.attn_decode_paged_fused(q, sets[i % 2][0], sets[i % 2][1], sets[i % 2][2], lens,
+                                                              w.scale, o=o, lse=lse, workspace=ws), args)
     out["decode_paged"] = {"workload": w.desc + ", paged KV: 16-key token-major pages, shuffled",
                            "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                            "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "chunk_ms": round(ms, 4),
+                           "fused_ms": round(ms_f, 4), "fused_GBps": round(nbytes / (ms_f * 1e-3) / 1e9, 1),
+                           "fused_frac": round(nbytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                            "kernel": "decode_gqa_mfma_kernel<128,bf16,paged>"}
     del sets
     sets8 = [(torch.randint(0, 126, (w.B, w.Hkv, w.M, w.d), dtype=torch.uint8, device=dev),
