@@ -401,6 +401,37 @@ def test_decode_shapes(shape):
     check_decode(q, k, v, 128, float(np.float32(d ** -0.5)), dt, str(shape))
 
 
+def test_decode_kv_slice_beyond_2_31_bytes():
+    """One (batch, kv head) slice of K and V of 8.4M keys (2.1 GB each, past
+    2^31 bytes; the kernels address a slice with 32-bit buffer offsets),
+    through the two-launch and the one-launch decode.  The oracle runs over
+    ranges of whole chunks (a chunk's partial depends only on its own keys)
+    and merges all partials once, so the whole output is compared."""
+    B, Hq, Hkv, d, dt, chunk = 1, 2, 1, 128, "bf16", 1024
+    M = (1 << 23) + 77
+    say(f"case decode with a {M}-key slice")
+    q, k, v = decode_inputs(B, Hq, Hkv, M, d, dt, seed=5, device=DEV)
+    scale = float(np.float32(d ** -0.5))
+    o, lse, op, lp = attn().attn_decode(q, k, v, chunk, scale)
+    of, lf = attn().attn_decode_fused(q, k, v, scale)
+    torch.cuda.synchronize()
+    C = -(-M // chunk)
+    qc, parts_o, parts_l = q.cpu(), [], []
+    step = 1024                                   # chunks per oracle call
+    for c0 in range(0, C, step):
+        lo, hi = c0 * chunk, min(M, (c0 + step) * chunk)
+        po, pl = oracle.decode_partials_ref(qc, k[:, :, lo:hi].cpu(), v[:, :, lo:hi].cpu(), scale, chunk)
+        parts_o.append(po)
+        parts_l.append(pl)
+    OPr, LPr = np.concatenate(parts_o, axis=2), np.concatenate(parts_l, axis=2)
+    Or, Lr = oracle.lse_merge_ref(OPr, LPr)
+    errs = dict(o=maxerr(f64(o), Or), lse=maxerr(f64(lse), Lr), o_part=maxerr(f64(op), OPr),
+                lse_part=maxerr(f64(lp), LPr), o_fused=maxerr(f64(of), Or), lse_fused=maxerr(f64(lf), Lr))
+    say("  " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
+    assert max(errs["o"], errs["o_part"], errs["o_fused"]) <= TOL_O[dt], errs
+    assert max(errs["lse"], errs["lse_part"], errs["lse_fused"]) <= TOL_LSE, errs
+
+
 # chunks longer than 128 keys (walked as 128-key sub-chunks with the online
 # rescale between them), with short last chunks and sub-chunks
 @pytest.mark.parametrize("shape", [(1, 8, 2, 1000, 128, "bf16", 256), (2, 4, 4, 3000, 64, "f16", 512),

@@ -8,7 +8,9 @@ inputs from here, so the two sides always see bit-identical values.
 
 Input recipe: ``torch.Generator('cpu').manual_seed(seed)``, then q, k, v are
 drawn in that order with ``torch.randn(shape, dtype=float32)`` and rounded
-(round-to-nearest-even) to fp16 or bf16.  The pages' workloads are
+(round-to-nearest-even) to fp16 or bf16 (inputs too large to draw on the host
+quickly, the 2.1 GB key slices of one decode test, come from the GPU's seeded
+generator instead, and the oracle reads copies of them).  The pages' workloads are
 i.i.d. N(0, 1) inputs of these shapes ("Flash Decoding" page, section 7;
 "fmha sm120" page, section 3 benchmark).
 
@@ -86,11 +88,11 @@ def workload(name: str) -> Workload:
     return WORKLOADS[name]
 
 
-def _draw(shapes, dtype: str, seed: int):
-    g = torch.Generator("cpu").manual_seed(seed)
+def _draw(shapes, dtype: str, seed: int, device: str = "cpu"):
+    g = torch.Generator(device).manual_seed(seed)
     out = []
     for shape in shapes:
-        x = torch.randn(shape, dtype=torch.float32, generator=g)
+        x = torch.randn(shape, dtype=torch.float32, generator=g, device=device)
         out.append(x.to(torch_dtype(dtype)))
     return out
 
@@ -100,9 +102,11 @@ def prefill_inputs(B, Hq, Hkv, N, M, d, dtype="f16", seed=0):
     return tuple(_draw([(B, N, Hq, d), (B, M, Hkv, d), (B, M, Hkv, d)], dtype, seed))
 
 
-def decode_inputs(B, Hq, Hkv, M, d, dtype="f16", seed=0):
-    """q [B,Hq,d], k [B,Hkv,M,d], v [B,Hkv,M,d] on the CPU, rounded to ``dtype``."""
-    return tuple(_draw([(B, Hq, d), (B, Hkv, M, d), (B, Hkv, M, d)], dtype, seed))
+def decode_inputs(B, Hq, Hkv, M, d, dtype="f16", seed=0, device="cpu"):
+    """q [B,Hq,d], k [B,Hkv,M,d], v [B,Hkv,M,d], rounded to ``dtype``; drawn on
+    the CPU, or with the given device's generator (another stream of numbers,
+    for inputs too large to draw on the host quickly)."""
+    return tuple(_draw([(B, Hq, d), (B, Hkv, M, d), (B, Hkv, M, d)], dtype, seed, device))
 
 
 def prefill_ramp_inputs(B, Hq, Hkv, N, M, d, dtype="f16", seed=0, a=4.0, slope=6.0, v_scale=0.25):
