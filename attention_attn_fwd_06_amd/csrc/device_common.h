@@ -74,6 +74,16 @@ __device__ __forceinline__ f32x2 unpack2(uint32_t u) {
   }
 }
 
+// This lane's index in the wave, read afresh at each call (asm volatile, so
+// neither hoisted nor merged with another read): a value the compiler would
+// otherwise keep in a register for the whole kernel is recomputed where it is
+// needed, in two instructions.
+__device__ __forceinline__ uint32_t lane_id_now() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // x, hidden from the optimiser: values computed from the result inside a loop
 // cannot be hoisted out of it, so a loop-invariant per-lane base plus several
 // per-iteration offsets costs one register instead of one per offset.

@@ -208,6 +208,23 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[kKB], uint32_t k_tile, uint3
   }
 }
 
+// The same with 16-bit K and this lane's K operand address of each step t
+// in K buffer 0 given (kaddr[t]; k_tile selects the buffer).
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile_addr(f32x16 (&s)[kKB], uint32_t k_tile, const uint32_t (&kaddr)[D / 16],
+                                             const s16x8 (&qreg)[D / 16]) {
+#pragma unroll
+  for (int kb = 0; kb < kKB; ++kb) s[kb] = (f32x16){};
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      const s16x8 a = lds_read_b128(kaddr[t] + k_tile + (uint32_t)(kb * 32 * D * 2));
+      s[kb] = mfma32x32x16<BF16>(a, qreg[t], s[kb]);
+    }
+  }
+}
+
 // Division of a non-negative int below 2^31 by a fixed divisor d >= 1 with a
 // multiplier and a shift worked out on the host (round-up method of
 // Granlund and Montgomery): q = (mulhi(n, mul) + n) >> shift, with
@@ -244,6 +261,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   constexpr int kEB = QK8 ? 1 : 2;  // bytes per q or k element
   // LDS: K buffers 0, 1, V buffers 0, 1 (64 KB at d = 128; 48 KB with FP8 K).
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(2 * kTBK + 2 * kTB) / 2];
+  __shared__ int restart_flag[kWaves];  // bf16: a wave's pass left its range (see the KV pass)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u16*)smem;
   const uint32_t kbuf0 = lds0, vbuf0 = lds0 + 2 * kTBK;
 
@@ -274,7 +292,10 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   const int q_start = qt * rows;
   const int qw = q_start + (wave & ((1 << wshift) - 1)) * 32;  // first query of this wave
   const int qlast = qw + 31;           // last query of this wave
-  const int qi = qw + l32;             // this lane's query
+  const int qi = qw + l32;             // this lane's query (prologue; see query_now)
+  // the same, recomputed where the general steps and the epilogue need it,
+  // instead of one register held for the whole kernel
+  auto query_now = [&]() __attribute__((always_inline)) { return qw + (int)(lane_id_now() & 31); };
 
   // element strides {batch, token, head}; k and v share their token stride
   // (in elements; FP8 k elements are bytes)
@@ -329,6 +350,14 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   LdsAddr<D> la;
   la.k_row = lds0 + (uint32_t)l32 * Gq::kDK * 2;
   la.kx = (uint32_t)((g ^ swz<Gq::kDK>(l32)) << 4);
+  // 16-bit Q and K: this lane's K operand address of each contraction step t
+  // in K buffer 0, worked out once per item; the K buffer (16 KB apart) and
+  // the 32-key block (8 KB) are instruction offsets of the reads.
+  uint32_t kaddr[QK8 ? 1 : kDT];
+  if constexpr (!QK8) {
+#pragma unroll
+    for (int t = 0; t < kDT; ++t) kaddr[t] = la.k_row + ((uint32_t)(32 * t) ^ la.kx);
+  }
   {
     // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4
     // of the 8 bytes addressed by lane 4*jj + i/4, for jj = 0..3.  Lane s of
@@ -348,15 +377,11 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
   }
 
-  wait_tile_loads();
-  kv_barrier();
   f32x16 s_a[kKB], s_b[kKB];  // S of the current tile is always in s_a between steps
-  qk_tile<D, BF16, QK8>(s_a, 0, la.k_row, la.kx, qreg);
-  kv_barrier();  // K buffer 0 is refilled in iteration 0
 
   // O^T += V(j)^T P(j) for one 16-key k-step (kb, st) and all d blocks; v_tile
   // is the V buffer's offset from V buffer 0.
-  auto pv_kstep = [&](uint32_t v_tile, int kb, int st, const s16x8& pb, const s16x8* pl) {
+  auto pv_kstep = [&](uint32_t v_tile, int kb, int st, const s16x8& pb, const s16x8* pl) __attribute__((always_inline)) {
     const uint32_t koff = v_tile + (uint32_t)((32 * kb + 16 * st) * D * 2);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
@@ -368,8 +393,21 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
   };
 
+  // Multiply O and l by alpha = 2^(m_run - m_new) when the reference max moves
+  // up to m_new.  alpha is applied as two factors 2^((m_run - m_new) / 2):
+  // after a max-free pass (bf16) the reference can lag by up to about 2^7
+  // while O and l carry the same factor 2^lag, and a single factor would fall
+  // below fp32's normal range although the products do not.
+  auto move_reference_to = [&](const float m_new) __attribute__((always_inline)) {
+    const float half = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(0.5f * (m_run - m_new));
+    l_run = l_run * half * half;
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) acc_o[i] = acc_o[i] * half * half;
+    m_run = m_new;
+  };
+
   // Row max of tile j and the rare move of the reference max (see below).
-  auto row_max_update = [&](f32x16 (&s_cur)[kKB]) {
+  auto row_max_update = [&](f32x16 (&s_cur)[kKB]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -380,12 +418,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     // Move the reference max only when it grows by more than 2^8; otherwise
     // p may reach 2^8, which fp32 accumulation and 16-bit P represent fine.
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < kDB; ++i) acc_o[i] *= alpha;
-      m_run = m_new;
+      move_reference_to(fmaxf(m_run, m_tile));
     }
   };
 
@@ -394,7 +427,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // keys 32*kb + 16*st + 8*(jj/4) + 4*g + jj%4 for slot jj.  The row sum l is
   // accumulated from the unrounded fp32 p (a sum of 16-bit-rounded weights
   // can be off by 2^-9 relative when a few keys dominate, too much for lse).
-  auto exp_pack = [&](const f32x16& sv, int st, float m_use, float& lsum, bool masked, s16x8& pb, s16x8* pl) {
+  auto exp_pack = [&](const f32x16& sv, int st, float m_use, float& lsum, bool masked, s16x8& pb, s16x8* pl) __attribute__((always_inline)) {
     float pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -424,7 +457,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // fetches K(j+2) and V(j+1), computes S(j+1) into s_b if this wave needs it,
   // then mask, softmax and PV of tile j from s_a; ends with S(j+1) in s_a.  The
   // buffer parity is a run-time value here (these steps are few).
-  auto step_general = [&](const int j, auto first) {
+  auto step_general = [&](const int j, auto first) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
     // bf16: P is split into hi + lo parts on the first tile
     constexpr bool kSplit = BF16 && kFirst;
@@ -433,16 +466,22 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int n0 = j * kBN;
     if (j + 2 < n_tiles) FK::tile(kdesc, kbuf0 + par * kTBK, n0 + 2 * kBN, wave, voffk, k_row_bytes);
     if (j + 1 < n_tiles) F::tile(vdesc, vbuf0 + (1 - par) * kTB, n0 + kBN, wave, voff, kv_row_bytes);
-    if (j + 1 < wave_tiles) qk_tile<D, BF16, QK8>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
+    if (j + 1 < wave_tiles) {
+      if constexpr (QK8)
+        qk_tile<D, BF16, QK8>(s_b, k_next, la.k_row, opaque(la.kx), qreg);
+      else
+        qk_tile_addr<D, BF16>(s_b, k_next, kaddr, qreg);
+    }
     if (j < wave_tiles) {
       const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw + causal_off) || (n0 + kBN > M);
       if (need_mask) {
+        const int qn = query_now();
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool ok = key < M && (!CAUSAL || key <= qi + causal_off);
+            const bool ok = key < M && (!CAUSAL || key <= qn + causal_off);
             s_a[kb][i] = ok ? s_a[kb][i] : -INFINITY;
           }
       }
@@ -466,7 +505,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   };
 
   // Raw row max of a tile's S (unscaled, over this lane and lane ^ 32).
-  auto tile_max = [&](const f32x16 (&sv)[kKB]) {
+  auto tile_max = [&](const f32x16 (&sv)[kKB]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -485,29 +524,30 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // MFMAs have finished by then), which the next step uses.  The slots are
   // separated by scheduling fences, so the order is the one written here.
   // mx: row max of tile j on entry, of tile j+1 on return.  first: j == 0.
+  // exact == false (bf16 P only): the step neither takes the row max of
+  // S(j+1) nor moves the reference max, which stays where the first tile put
+  // it (see the KV pass below).
   auto step_fast = [&](const uint32_t k_next, const uint32_t v_cur, f32x16 (&s_cur)[kKB],
-                       f32x16 (&s_next)[kKB], float& mx, auto&& fetch, auto first) {
+                       f32x16 (&s_next)[kKB], float& mx, auto&& fetch, auto first, auto exact) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
-    if constexpr (kFirst) {
-      // O and l are still zero: the reference max is simply set
-      m_run = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
-    } else {
+    constexpr bool kExact = decltype(exact)::value;
+    static_assert(kExact || BF16, "16-bit P without a moving reference needs bf16's range");
+    auto move_reference = [&]() __attribute__((always_inline)) {
       // mx is finite here: the tile has no masked key (inputs holding Inf or
       // NaN give NaN outputs either way)
       const float m_tile = mx * scale_log2;
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.0f)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) acc_o[i] *= alpha;
-        m_run = m_new;
+        move_reference_to(fmaxf(m_run, m_tile));
       }
+    };
+    if constexpr (kFirst) {
+      // O and l are still zero: the reference max is simply set
+      m_run = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+    } else if constexpr (kExact) {
+      move_reference();
     }
-    // fresh copies per step keep the per-step K addresses from being hoisted
-    // out of the KV loop as kDT live registers; the address of contraction
-    // step t is then one v_xad_u32, and the second 32-key block is an
-    // instruction offset
+    // FP8 K: fresh copies per step keep the per-step K addresses from being
+    // hoisted out of the KV loop as live registers (16-bit K uses kaddr)
     const uint32_t kx = opaque(la.kx);
     const uint32_t kbase = opaque(la.k_row + k_next);
     constexpr int kNQ = 2 * kDT, kNP = 4 * kDB, kN = kNQ + kNP;
@@ -521,15 +561,14 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     float lsum = 0.f, mxn = -INFINITY;
     const float neg_m = (kFirst && m_run == -INFINITY) ? 0.f : -m_run;
 
-    auto reads = [&](const int i) {
+    auto reads = [&](const int i) __attribute__((always_inline)) {
       if (i < kNQ) {
         const int t = i >> 1, kb = i & 1;
         if (kb == 0) qv[t] = qreg[t];
         if constexpr (QK8) {
           ka[i] = k_operand<D, QK8>(kx, kbase + (uint32_t)(kb * 32 * Gq::kDK * 2), t);
         } else {
-          const uint32_t row_t = xor_add(kx, (uint32_t)(32 * t), kbase);
-          ka[i] = lds_read_b128(row_t + (uint32_t)(kb * 32 * D * 2));
+          ka[i] = lds_read_b128(kaddr[t] + k_next + (uint32_t)(kb * 32 * D * 2));
         }
       } else if (i < kN) {
         const int pi = i - kNQ, ks = pi / kDB, db = pi % kDB;
@@ -540,7 +579,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
       }
     };
     // element e of P k-step ks (see exp_pack for the key order)
-    auto exp_elem = [&](const int k) {
+    auto exp_elem = [&](const int k) __attribute__((always_inline)) {
       const int ks = k >> 3, e = k & 7;
       const float y = __builtin_amdgcn_exp2f(fmaf(s_cur[ks >> 1][8 * (ks & 1) + e], scale_log2, neg_m));
       pe[ks][e] = y;
@@ -572,7 +611,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
       for (int k = 0; k < 32; ++k)
         if (k * kExpEnd / 32 == i) exp_elem(k);
-      if (i >= kExpEnd) {
+      if (kExact && i >= kExpEnd) {
         // row max of S(j+1), spread over the slots after the exp work
         constexpr int kMaxSlots = kN - kExpEnd;
         const int r = i - kExpEnd;
@@ -590,7 +629,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // between tiles): S(j+1) reads K buffer 1-P, PV(j) reads V buffer P, and the
   // iteration fetches K(j+2) into K buffer P and V(j+1) into V buffer 1-P.
   auto step_fast_p = [&](const int j, f32x16 (&s_cur)[kKB], f32x16 (&s_next)[kKB], float& mx, auto parity,
-                         auto first) {
+                         auto first, auto exact) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     const uint32_t k_fill = kbuf0 + P * kTBK, v_fill = vbuf0 + (1 - P) * kTB;
     const int n0 = j * kBN;
@@ -602,7 +641,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const i32x4 d2 = has_k ? kdesc : vdesc;
     const uint32_t l2 = has_k ? k_fill : v_fill;
     const int r2 = has_k ? n0 + 2 * kBN : n0 + kBN;
-    auto fetch = [&](int i) {
+    auto fetch = [&](int i) __attribute__((always_inline)) {
       if (i < F::kInst)
         F::issue(vdesc, v_fill, n0 + kBN, i, wave, voff, kv_row_bytes);
       else if constexpr (QK8)
@@ -610,7 +649,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
       else
         F::issue(d2, l2, r2, i - F::kInst, wave, voff, kv_row_bytes);
     };
-    step_fast((1 - P) * kTBK, P * kTB, s_cur, s_next, mx, fetch, first);
+    step_fast((1 - P) * kTBK, P * kTB, s_cur, s_next, mx, fetch, first, exact);
     wait_tile_loads();
     kv_barrier();
   };
@@ -620,30 +659,81 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // Every wave runs n_tiles steps, each ending in one barrier.
   const int fast_end =
       min(min(wave_tiles - 1, M / kBN), CAUSAL ? (qw + causal_off + 1) / kBN : wave_tiles);
-  // tile 0 takes the steady-state path too when it has no masked key and S(1)
-  // is needed (fast_end >= 1); O and l start at zero there
-  float mx;  // row max of the tile in s_a, carried by the fast steps
-  if (fast_end >= 1) {
-    mx = tile_max(s_a);
-    step_fast_p(0, s_a, s_b, mx, std::integral_constant<int, 0>{}, std::true_type{});
+
+  // One pass over the KV tiles: S(0) from K(0) (fetched before the pass), then
+  // every tile through the steady-state or the general step.
+  auto kv_pass = [&](auto exact) __attribute__((always_inline)) {
+    wait_tile_loads();
+    kv_barrier();
+    if constexpr (QK8)
+      qk_tile<D, BF16, QK8>(s_a, 0, la.k_row, la.kx, qreg);
+    else
+      qk_tile_addr<D, BF16>(s_a, 0, kaddr, qreg);
+    kv_barrier();  // K buffer 0 is refilled in iteration 0
+    // tile 0 takes the steady-state path too when it has no masked key and S(1)
+    // is needed (fast_end >= 1); O and l start at zero there
+    float mx;  // row max of the tile in s_a, carried by the fast steps
+    if (fast_end >= 1) {
+      mx = tile_max(s_a);
+      step_fast_p(0, s_a, s_b, mx, std::integral_constant<int, 0>{}, std::true_type{}, exact);
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+      for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+    } else {
+      step_general(0, std::true_type{});
+      mx = tile_max(s_a);
+    }
+    int j = 1;
+    for (; j + 1 < fast_end; j += 2) {
+      step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{}, exact);
+      step_fast_p(j + 1, s_b, s_a, mx, std::integral_constant<int, 0>{}, std::false_type{}, exact);
+    }
+    if (j < fast_end) {
+      step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{}, exact);
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
+      ++j;
+    }
+    for (; j < n_tiles; ++j) step_general(j, std::false_type{});
+  };
+
+  // bf16 P: the steady-state steps first run without a moving reference max
+  // (the reference is the first tile's row max; the general steps still move
+  // it).  Tiles whose scores exceed it give large weights, which bf16 and the
+  // fp32 accumulators hold at full relative precision up to 2^127, so the
+  // result is the same up to rounding.  A pass whose scores outgrew that range
+  // leaves l >= 2^100 or an accumulator that is no longer finite; then the
+  // whole workgroup runs the pass again with the exact steps (all four waves
+  // share the K/V fetches, so the decision is taken jointly through LDS).
+  // 16-bit P in fp16 (largest value 65504) always takes the exact steps, and
+  // so does head dim 256, whose max-free instance the compiler cannot build
+  // with the fetch descriptors in scalar registers.
+  if constexpr (BF16 && D <= 128) {
+    kv_pass(std::false_type{});
+    float z = 0.f;  // NaN iff some O accumulator is Inf or NaN
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z = fmaf(acc_o[db][i], 0.f, z);
+    const bool bad = !(l_run < 0x1p100f) || z != z;
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) restart_flag[wave] = wave_bad ? 1 : 0;
+    __syncthreads();
+    // uniform by construction; readfirstlane tells the compiler so
+    const bool again =
+        __builtin_amdgcn_readfirstlane(restart_flag[0] | restart_flag[1] | restart_flag[2] | restart_flag[3]) != 0;
+    if (again) {
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDB; ++i) acc_o[i] = (f32x16){};
+      FK::tile(kdesc, kbuf0, 0, wave, voffk, k_row_bytes);
+      F::tile(vdesc, vbuf0, 0, wave, voff, kv_row_bytes);
+      if (n_tiles > 1) FK::tile(kdesc, kbuf0 + kTBK, kBN, wave, voffk, k_row_bytes);
+      kv_pass(std::true_type{});
+    }
   } else {
-    step_general(0, std::true_type{});
-    mx = tile_max(s_a);
+    kv_pass(std::true_type{});
   }
-  int j = 1;
-  for (; j + 1 < fast_end; j += 2) {
-    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{});
-    step_fast_p(j + 1, s_b, s_a, mx, std::integral_constant<int, 0>{}, std::false_type{});
-  }
-  if (j < fast_end) {
-    step_fast_p(j, s_a, s_b, mx, std::integral_constant<int, 1>{}, std::false_type{});
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
-    ++j;
-  }
-  for (; j < n_tiles; ++j) step_general(j, std::false_type{});
 
   // ---- epilogue: O / l -> 16-bit, lse = ln2 * (m + log2 l) ----
   // Lane (l32, g) holds d = 32 db + 8 r + 4 g + (0..3) of its query row: half g
@@ -684,7 +774,8 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
         *reinterpret_cast<s16x8*>(o + b * st.o[0] + (int64_t)qrow * st.o[1] + h * st.o[2] + 8 * c) = val[k];
     }
   }
-  if (lse != nullptr && g == 0 && qi < N) lse[((int64_t)b * Hq + h) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+  const int qe = query_now();
+  if (lse != nullptr && g == 0 && qe < N) lse[((int64_t)b * Hq + h) * N + qe] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // Host-side launcher (one instance per head dim, dtype, mask and Q/K format).

@@ -1,7 +1,9 @@
 """The ramped-score prefill cases reach the kernel's rescale of the reference
-maximum on both code paths (host emulation of the kernel's tile maxima; no
-GPU).  The GPU parity test of the same cases is ``test_prefill_rescale_branch``
-in test_parity_gpu.py."""
+maximum on both code paths, and with bf16 P both outcomes of the max-free
+pass (kept with weights far above the reference, or rerun with the exact
+steps), by host emulation of the kernel's tile maxima and row sums (no GPU).
+The GPU parity test of the same cases is ``test_prefill_rescale_branch`` in
+test_parity_gpu.py."""
 import numpy as np
 import pytest
 
@@ -9,7 +11,8 @@ from tests.rescale_emu import rescale_events
 from workloads import prefill_inputs, prefill_ramp_inputs
 
 # B, N, M, Hq, Hkv, d, dtype, causal: causal with N == M and N < M, non-causal,
-# fp16 and bf16, head dims 64 and 128, GQA and MHA
+# fp16 and bf16, head dims 64 and 128, GQA and MHA; the last three are long
+# enough for bf16 workgroups to outgrow the max-free pass and rerun it
 RESCALE_CASES = [
     (1, 1024, 1024, 4, 2, 128, "bf16", True),
     (1, 1024, 1024, 4, 4, 64, "f16", True),
@@ -17,6 +20,9 @@ RESCALE_CASES = [
     (1, 200, 700, 4, 2, 64, "bf16", True),
     (1, 256, 1000, 2, 2, 64, "bf16", False),
     (2, 512, 512, 8, 2, 128, "f16", False),
+    (1, 2048, 2048, 2, 2, 64, "bf16", True),
+    (1, 512, 2048, 2, 2, 64, "bf16", False),
+    (1, 1024, 4096, 4, 2, 128, "bf16", False),
 ]
 RESCALE_SEED = 11
 
@@ -27,18 +33,54 @@ def rescale_case_inputs(case):
     return q, k, v, float(np.float32(d ** -0.5))
 
 
+def max_free(case):
+    """The kernel runs a max-free first pass for bf16 P up to head dim 128."""
+    return case[6] == "bf16" and case[5] <= 128
+
+
+def case_events(case):
+    q, k, v, scale = rescale_case_inputs(case)
+    return rescale_events(q, k, scale, case[-1], max_free=max_free(case))
+
+
+def check_case_events(case, ev):
+    """What a ramped case must reach: the general path's rescale, and on the
+    steady-state path the exact rescale (fp16) or, with bf16, growth the
+    max-free pass keeps or a rerun; no workgroup too close to call."""
+    assert ev["general"] > 0 and ev["uncertain"] == 0, ev
+    if max_free(case):
+        assert ev["free_growth"] > 0 or (ev["restart"] > 0 and ev["fast"] > 0), ev
+    else:
+        assert ev["fast"] > 0 and ev["restart"] == 0, ev
+
+
 @pytest.mark.parametrize("case", RESCALE_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_ramp_inputs_rescale_on_both_paths(case):
-    q, k, v, scale = rescale_case_inputs(case)
-    ev = rescale_events(q, k, scale, case[-1])
-    assert ev["fast"] > 0 and ev["general"] > 0, ev
+    check_case_events(case, case_events(case))
     # |O| stays below 2, where the bf16 output's half-ulp is below the bound
+    _, _, v, _ = rescale_case_inputs(case)
     assert float(v.abs().max()) < 1.5
+
+
+def test_bf16_cases_reach_both_outcomes_of_the_max_free_pass():
+    """Some bf16 workgroups keep a max-free pass whose steady tiles exceeded
+    the reference by far more than 8 (up to about 2^100 in the row sums), and
+    some rerun the pass with the exact steps, which then rescale on the
+    steady-state path."""
+    evs = [case_events(c) for c in RESCALE_CASES if max_free(c)]
+    assert any(ev["free_growth"] > 0 and ev["max_jump"] > 60 for ev in evs), evs
+    assert any(ev["restart"] > 0 and ev["fast"] > 0 for ev in evs), evs
+    assert any(ev["free_growth"] > 0 and ev["restart"] > 0 for ev in evs), evs
+    # a kept pass whose reference then moves by more than 126 log2 units: the
+    # kernel applies that rescale as two factors, each within fp32's range
+    assert any(ev["max_lag"] > 126.5 for ev in evs), evs
 
 
 def test_plain_inputs_never_rescale():
     """The i.i.d. N(0, 1) inputs of the other parity cases never move the
     reference max (which is why the ramped cases exist)."""
     q, k, _ = prefill_inputs(2, 8, 2, 1024, 1024, 128, "bf16", 0)
-    ev = rescale_events(q, k, float(np.float32(128 ** -0.5)), True)
-    assert ev["fast"] == 0 and ev["general"] == 0 and ev["max_jump"] < 8.0, ev
+    for free in (False, True):
+        ev = rescale_events(q, k, float(np.float32(128 ** -0.5)), True, max_free=free)
+        assert ev["fast"] == 0 and ev["general"] == 0 and ev["max_jump"] < 8.0, ev
+        assert ev["restart"] == 0 and ev["free_growth"] == 0 and ev["uncertain"] == 0, ev
