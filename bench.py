@@ -2,17 +2,18 @@
 
 One step = one causal GQA bf16 prefill forward (B=4, Hq=32, Hkv=8,
 N=M=4096, d=128) plus one split-KV decode (B=2, H=8, M=65536, d=128, fp16,
-chunk 128: partial kernel + LSE merge), all through the C ABI, with inputs
-already resident in HBM.  The decode rotates between two independent K/V sets
-(1.07 GB together) so the 256 MB last-level cache cannot serve repeats.
+chunks of 128 keys: partials and LSE merge in one launch), all through the C
+ABI, with inputs already resident in HBM.  The decode rotates between two
+independent K/V sets (1.07 GB together) so the 256 MB last-level cache cannot
+serve repeats.
 
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 (4*B*Hq*N*M*d, halved for the causal mask) over the prefill kernel's average
 duration, measured with HIP events on the launch stream; the decode result is
-reported in the ``decode`` object: GB/s of K+V+q+O over the one-launch decode
-(partials and merge fused, timed on its own), with the two-launch path of the
-step (chunk + merge) beside it; ``decode_fused`` repeats the one-launch figure
-with its kernel name.  ``configs`` holds all five
+reported in the ``decode`` object: GB/s of K+V+q+O over the step's one-launch
+decode, with the two-launch path (chunk kernel + merge) and the chunk kernel
+alone, timed after the steps, beside it; ``roofline_decode`` is the one-launch
+decode kernel's roofline.  ``configs`` holds all five
 workloads (tiny MHA and small decode as latencies, the MHA fp16 d=64 prefill
 as TFLOP/s, the two headline workloads), each with the largest deviation from
 the CPU oracle over its whole output (checked after the timed region).  The
@@ -65,21 +66,22 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kind: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the summary is missing or was taken on a different kernel source."""
+def read_traffic(kind: str, workload: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (the summary line ``key``) from the committed
+    rocprofv3 counter summary, or None when the summary is missing or was
+    taken on a different kernel source."""
     p = ROOT / "profiles" / f"{kind}_{workload}_traffic.md"
     if not p.exists():
         return None
     vals = {}
     for line in p.read_text().splitlines():
         if ":" in line and line.startswith("- "):
-            key, val = line[2:].split(":", 1)
-            vals[key.strip()] = val.strip().strip("`")
+            name, val = line[2:].split(":", 1)
+            vals[name.strip()] = val.strip().strip("`")
     if vals.get("kernel_source_sha256") != source_hash(kind):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -417,6 +419,8 @@ def main():
         lse_part = torch.empty((wd.B, wd.Hq, C), dtype=torch.float32, device=dev)
         do_ = torch.empty((wd.B, wd.Hq, wd.d), dtype=torch.float16, device=dev)
         dlse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+        dws = torch.zeros(attn.attn_decode_fused_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d),
+                          dtype=torch.uint8, device=dev)
 
     stream = torch.cuda.current_stream()
 
@@ -426,20 +430,24 @@ def main():
             attn.attn_fwd(q, k, v, causal=True, scale=wp.scale, o=o, lse=lse, stream=stream)
             if ev: ev[1].record(stream)
         if do_d:
-            # no event between the two launches: one there adds about 3 us of its own
+            # the decode in one launch: chunk partials and their merge
             kk, vv = kv_sets[i % 2]
             if ev: ev[2].record(stream)
-            attn.attn_decode_splitkv(dq, kk, vv, wd.chunk, wd.scale, o_part=o_part, lse_part=lse_part,
-                                     stream=stream)
-            attn.lse_merge(o_part, lse_part, o=do_, lse=dlse, stream=stream)
+            attn.attn_decode_fused(dq, kk, vv, wd.scale, o=do_, lse=dlse, workspace=dws, stream=stream)
             if ev: ev[3].record(stream)
 
-    def chunk_only(i, ev):
+    def chunk_merge(i):
+        # the two-launch path; no event between the launches (one there adds
+        # about 3 us of its own)
         kk, vv = kv_sets[i % 2]
-        ev[0].record(stream)
         attn.attn_decode_splitkv(dq, kk, vv, wd.chunk, wd.scale, o_part=o_part, lse_part=lse_part,
                                  stream=stream)
-        ev[1].record(stream)
+        attn.lse_merge(o_part, lse_part, o=do_, lse=dlse, stream=stream)
+
+    def chunk_only(i):
+        kk, vv = kv_sets[i % 2]
+        attn.attn_decode_splitkv(dq, kk, vv, wd.chunk, wd.scale, o_part=o_part, lse_part=lse_part,
+                                 stream=stream)
 
     # The GPU reaches its sustained clock only after about a second of load:
     # run untimed steps for --prewarm-s seconds, then the counted warm-up.
@@ -459,16 +467,10 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     if do_d:
-        # the chunk kernel alone (its roofline), timed after the steps
-        c_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            chunk_only(i, c_events[i])
-        torch.cuda.synchronize()
-        # the same decode in one launch (partials and merge fused)
-        ws = torch.zeros(attn.attn_decode_fused_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d), dtype=torch.uint8,
-                         device=dev)
-        f_ms = _time_chunk(lambda i: attn.attn_decode_fused(dq, kv_sets[i % 2][0], kv_sets[i % 2][1], wd.scale, o=do_,
-                                                            lse=dlse, workspace=ws, stream=stream), args)
+        # the same decode in two launches (chunk kernel + merge), and the chunk
+        # kernel alone, timed after the steps
+        cm_ms = _time_chunk(chunk_merge, args)
+        c_ms = _time_chunk(chunk_only, args)
 
     out = {
         "metric": "attn fwd TFLOP/s & % MFMA peak (prefill); decode HBM GB/s & % peak",
@@ -490,30 +492,25 @@ def main():
                            "traffic": traffic, "kernel": "prefill_fwd_kernel<128,bf16,causal>",
                            "per_launch": f"{flops:.6g} FLOP (causal-halved)"}
     if do_d:
-        d_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in events)
-        c_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in c_events)
+        f_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in events)
         nbytes = decode_bytes(wd.B, wd.Hq, wd.Hkv, wd.M, wd.d)
         chunk_bytes = nbytes - wd.B * wd.Hq * wd.d * 2  # K+V+q (O is written by the merge)
-        gbps = nbytes / (d_ms * 1e-3) / 1e9
+        gbps = nbytes / (cm_ms * 1e-3) / 1e9
         f_gbps = nbytes / (f_ms * 1e-3) / 1e9
-        # the decode's headline is its one-launch path (attn_decode_fused); the
+        # the step's decode is the one-launch path (attn_decode_fused); the
         # two-launch path (attn_decode_splitkv + lse_merge) is reported beside it
         out["decode"] = {"value": round(f_gbps, 1), "unit": "GB/s", "frac": round(f_gbps / PEAK_HBM_GBPS, 4),
                          "dtype": "f16", "ms": round(f_ms, 4), "path": "attn_decode_fused (one launch)",
-                         "chunk_merge_ms": round(d_ms, 4), "chunk_merge_GBps": round(gbps, 1),
+                         "chunk_merge_ms": round(cm_ms, 4), "chunk_merge_GBps": round(gbps, 1),
                          "chunk_merge_frac": round(gbps / PEAK_HBM_GBPS, 4), "chunk_ms": round(c_ms, 4),
                          "chunk_only_GBps": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
                          "algorithmic_bytes": nbytes}
-        out["decode_fused"] = {"value": round(nbytes / (f_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                               "frac": round(nbytes / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "ms": round(f_ms, 4),
-                               "kernel": "decode_gqa_mfma_kernel<128,f16,fused>",
-                               "note": "partials of 128-key chunk runs and their merge in one launch"}
-        out["roofline_decode"] = {"bound": "hbm", "achieved": round(chunk_bytes / (c_ms * 1e-3) / 1e9, 1),
+        out["roofline_decode"] = {"bound": "hbm", "achieved": round(f_gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                  "frac": round(chunk_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                                  "traffic": read_traffic("decode", DECODE),
-                                  "kernel": "decode_gqa_mfma_kernel<128,f16>",
-                                  "per_launch": f"{chunk_bytes:.6g} B (K+V+q)"}
+                                  "frac": round(f_gbps / PEAK_HBM_GBPS, 4),
+                                  "traffic": read_traffic("decode", DECODE, "fused_hbm_bytes_per_launch"),
+                                  "kernel": "decode_gqa_mfma_kernel<128,f16,fused>",
+                                  "per_launch": f"{nbytes:.6g} B (K+V+q read, O written)"}
         if not do_p:
             out["value"], out["unit"], out["dtype"] = out["decode"]["value"], "GB/s", "f16"
     if args.only in (None, "decode_gqa"):
