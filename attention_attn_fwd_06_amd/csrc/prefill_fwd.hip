@@ -39,8 +39,14 @@
 //    transposed V reads free of bank conflicts; tile rows past M come back as
 //    zeros from bounds-checked buffer loads (no branches).
 //  * exp2 domain with scale*log2(e) folded into one FMA; the O / l rescale is
-//    skipped unless some row's max grew by more than 2^8 (exact: O and l
-//    always share the same reference max).
+//    skipped unless some row's max grew by more than 2^8 (O and l always
+//    share the same reference max, so the result is the same up to rounding).
+//  * bf16 P (head dims up to 128): the steady-state steps of a first pass do
+//    not track the row max at all; the reference stays at the first tile's
+//    row max (the masked steps still move it), and weights above it keep
+//    their relative precision in bf16 and fp32 up to 2^127.  A workgroup whose
+//    pass ends with a row sum of 2^100 or more, or with a non-finite
+//    accumulator, runs the pass again with the exact steps.
 //  * bf16 only: where a wave's first KV tile is masked or is its only tile
 //    (rows with at most 64 keys: early causal rows, where |O| is large), P of
 //    that tile is split into hi + lo bf16 parts (two PV MFMAs), so those rows
