@@ -82,6 +82,25 @@ __device__ __forceinline__ void dma16(i32x4 desc, uint32_t lds, uint32_t voff) {
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc)
                  : "memory", "m0");
 }
+// The same with a uniform byte offset soff in the instruction's scalar offset
+// operand: the bounds check covers voff + soff (measured on gfx950: bytes at
+// or past the buffer's size read as zero also when soff takes them there), so
+// a tile's row offset needs no per-lane add.
+template <bool kStream = false>
+__device__ __forceinline__ void dma16_so(i32x4 desc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(desc),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

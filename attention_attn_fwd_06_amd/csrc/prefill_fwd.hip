@@ -108,10 +108,11 @@ struct Fetch {
     return o;
   }
   // instruction i of the tile starting at key row n0, into the LDS tile at lds_tile
+  // (the tile's row offset goes in the scalar offset operand)
   static __device__ __forceinline__ void issue(i32x4 desc, uint32_t lds_tile, int n0, int i, int wave,
                                                const Voff& voff, int row_stride_bytes) {
-    dma16(desc, lds_tile + (uint32_t)(i * kWaves + wave) * kInstBytes,
-          voff.v[i % kVar] + (uint32_t)(n0 + kRowsPerInst * i) * (uint32_t)row_stride_bytes);
+    dma16_so(desc, lds_tile + (uint32_t)(i * kWaves + wave) * kInstBytes, voff.v[i % kVar],
+             (uint32_t)(n0 + kRowsPerInst * i) * (uint32_t)row_stride_bytes);
   }
   static __device__ __forceinline__ void tile(i32x4 desc, uint32_t lds_tile, int n0, int wave, const Voff& voff,
                                               int row_stride_bytes) {
