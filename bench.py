@@ -177,6 +177,7 @@ def gqa_decode_rate(attn, w, args, dev):
         attn.lse_merge(o_part, lse_part, o=o, lse=lse, stream=stream)
         if ev: ev[2].record(stream)
 
+    _prewarm(step, args)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -203,10 +204,27 @@ def gqa_decode_rate(attn, w, args, dev):
             "bytes_note": "K and V counted once per kv head"}
 
 
+def _prewarm(fn, args):
+    """Untimed calls of fn(i) for up to half a second (at most --prewarm-s):
+    each measurement starts after the input set-up on the host, an idle spell
+    in which the GPU drops its clock, and the clock ramps up again only under
+    load."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < min(0.5, args.prewarm_s):
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def _time_chunk(fn, args):
-    """Mean HIP-event time (ms) of fn(i) on the current stream over args.steps calls."""
+    """Mean HIP-event time (ms) of fn(i) on the current stream over args.steps
+    calls, after the pre-warm and args.warmup untimed calls."""
     import torch
     stream = torch.cuda.current_stream()
+    _prewarm(fn, args)
     for i in range(args.warmup):
         fn(i)
     torch.cuda.synchronize()
