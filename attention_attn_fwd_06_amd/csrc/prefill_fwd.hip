@@ -41,11 +41,12 @@
 //  * exp2 domain with scale*log2(e) folded into one FMA; the O / l rescale is
 //    skipped unless some row's max grew by more than 2^8 (O and l always
 //    share the same reference max, so the result is the same up to rounding).
-//  * bf16 P (head dims up to 128): the steady-state steps of a first pass do
-//    not track the row max at all; the reference stays at the first tile's
-//    row max (the masked steps still move it), and weights above it keep
-//    their relative precision in bf16 and fp32 up to 2^127.  A workgroup whose
-//    pass ends with a row sum of 2^100 or more, or with a non-finite
+//  * head dims up to 128: the steady-state steps of a first pass do not
+//    track the row max at all; the reference stays at the first tile's row
+//    max (the masked steps still move it), and weights above it keep their
+//    relative precision in P and fp32 up to P's largest value (2^127 in
+//    bf16, 65504 in fp16).  A workgroup whose pass ends with a lane's row sum
+//    of 2^100 (bf16) or 2^15 (fp16) or more, or with a non-finite
 //    accumulator, runs the pass again with the exact steps.
 //  * bf16 only: where a wave's first KV tile is masked or is its only tile
 //    (rows with at most 64 keys: early causal rows, where |O| is large), P of
@@ -464,8 +465,13 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // fetches K(j+2) and V(j+1), computes S(j+1) into s_b if this wave needs it,
   // then mask, softmax and PV of tile j from s_a; ends with S(j+1) in s_a.  The
   // buffer parity is a run-time value here (these steps are few).
-  auto step_general = [&](const int j, auto first) __attribute__((always_inline)) {
+  // exact == false (the max-free pass, tiles after the first): the reference
+  // max stays where it is, as in the steady-state steps, so the tile needs no
+  // row max; its masked keys get weight 0 after the exponential instead of a
+  // score of -inf before it.
+  auto step_general = [&](const int j, auto first, auto exact) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
+    constexpr bool kFree = !decltype(exact)::value && !kFirst;
     // bf16: P is split into hi + lo parts on the first tile
     constexpr bool kSplit = BF16 && kFirst;
     const uint32_t par = (uint32_t)(j & 1);
@@ -481,29 +487,59 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
     if (j < wave_tiles) {
       const bool need_mask = (CAUSAL && n0 + kBN - 1 > qw + causal_off) || (n0 + kBN > M);
-      if (need_mask) {
-        const int qn = query_now();
+      // element i of block kb holds key n0 + 4 g + kc(kb, i), kc = 32 kb +
+      // 8 (i / 4) + i % 4; the key is valid iff kc <= lim (key < M and, causal,
+      // key <= query + causal_off)
+      auto key_limit = [&]() __attribute__((always_inline)) {
+        const int last = CAUSAL ? min(query_now() + causal_off, M - 1) : M - 1;
+        return last - n0 - 4 * g;
+      };
+      if constexpr (kFree) {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // finite after tile 0
+        const int lim = need_mask ? key_limit() : kBN;
+        float lsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = n0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool ok = key < M && (!CAUSAL || key <= qn + causal_off);
-            s_a[kb][i] = ok ? s_a[kb][i] : -INFINITY;
+          for (int st = 0; st < 2; ++st) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kc = 32 * kb + 16 * st + 8 * (e >> 2) + (e & 3);
+              const float y = __builtin_amdgcn_exp2f(fmaf(s_a[kb][8 * st + e], scale_log2, -m_use));
+              pv[e] = kc <= lim ? y : 0.f;
+              lsum += pv[e];
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = pack2<BF16>(pv[2 * u], pv[2 * u + 1]);
+            pv_kstep(v_cur, kb, st, __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3])), nullptr);
           }
-      }
-      row_max_update(s_a);
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
+        l_run += lsum;
+      } else {
+        if (need_mask) {
+          const int lim = key_limit();
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
+          for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          s16x8 pb, pl;
-          exp_pack(s_a[kb], st, m_use, lsum, need_mask, pb, kSplit ? &pl : nullptr);
-          pv_kstep(v_cur, kb, st, pb, kSplit ? &pl : nullptr);
+            for (int i = 0; i < 16; ++i) {
+              const int kc = 32 * kb + 8 * (i >> 2) + (i & 3);
+              s_a[kb][i] = kc <= lim ? s_a[kb][i] : -INFINITY;
+            }
         }
-      l_run += lsum;
+        row_max_update(s_a);
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            s16x8 pb, pl;
+            exp_pack(s_a[kb], st, m_use, lsum, need_mask, pb, kSplit ? &pl : nullptr);
+            pv_kstep(v_cur, kb, st, pb, kSplit ? &pl : nullptr);
+          }
+        l_run += lsum;
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
@@ -531,14 +567,13 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // MFMAs have finished by then), which the next step uses.  The slots are
   // separated by scheduling fences, so the order is the one written here.
   // mx: row max of tile j on entry, of tile j+1 on return.  first: j == 0.
-  // exact == false (bf16 P only): the step neither takes the row max of
+  // exact == false: the step neither takes the row max of
   // S(j+1) nor moves the reference max, which stays where the first tile put
   // it (see the KV pass below).
   auto step_fast = [&](const uint32_t k_next, const uint32_t v_cur, f32x16 (&s_cur)[kKB],
                        f32x16 (&s_next)[kKB], float& mx, auto&& fetch, auto first, auto exact) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
     constexpr bool kExact = decltype(exact)::value;
-    static_assert(kExact || BF16, "16-bit P without a moving reference needs bf16's range");
     auto move_reference = [&]() __attribute__((always_inline)) {
       // mx is finite here: the tile has no masked key (inputs holding Inf or
       // NaN give NaN outputs either way)
@@ -686,7 +721,7 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
     } else {
-      step_general(0, std::true_type{});
+      step_general(0, std::true_type{}, exact);
       mx = tile_max(s_a);
     }
     int j = 1;
@@ -700,28 +735,32 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
       for (int kb = 0; kb < kKB; ++kb) s_a[kb] = s_b[kb];
       ++j;
     }
-    for (; j < n_tiles; ++j) step_general(j, std::false_type{});
+    for (; j < n_tiles; ++j) step_general(j, std::false_type{}, exact);
   };
 
-  // bf16 P: the steady-state steps first run without a moving reference max
-  // (the reference is the first tile's row max; the general steps still move
-  // it).  Tiles whose scores exceed it give large weights, which bf16 and the
-  // fp32 accumulators hold at full relative precision up to 2^127, so the
-  // result is the same up to rounding.  A pass whose scores outgrew that range
-  // leaves l >= 2^100 or an accumulator that is no longer finite; then the
-  // whole workgroup runs the pass again with the exact steps (all four waves
-  // share the K/V fetches, so the decision is taken jointly through LDS).
-  // 16-bit P in fp16 (largest value 65504) always takes the exact steps, and
-  // so does head dim 256, whose max-free instance the compiler cannot build
+  // The steady-state steps first run without a moving reference max (the
+  // reference is the first tile's row max; the general steps still move it).
+  // Tiles whose scores exceed it give large weights, which P and the fp32
+  // accumulators hold at full relative precision up to P's largest value, so
+  // the result is the same up to rounding.  A pass whose weights may have
+  // outgrown that range leaves a lane's row sum at or above kRerun (2^100 for
+  // bf16, whose weights reach 2^127; 2^15 for fp16, so that no kept weight
+  // exceeds 2^15 < 65504: a weight that rounded to Inf in fp16 passed 2^15,
+  // and where a general step scaled the sum back below kRerun it left an
+  // accumulator that is not finite), or such an accumulator; then the whole
+  // workgroup runs the pass again with the exact steps (all four waves share
+  // the K/V fetches, so the decision is taken jointly through LDS).  Head dim
+  // 256 always takes the exact steps: its max-free instance does not compile
   // with the fetch descriptors in scalar registers.
-  if constexpr (BF16 && D <= 128) {
+  if constexpr (D <= 128) {
+    constexpr float kRerun = BF16 ? 0x1p100f : 0x1p15f;
     kv_pass(std::false_type{});
     float z = 0.f;  // NaN iff some O accumulator is Inf or NaN
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) z = fmaf(acc_o[db][i], 0.f, z);
-    const bool bad = !(l_run < 0x1p100f) || z != z;
+    const bool bad = !(l_run < kRerun) || z != z;
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) restart_flag[wave] = wave_bad ? 1 : 0;
     __syncthreads();

@@ -12,14 +12,16 @@ than 8.  The tiles go through one of two code paths:
   * the general step (a masked or only first tile, the causal diagonal and
     tail tiles, and the wave's last tile), which tests it after masking.
 
-With bf16 P and head dim up to 128 a workgroup (four waves sharing the K/V
-tiles) first runs a pass whose steady-state steps never move the reference
-(it stays at the first tile's row max, the general steps still move it).  The
-weights of tiles that outgrow the reference are then up to 2^(excess), which
-bf16 and fp32 hold; the pass is rerun with the exact steps when, at its end,
-some lane's row sum is 2^100 or more or a weight or an accumulator
-overflowed.  The emulation follows each row's sum (over both lanes that share
-the row) through the pass, rescales included.
+With head dim up to 128 a workgroup (four waves sharing the K/V tiles) first
+runs a pass whose steady-state steps never move the reference (it stays at
+the first tile's row max, the general steps still move it).  The weights of
+tiles that outgrow the reference are then up to 2^(excess), which P and fp32
+hold up to P's largest value; the pass is rerun with the exact steps when, at
+its end, some lane's row sum is 2^100 (bf16 P) or 2^15 (fp16 P) or more, or a
+weight or an accumulator overflowed (bf16: fp32's range; fp16: a weight of
+65520 or more, which rounds to Inf in P and leaves an accumulator that is not
+finite).  The emulation follows each row's sum (over both lanes that share
+the row) and its largest weight through the pass, rescales included.
 
 This module replays that control flow on the host in float64 (which rows a
 wave owns, which tiles it visits and along which path, the masks, the
@@ -38,19 +40,22 @@ WAVE_ROWS = 32   # query rows per wave
 WAVES = 4        # waves per workgroup
 BM = 128         # query rows per workgroup
 LAZY = 8.0       # log2 units the tile max must exceed the reference by
-RESTART = 100.0  # log2 of a lane's row sum at which the max-free pass is rerun
-OVERFLOW = 127.0  # log2 of a weight, row sum or accumulator that may overflow fp32 (|v| < 2)
+RESTART = {"bf16": 100.0, "f16": 15.0}  # log2 of a lane's row sum at which the max-free pass is rerun
+OVERFLOW = 127.0  # bf16 P: log2 of a weight, row sum or accumulator that may overflow fp32 (|v| < 2)
+F16_INF = math.log2(65520.0)  # fp16 P: log2 of the smallest weight that rounds to Inf
 
 
 def _f64(x):
     return x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
 
 
-def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, margin: float = 0.05):
+def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_dtype: str = "bf16",
+                   margin: float = 0.05):
     """Count the kernel's rescale decisions on inputs q [B,N,Hq,d], k [B,M,Hkv,d].
 
     ``max_free``: the kernel's first pass runs the steady-state steps without
-    a moving reference (bf16 P, head dim <= 128).
+    a moving reference (head dim <= 128); ``p_dtype`` ("bf16" or "f16") is
+    the type of P, which sets when that pass is rerun.
 
     Returns a dict of counts of decisions the kernel surely takes (each more
     than ``margin`` log2 units, far beyond the fp32 rounding of the scores,
@@ -102,7 +107,8 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, mar
         fast_end = min(min(wave_tiles - 1, M // BN), (qw + off + 1) // BN if causal else wave_tiles)
         m_run = np.full(WAVE_ROWS, -math.inf)
         l_row = np.zeros(WAVE_ROWS)
-        out = {"fast": 0, "general": 0, "excess": -math.inf, "l_max": -math.inf, "lag": -math.inf}
+        out = {"fast": 0, "general": 0, "excess": -math.inf, "l_max": -math.inf, "lag": -math.inf,
+               "w_max": -math.inf}
 
         def tile_scores(j, masked):
             t = S[:, j * BN:min((j + 1) * BN, M)] * c
@@ -135,6 +141,7 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, mar
         def accumulate(t):
             nonlocal l_row
             m_use = np.where(m_run == -math.inf, 0.0, m_run)
+            out["w_max"] = max(out["w_max"], float(np.max(t - m_use[:, None])))
             l_row = l_row + np.exp2(t - m_use[:, None]).sum(axis=1)
             out["l_max"] = max(out["l_max"], float(np.log2(np.max(l_row))) if np.max(l_row) > 0 else -math.inf)
 
@@ -171,11 +178,19 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, mar
                     if max_free:
                         l_end = max(r["l_end"] for r in first)
                         l_max = max(r["l_max"] for r in first)
+                        w_max = max(r["w_max"] for r in first)
+                        rs = RESTART[p_dtype]
                         # one of a row's two lanes holds at least half its sum
-                        if l_end - 1.0 > RESTART + margin or l_max - 1.0 > OVERFLOW + 2.0:
+                        if p_dtype == "bf16":
+                            surely = l_end - 1.0 > rs + margin or l_max - 1.0 > OVERFLOW + 2.0
+                            never = l_end < rs - margin and l_max < OVERFLOW - 1.0
+                        else:
+                            surely = l_end - 1.0 > rs + margin or w_max > F16_INF + margin
+                            never = l_end < rs - margin and w_max < F16_INF - margin
+                        if surely:
                             ev["restart"] += 1
                             kept = [run_wave(b, h, qw, q_start, exact=True) for h, qw in waves]
-                        elif l_end < RESTART - margin and l_max < OVERFLOW - 1.0:
+                        elif never:
                             ev["free_growth"] += sum(r["excess"] > LAZY + margin for r in first)
                         else:
                             ev["uncertain"] += 1

@@ -1,7 +1,7 @@
 """The ramped-score prefill cases reach the kernel's rescale of the reference
-maximum on both code paths, and with bf16 P both outcomes of the max-free
-pass (kept with weights far above the reference, or rerun with the exact
-steps), by host emulation of the kernel's tile maxima and row sums (no GPU).
+maximum on both code paths, and with bf16 and with fp16 P both outcomes of
+the max-free pass (kept with weights far above the reference, or rerun with
+the exact steps), by host emulation of the kernel's tile maxima and row sums (no GPU).
 The GPU parity test of the same cases is ``test_prefill_rescale_branch`` in
 test_parity_gpu.py."""
 import numpy as np
@@ -11,8 +11,9 @@ from tests.rescale_emu import rescale_events
 from workloads import prefill_inputs, prefill_ramp_inputs
 
 # B, N, M, Hq, Hkv, d, dtype, causal: causal with N == M and N < M, non-causal,
-# fp16 and bf16, head dims 64 and 128, GQA and MHA; the last three are long
-# enough for bf16 workgroups to outgrow the max-free pass and rerun it
+# fp16 and bf16, head dims 64 and 128, GQA and MHA; fp16 workgroups outgrow
+# their max-free pass (weights past 2^15) within a few tiles, the last three
+# bf16 cases are long enough to outgrow it too (row sums past 2^100)
 RESCALE_CASES = [
     (1, 1024, 1024, 4, 2, 128, "bf16", True),
     (1, 1024, 1024, 4, 4, 64, "f16", True),
@@ -34,19 +35,20 @@ def rescale_case_inputs(case):
 
 
 def max_free(case):
-    """The kernel runs a max-free first pass for bf16 P up to head dim 128."""
-    return case[6] == "bf16" and case[5] <= 128
+    """The kernel runs a max-free first pass up to head dim 128."""
+    return case[5] <= 128
 
 
 def case_events(case):
     q, k, v, scale = rescale_case_inputs(case)
-    return rescale_events(q, k, scale, case[-1], max_free=max_free(case))
+    return rescale_events(q, k, scale, case[7], max_free=max_free(case), p_dtype=case[6])
 
 
 def check_case_events(case, ev):
     """What a ramped case must reach: the general path's rescale, and on the
-    steady-state path the exact rescale (fp16) or, with bf16, growth the
-    max-free pass keeps or a rerun; no workgroup too close to call."""
+    steady-state path growth that the max-free pass keeps or a rerun whose
+    exact steps rescale (head dim 256: the exact steps' rescale); no
+    workgroup too close to call."""
     assert ev["general"] > 0 and ev["uncertain"] == 0, ev
     if max_free(case):
         assert ev["free_growth"] > 0 or (ev["restart"] > 0 and ev["fast"] > 0), ev
@@ -62,12 +64,22 @@ def test_ramp_inputs_rescale_on_both_paths(case):
     assert float(v.abs().max()) < 1.5
 
 
+def test_f16_cases_reach_both_outcomes_of_the_max_free_pass():
+    """Some fp16 workgroups keep a max-free pass whose steady tiles exceeded
+    the reference by more than 8 (weights up to 2^15, within fp16's range),
+    and some rerun the pass with the exact steps, which then rescale on the
+    steady-state path."""
+    evs = [case_events(c) for c in RESCALE_CASES if max_free(c) and c[6] == "f16"]
+    assert any(ev["free_growth"] > 0 and ev["restart"] > 0 for ev in evs), evs
+    assert any(ev["restart"] > 0 and ev["fast"] > 0 for ev in evs), evs
+
+
 def test_bf16_cases_reach_both_outcomes_of_the_max_free_pass():
     """Some bf16 workgroups keep a max-free pass whose steady tiles exceeded
     the reference by far more than 8 (up to about 2^100 in the row sums), and
     some rerun the pass with the exact steps, which then rescale on the
     steady-state path."""
-    evs = [case_events(c) for c in RESCALE_CASES if max_free(c)]
+    evs = [case_events(c) for c in RESCALE_CASES if max_free(c) and c[6] == "bf16"]
     assert any(ev["free_growth"] > 0 and ev["max_jump"] > 60 for ev in evs), evs
     assert any(ev["restart"] > 0 and ev["fast"] > 0 for ev in evs), evs
     assert any(ev["free_growth"] > 0 and ev["restart"] > 0 for ev in evs), evs
