@@ -151,7 +151,9 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   constexpr int kXcd = 8;
   const int xcd = id % kXcd, local = id / kXcd;
   const int per = total / kXcd, rem = total % kXcd;
-  return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  // XCDs below rem own per + 1 ids, the others per (no branch, so that the
+  // kernel's argument loads are not split around one)
+  return xcd * per + min(xcd, rem) + local;
 }
 
 }  // namespace attn

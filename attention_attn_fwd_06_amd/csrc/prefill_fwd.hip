@@ -755,11 +755,18 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   if constexpr (D <= 128) {
     constexpr float kRerun = BF16 ? 0x1p100f : 0x1p15f;
     kv_pass(std::false_type{});
-    float z = 0.f;  // NaN iff some O accumulator is Inf or NaN
+    // z is NaN iff some O accumulator is Inf or NaN (o * 0 is NaN exactly
+    // then); one chain per d block, so the chains run side by side
+    float zc[kDB];
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < kDB; ++db) {
+      zc[db] = acc_o[db][0] * 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) z = fmaf(acc_o[db][i], 0.f, z);
+      for (int i = 1; i < 16; ++i) zc[db] = fmaf(acc_o[db][i], 0.f, zc[db]);
+    }
+    float z = zc[0];
+#pragma unroll
+    for (int db = 1; db < kDB; ++db) z += zc[db];
     const bool bad = !(l_run < kRerun) || z != z;
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     if (lane == 0) restart_flag[wave] = wave_bad ? 1 : 0;
