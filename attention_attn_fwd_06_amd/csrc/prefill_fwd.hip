@@ -402,15 +402,15 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   };
 
   // Multiply O and l by alpha = 2^(m_run - m_new) when the reference max moves
-  // up to m_new.  alpha is applied as two factors 2^((m_run - m_new) / 2):
-  // after a max-free pass (bf16) the reference can lag by up to about 2^7
-  // while O and l carry the same factor 2^lag, and a single factor would fall
-  // below fp32's normal range although the products do not.
+  // up to m_new.  Moves happen only where O and l hold weights of at most 2^8
+  // per key (exact steps, or a wave's first tile), so an alpha that flushes
+  // to zero (a move of more than 126 log2 units) drops contributions below
+  // 2^-100 of the new tile's.
   auto move_reference_to = [&](const float m_new) __attribute__((always_inline)) {
-    const float half = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(0.5f * (m_run - m_new));
-    l_run = l_run * half * half;
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run = l_run * alpha;
 #pragma unroll
-    for (int i = 0; i < kDB; ++i) acc_o[i] = acc_o[i] * half * half;
+    for (int i = 0; i < kDB; ++i) acc_o[i] = acc_o[i] * alpha;
     m_run = m_new;
   };
 

@@ -10,11 +10,12 @@ than 8.  The tiles go through one of two code paths:
     still needs), which tests the condition on the tile's row max computed
     during the previous step;
   * the general step (a masked or only first tile, the causal diagonal and
-    tail tiles, and the wave's last tile), which tests it after masking.
+    tail tiles, and the wave's last tile), which tests it after masking; in
+    a max-free pass (below) only on a wave's first tile.
 
 With head dim up to 128 a workgroup (four waves sharing the K/V tiles) first
-runs a pass whose steady-state steps never move the reference (it stays at
-the first tile's row max, the general steps still move it).  The weights of
+runs a pass whose steps never move the reference (it stays at the first
+tile's row max; a general step sets it only when it is the wave's first).  The weights of
 tiles that outgrow the reference are then up to 2^(excess), which P and fp32
 hold up to P's largest value; the pass is rerun with the exact steps when, at
 its end, some lane's row sum is 2^100 (bf16 P) or 2^15 (fp16 P) or more, or a
@@ -69,8 +70,9 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_d
                    more than 8 (where an exact step would have rescaled);
       ``restart``  workgroups that surely rerun with the exact steps;
       ``uncertain`` workgroups too close to the restart threshold to say;
-    ``max_jump``, the largest excess of a steady tile max over its row's
-    reference (in the pass whose result is kept, or the first pass), and
+    ``max_jump``, the largest excess of a tile max over its row's reference
+    where the step did not rescale (in the pass whose result is kept, or the
+    first pass), and
     ``max_lag``, the largest move of a row's reference in a rescale of a kept
     pass (its factor 2^-lag is below fp32's normal range past 126).
     """
@@ -92,8 +94,9 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_d
 
     def run_wave(b, h, qw, q_start, exact):
         """One wave's pass: its fast and general rescale events, the largest
-        steady excess over the reference, the log2 of the rows' sums at the
-        end and their largest log2 during the pass (float64: no overflow)."""
+        excess of a tile over the reference where no rescale followed, the
+        log2 of the rows' sums at the end and their largest log2 during the
+        pass (float64, whose range covers fp32's many times over)."""
         kh = h // group
         Kb = k[b, :, kh, :]
         qi = np.arange(qw, qw + WAVE_ROWS)
@@ -142,7 +145,8 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_d
             nonlocal l_row
             m_use = np.where(m_run == -math.inf, 0.0, m_run)
             out["w_max"] = max(out["w_max"], float(np.max(t - m_use[:, None])))
-            l_row = l_row + np.exp2(t - m_use[:, None]).sum(axis=1)
+            with np.errstate(over="ignore"):  # inf past float64's range: an overflow either way
+                l_row = l_row + np.exp2(t - m_use[:, None]).sum(axis=1)
             out["l_max"] = max(out["l_max"], float(np.log2(np.max(l_row))) if np.max(l_row) > 0 else -math.inf)
 
         for j in range(n_tiles):
@@ -161,7 +165,13 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_d
                 need_mask = (causal and n0 + BN - 1 > qw + off) or (n0 + BN > M)
                 t = tile_scores(j, need_mask)
                 mx = t.max(axis=1)
-                ballot(np.where(np.isfinite(mx), mx, -math.inf), "general")
+                if exact or j == 0:
+                    ballot(np.where(np.isfinite(mx), mx, -math.inf), "general")
+                else:
+                    # a max-free pass keeps its reference here too (masked keys weigh 0)
+                    ok = np.isfinite(mx) & np.isfinite(m_run)
+                    if ok.any():
+                        out["excess"] = max(out["excess"], float(np.max((mx - m_run)[ok])))
                 accumulate(t)
         out["l_end"] = float(np.log2(np.max(l_row)))
         return out

@@ -161,12 +161,12 @@ def test_prefill_causal_gqa_bf16_full_size_whole():
 def test_prefill_rescale_branch(case):
     """Scores that grow with the key index, so that rows' maxima rise by more
     than 8 log2 units from tile to tile: the kernel moves its reference max
-    (O and l rescaled by alpha = 2^(m_old - m_new)) on the general path; its
-    max-free pass keeps weights far above the reference or is rerun with the
-    exact steps, which rescale on the steady-state path (all checked on the
+    (O and l rescaled by alpha = 2^(m_old - m_new)): its max-free pass keeps
+    weights far above the reference, or is rerun with the exact steps, which
+    rescale on the steady-state and the general path (all checked on the
     host first); and the output still matches the oracle element by
     element."""
-    B, N, M, Hq, Hkv, d, dt, causal = case
+    B, N, M, Hq, Hkv, d, dt, causal = case[:8]
     say(f"case prefill rescale {case}")
     q, k, v, scale = rescale_case_inputs(case)
     ev = rescale_events(q, k, scale, causal, max_free=max_free(case), p_dtype=dt)
