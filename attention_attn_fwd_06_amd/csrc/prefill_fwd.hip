@@ -41,12 +41,11 @@
 //  * exp2 domain with scale*log2(e) folded into one FMA; the O / l rescale is
 //    skipped unless some row's max grew by more than 2^8 (O and l always
 //    share the same reference max, so the result is the same up to rounding).
-//  * head dims up to 128: the steady-state steps of a first pass do not
-//    track the row max at all; the reference stays at the first tile's row
-//    max (the masked steps still move it), and weights above it keep their
-//    relative precision in P and fp32 up to P's largest value (2^127 in
-//    bf16, 65504 in fp16).  A workgroup whose pass ends with a lane's row sum
-//    of 2^100 (bf16) or 2^15 (fp16) or more, or with a non-finite
+//  * the steps of a first pass do not track the row max at all; the
+//    reference stays at the first tile's row max, and weights above it keep
+//    their relative precision in P and fp32 up to P's largest value (2^127
+//    in bf16, 65504 in fp16).  A workgroup whose pass ends with a lane's row
+//    sum of 2^100 (bf16) or 2^15 (fp16) or more, or with a non-finite
 //    accumulator, runs the pass again with the exact steps.
 //  * bf16 only: where a wave's first KV tile is masked or is its only tile
 //    (rows with at most 64 keys: early causal rows, where |O| is large), P of
@@ -738,21 +737,17 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     for (; j < n_tiles; ++j) step_general(j, std::false_type{}, exact);
   };
 
-  // The steady-state steps first run without a moving reference max (the
-  // reference is the first tile's row max; the general steps still move it).
-  // Tiles whose scores exceed it give large weights, which P and the fp32
-  // accumulators hold at full relative precision up to P's largest value, so
-  // the result is the same up to rounding.  A pass whose weights may have
-  // outgrown that range leaves a lane's row sum at or above kRerun (2^100 for
-  // bf16, whose weights reach 2^127; 2^15 for fp16, so that no kept weight
-  // exceeds 2^15 < 65504: a weight that rounded to Inf in fp16 passed 2^15,
-  // and where a general step scaled the sum back below kRerun it left an
-  // accumulator that is not finite), or such an accumulator; then the whole
-  // workgroup runs the pass again with the exact steps (all four waves share
-  // the K/V fetches, so the decision is taken jointly through LDS).  Head dim
-  // 256 always takes the exact steps: its max-free instance does not compile
-  // with the fetch descriptors in scalar registers.
-  if constexpr (D <= 128) {
+  // A first pass runs without a moving reference max (the reference is the
+  // first tile's row max).  Tiles whose scores exceed it give large weights,
+  // which P and the fp32 accumulators hold at full relative precision up to
+  // P's largest value, so the result is the same up to rounding.  A pass
+  // whose weights may have outgrown that range leaves a lane's row sum at or
+  // above kRerun (2^100 for bf16, whose weights reach 2^127; 2^15 for fp16,
+  // so that no kept weight exceeds 2^15 < 65504: a weight that rounded to Inf
+  // in fp16 passed 2^15), or an accumulator that is not finite; then the
+  // whole workgroup runs the pass again with the exact steps (all four waves
+  // share the K/V fetches, so the decision is taken jointly through LDS).
+  {
     constexpr float kRerun = BF16 ? 0x1p100f : 0x1p15f;
     kv_pass(std::false_type{});
     // z is NaN iff some O accumulator is Inf or NaN (o * 0 is NaN exactly
@@ -784,8 +779,6 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
       if (n_tiles > 1) FK::tile(kdesc, kbuf0 + kTBK, kBN, wave, voffk, k_row_bytes);
       kv_pass(std::true_type{});
     }
-  } else {
-    kv_pass(std::true_type{});
   }
 
   // ---- epilogue: O / l -> 16-bit, lse = ln2 * (m + log2 l) ----

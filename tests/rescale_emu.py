@@ -13,16 +13,16 @@ than 8.  The tiles go through one of two code paths:
     tail tiles, and the wave's last tile), which tests it after masking; in
     a max-free pass (below) only on a wave's first tile.
 
-With head dim up to 128 a workgroup (four waves sharing the K/V tiles) first
-runs a pass whose steps never move the reference (it stays at the first
-tile's row max; a general step sets it only when it is the wave's first).  The weights of
-tiles that outgrow the reference are then up to 2^(excess), which P and fp32
-hold up to P's largest value; the pass is rerun with the exact steps when, at
-its end, some lane's row sum is 2^100 (bf16 P) or 2^15 (fp16 P) or more, or a
-weight or an accumulator overflowed (bf16: fp32's range; fp16: a weight of
-65520 or more, which rounds to Inf in P and leaves an accumulator that is not
-finite).  The emulation follows each row's sum (over both lanes that share
-the row) and its largest weight through the pass, rescales included.
+A workgroup (four waves sharing the K/V tiles) first runs a pass whose steps
+never move the reference (it stays at the first tile's row max; a general
+step sets it only when it is the wave's first).  The weights of tiles that
+outgrow the reference are then up to 2^(excess), which P and fp32 hold up to
+P's largest value; the pass is rerun with the exact steps when, at its end,
+some lane's row sum is 2^100 (bf16 P) or 2^15 (fp16 P) or more, or a weight or
+an accumulator overflowed (bf16: fp32's range; fp16: a weight of 65520 or
+more, which rounds to Inf in P and leaves an accumulator that is not finite).
+The emulation follows each row's sum (over both lanes that share the row) and
+its largest weight through the pass, rescales included.
 
 This module replays that control flow on the host in float64 (which rows a
 wave owns, which tiles it visits and along which path, the masks, the
@@ -54,8 +54,8 @@ def rescale_events(q, k, scale: float, causal: bool, max_free: bool = False, p_d
                    margin: float = 0.05):
     """Count the kernel's rescale decisions on inputs q [B,N,Hq,d], k [B,M,Hkv,d].
 
-    ``max_free``: the kernel's first pass runs the steady-state steps without
-    a moving reference (head dim <= 128); ``p_dtype`` ("bf16" or "f16") is
+    ``max_free``: the kernel's first pass runs without a moving reference
+    (every head dim; False replays the exact steps alone); ``p_dtype`` ("bf16" or "f16") is
     the type of P, which sets when that pass is rerun.
 
     Returns a dict of counts of decisions the kernel surely takes (each more

@@ -26,6 +26,10 @@ RESCALE_CASES = [
     (1, 512, 2048, 2, 2, 64, "bf16", False),
     (1, 1024, 4096, 4, 2, 128, "bf16", False),
     (1, 512, 512, 2, 2, 64, "bf16", True, 176.0),
+    # head dim 256
+    (1, 256, 1000, 2, 2, 256, "bf16", False),
+    (1, 256, 700, 4, 2, 256, "f16", True),
+    (1, 512, 4096, 2, 1, 256, "bf16", False),
 ]
 RESCALE_SEED = 11
 
@@ -37,25 +41,17 @@ def rescale_case_inputs(case):
     return q, k, v, float(np.float32(d ** -0.5))
 
 
-def max_free(case):
-    """The kernel runs a max-free first pass up to head dim 128."""
-    return case[5] <= 128
-
-
 def case_events(case):
     q, k, v, scale = rescale_case_inputs(case)
-    return rescale_events(q, k, scale, case[7], max_free=max_free(case), p_dtype=case[6])
+    return rescale_events(q, k, scale, case[7], max_free=True, p_dtype=case[6])
 
 
 def check_case_events(case, ev):
-    """What a ramped case must reach: growth that the max-free pass keeps, or
-    a rerun whose exact steps rescale (head dim 256: the exact steps'
-    rescale); no workgroup too close to call."""
+    """What a ramped case must reach: growth that the max-free first pass
+    keeps, or a rerun whose exact steps rescale; no workgroup too close to
+    call."""
     assert ev["uncertain"] == 0, ev
-    if max_free(case):
-        assert ev["free_growth"] > 0 or (ev["restart"] > 0 and ev["fast"] > 0), ev
-    else:
-        assert ev["fast"] > 0 and ev["restart"] == 0, ev
+    assert ev["free_growth"] > 0 or (ev["restart"] > 0 and ev["fast"] > 0), ev
 
 
 @pytest.mark.parametrize("case", RESCALE_CASES, ids=lambda c: "x".join(map(str, c)))
@@ -79,7 +75,7 @@ def test_f16_cases_reach_both_outcomes_of_the_max_free_pass():
     the reference by more than 8 (weights up to 2^15, within fp16's range),
     and some rerun the pass with the exact steps, which then rescale on the
     steady-state path."""
-    evs = [case_events(c) for c in RESCALE_CASES if max_free(c) and c[6] == "f16"]
+    evs = [case_events(c) for c in RESCALE_CASES if c[6] == "f16"]
     assert any(ev["free_growth"] > 0 and ev["restart"] > 0 for ev in evs), evs
     assert any(ev["restart"] > 0 and ev["fast"] > 0 for ev in evs), evs
 
@@ -89,7 +85,7 @@ def test_bf16_cases_reach_both_outcomes_of_the_max_free_pass():
     the reference by far more than 8 (up to about 2^100 in the row sums), and
     some rerun the pass with the exact steps, which then rescale on the
     steady-state path."""
-    evs = [case_events(c) for c in RESCALE_CASES if max_free(c) and c[6] == "bf16"]
+    evs = [case_events(c) for c in RESCALE_CASES if c[6] == "bf16"]
     assert any(ev["free_growth"] > 0 and ev["max_jump"] > 60 for ev in evs), evs
     assert any(ev["restart"] > 0 and ev["fast"] > 0 for ev in evs), evs
     assert any(ev["free_growth"] > 0 and ev["restart"] > 0 for ev in evs), evs
