@@ -16,7 +16,7 @@ __all__ = [
     "AttnError", "ATTN_F16", "ATTN_BF16", "attn_fwd", "attn_fwd_fp8qk", "attn_decode_splitkv", "lse_merge",
     "attn_decode_workspace_bytes", "attn_status_string", "attn_decode", "attn_decode_paged_splitkv",
     "attn_decode_paged", "attn_decode_paged_fused", "attn_decode_fp8kv_splitkv", "attn_decode_fp8kv", "attn_decode_fused",
-    "attn_decode_fused_workspace_bytes", "attn_decode_fused_noalloc",
+    "attn_decode_fused_workspace_bytes", "attn_decode_fused_noalloc", "attn_decode_fp8kv_fused",
 ]
 
 ATTN_F16 = 0
@@ -241,6 +241,36 @@ def attn_decode_fused_workspace_bytes(B: int, Hq: int, Hkv: int, M: int, d: int)
     return int(_lib.load().attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
 
 
+def _fused_out_checks(q, o, lse, workspace, nbytes):
+    """Checks of a fused decode's o [B,Hq,d] (q's dtype), lse [B,Hq] fp32 and
+    uint8 workspace of at least nbytes, where given."""
+    B, Hq, d = q.shape
+    if o is not None:
+        _shape(o, "o", (B, Hq, d))
+        _dtype(o, "o", q.dtype)
+        _contig(o, "o")
+    if lse is not None:
+        _check_f32(lse, "lse", (B, Hq))
+    if workspace is not None:
+        _dtype(workspace, "workspace", torch.uint8)
+        _contig(workspace, "workspace")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+
+
+def _fused_outputs(q, o, lse, return_lse, workspace, nbytes):
+    """o, lse and workspace of a fused decode, allocated where not given (a
+    fresh workspace is zero-filled)."""
+    B, Hq, d = q.shape
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    return o, lse, workspace
+
+
 def attn_decode_fused(q, k, v, scale: float | None = None, o=None, lse=None, return_lse: bool = True,
                       workspace=None, stream=None):
     """Split-KV decode end to end in one launch (partials and merge fused).
@@ -261,27 +291,12 @@ def attn_decode_fused(q, k, v, scale: float | None = None, o=None, lse=None, ret
     _dtype(v, "v", q.dtype)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _contig(t, n)
-    if o is not None:
-        _shape(o, "o", (B, Hq, d))
-        _dtype(o, "o", q.dtype)
-        _contig(o, "o")
-    if lse is not None:
-        _check_f32(lse, "lse", (B, Hq))
     nbytes = attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d)
-    if workspace is not None:
-        _dtype(workspace, "workspace", torch.uint8)
-        _contig(workspace, "workspace")
-        if workspace.numel() < nbytes:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    _fused_out_checks(q, o, lse, workspace, nbytes)
     _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (workspace, "workspace"))
     if scale is None:
         scale = d ** -0.5
-    if o is None:
-        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o, lse, workspace = _fused_outputs(q, o, lse, return_lse, workspace, nbytes)
     st = _lib.load().attn_decode_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
                                        workspace.numel(), B, Hq, Hkv, M, d, float(scale), dt, _stream(stream))
@@ -400,46 +415,43 @@ def attn_decode_paged_splitkv(q, k_cache, v_cache, block_table, seq_lens, chunk_
 
 
 def attn_decode_paged_fused(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None, o=None,
-                            lse=None, return_lse: bool = True, workspace=None, stream=None):
+                            lse=None, return_lse: bool = True, workspace=None, stream=None,
+                            k_scale: float | None = None, v_scale: float | None = None):
     """Split-KV decode over a paged KV cache in one launch (partials of
     128-key chunk runs and their merge fused).
 
     q [B,Hq,d]; k_cache, v_cache, block_table, seq_lens as in
-    attn_decode_paged_splitkv (16-bit caches).  Returns (o [B,Hq,d], lse
-    [B,Hq] fp32 or None).  ``workspace``: a uint8 GPU tensor of at least
-    attn_decode_fused_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, d)
-    bytes, zero-filled before its first use; by default a fresh zeroed one."""
-    if k_cache.dtype in _FP8:
-        raise TypeError("the fused paged decode takes 16-bit caches")
+    attn_decode_paged_splitkv.  Returns (o [B,Hq,d], lse [B,Hq] fp32 or
+    None).  Caches of E4M3 codes (torch.float8_e4m3fn or uint8) take k_scale
+    and v_scale (attn_decode_paged_fp8kv_fused).  ``workspace``: a uint8 GPU
+    tensor of at least attn_decode_fused_workspace_bytes(B, Hq, Hkv,
+    max_blocks * block_size, d) bytes, zero-filled before its first use; by
+    default a fresh zeroed one."""
+    fp8 = k_cache.dtype in _FP8
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("FP8 caches need k_scale and v_scale")
     dt, B, Hq, d, num_blocks, block_size, Hkv, max_blocks = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
-    if o is not None:
-        _shape(o, "o", (B, Hq, d))
-        _dtype(o, "o", q.dtype)
-        _contig(o, "o")
-    if lse is not None:
-        _check_f32(lse, "lse", (B, Hq))
     nbytes = attn_decode_fused_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, d)
-    if workspace is not None:
-        _dtype(workspace, "workspace", torch.uint8)
-        _contig(workspace, "workspace")
-        if workspace.numel() < nbytes:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+    _fused_out_checks(q, o, lse, workspace, nbytes)
     _devices((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
              (seq_lens, "seq_lens"), (o, "o"), (lse, "lse"), (workspace, "workspace"))
     if scale is None:
         scale = d ** -0.5
-    if o is None:
-        o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o, lse, workspace = _fused_outputs(q, o, lse, return_lse, workspace, nbytes)
     pk = _lib.PagedKv(block_table.data_ptr(), seq_lens.data_ptr(), num_blocks, block_size, max_blocks,
                       k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if fp8:
+        st = _lib.load().attn_decode_paged_fp8kv_fused(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                       float(k_scale), float(v_scale), ctypes.byref(pk), o.data_ptr(),
+                                                       lse_ptr, workspace.data_ptr(), workspace.numel(), B, Hq, Hkv,
+                                                       d, float(scale), dt, _stream(stream))
+        if st != 0:
+            raise AttnError(st, "attn_decode_paged_fp8kv_fused")
+        return o, lse
     st = _lib.load().attn_decode_paged_fused(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(pk),
-                                             o.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                             workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, d, float(scale), dt,
-                                             _stream(stream))
+                                             o.data_ptr(), lse_ptr, workspace.data_ptr(), workspace.numel(), B, Hq,
+                                             Hkv, d, float(scale), dt, _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged_fused")
     return o, lse
@@ -473,6 +485,40 @@ def attn_decode_fp8kv_splitkv(q, k, v, k_scale: float, v_scale: float, chunk_siz
     if st != 0:
         raise AttnError(st, "attn_decode_fp8kv_splitkv")
     return o_part, lse_part
+
+
+def attn_decode_fp8kv_fused(q, k, v, k_scale: float, v_scale: float, scale: float | None = None, o=None,
+                            lse=None, return_lse: bool = True, workspace=None, stream=None):
+    """FP8-KV split-KV decode end to end in one launch (partials and merge
+    fused).  q [B,Hq,d] fp16/bf16; k, v [B,Hkv,M,d] E4M3 codes
+    (torch.float8_e4m3fn or uint8); K = k_scale * e4m3(k), V = v_scale *
+    e4m3(v).  Returns (o [B,Hq,d] q.dtype, lse [B,Hq] fp32 or None);
+    ``workspace`` as in attn_decode_fused."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, M, d]")
+    dt = _dtype_code(q)
+    for t, n in ((k, "k"), (v, "v")):
+        if t.dtype not in _FP8:
+            raise TypeError(f"{n} must hold E4M3 codes (torch.float8_e4m3fn or uint8)")
+    B, Hq, d = q.shape
+    Hkv, M = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, Hkv, M, d))
+    _shape(v, "v", k.shape)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, n)
+    nbytes = attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d)
+    _fused_out_checks(q, o, lse, workspace, nbytes)
+    _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (workspace, "workspace"))
+    if scale is None:
+        scale = d ** -0.5
+    o, lse, workspace = _fused_outputs(q, o, lse, return_lse, workspace, nbytes)
+    st = _lib.load().attn_decode_fp8kv_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(k_scale),
+                                             float(v_scale), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                             workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, M, d, float(scale),
+                                             dt, _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fp8kv_fused")
+    return o, lse
 
 
 def attn_decode_fp8kv(q, k, v, k_scale: float, v_scale: float, chunk_size: int = 128,

@@ -48,6 +48,11 @@ SYMBOLS = {
                           + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "attn_decode_paged_fused": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.POINTER(PagedKv)] + [ctypes.c_void_p] * 3
                                 + [ctypes.c_size_t] + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_decode_fp8kv_fused": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_float] * 2 + [ctypes.c_void_p] * 3
+                                + [ctypes.c_size_t] + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_decode_paged_fp8kv_fused": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_float] * 2
+                                      + [ctypes.POINTER(PagedKv)] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t]
+                                      + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "attn_decode_fused_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5
                                   + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "lse_merge": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4

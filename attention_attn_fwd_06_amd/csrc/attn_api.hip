@@ -33,11 +33,15 @@ hipError_t decode_fp8kv_dispatch(const void* q, const void* k, const void* v, fl
 hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
                                  size_t ws_bytes, int B, int Hq, int Hkv, int M, int d, bool bf16, float scale,
                                  hipStream_t stream);
+hipError_t decode_fp8kv_fused_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                                       void* o, float* lse, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int M,
+                                       int d, bool bf16, float scale, hipStream_t stream);
 hipError_t decode_paged_fused_dispatch(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
                                        int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
                                        int64_t head_stride, void* o, float* lse, void* ws, size_t ws_bytes, int B,
-                                       int Hq, int Hkv, int d, bool bf16, float scale, hipStream_t stream);
+                                       int Hq, int Hkv, int d, bool bf16, float scale, bool fp8, float k_scale,
+                                       float v_scale, hipStream_t stream);
 size_t fused_workspace_layout(int B, int Hq, int Hkv, int d, int S, size_t* off_lse, size_t* off_o);
 int fused_segment_cap(int B, int Hq, int Hkv, int M);
 size_t scratch_capacity();
@@ -252,11 +256,33 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
                                                    chunk_size, dtype == ATTN_BF16, scale, stream));
 }
 
+int attn_decode_fp8kv_fused(const void* q, const void* k, const void* v, float k_scale, float v_scale, void* o,
+                            float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int M, int d,
+                            float scale, attn_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || d <= 0) return ATTN_ERR_BAD_DIMENSION;
+  if (!valid_head_dim(d)) return ATTN_ERR_HEAD_DIM;
+  if (!valid_dtype(dtype)) return ATTN_ERR_DTYPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA_GROUPS;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite(k_scale) || k_scale < 0.f || !std::isfinite(v_scale) ||
+      v_scale < 0.f)
+    return ATTN_ERR_SCALE;
+  if (decode_too_large(B, Hq, M, d, kDecodeChunk)) return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGNMENT;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(attn::decode_fp8kv_fused_dispatch(q, k, v, k_scale, v_scale, o, lse, workspace,
+                                                         workspace_bytes, B, Hq, Hkv, M, d, dtype == ATTN_BF16, scale,
+                                                         stream));
+}
+
 }  // extern "C"
 
 namespace {
 
-// Validation and launch shared by the 16-bit and FP8 paged entry points.
 // Checks shared by the paged entry points: pointers, sizes, head dim, dtype,
 // groups, scales, the page layout, index ranges and alignment of the inputs
 // (chunk_size 128 for the fused call).
@@ -305,6 +331,26 @@ int paged_decode(const void* q, const void* k_cache, const void* v_cache, const 
                                                    dtype == ATTN_BF16, scale, fp8, k_scale, v_scale, stream));
 }
 
+int paged_fused(const void* q, const void* k_cache, const void* v_cache, const attn_paged_kv_t* pages, void* o,
+                float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d, float scale,
+                attn_dtype_t dtype, bool fp8, float k_scale, float v_scale, hipStream_t stream) {
+  if (!o) return ATTN_ERR_NULL_POINTER;
+  const int st = check_paged(q, k_cache, v_cache, pages, B, Hq, Hkv, d, kDecodeChunk, scale, dtype, fp8, k_scale,
+                             v_scale);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))) return ATTN_ERR_ALIGNMENT;
+  const attn_paged_kv_t& pk = *pages;
+  const int M = pk.max_blocks * pk.block_size;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(attn::decode_paged_fused_dispatch(q, k_cache, v_cache, pk.block_table, pk.seq_lens,
+                                                         pk.num_blocks, pk.block_size, pk.max_blocks, pk.page_stride,
+                                                         pk.token_stride, pk.head_stride, o, lse, workspace,
+                                                         workspace_bytes, B, Hq, Hkv, d, dtype == ATTN_BF16, scale,
+                                                         fp8, k_scale, v_scale, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,20 +365,16 @@ int attn_decode_paged_splitkv(const void* q, const void* k_cache, const void* v_
 int attn_decode_paged_fused(const void* q, const void* k_cache, const void* v_cache, const attn_paged_kv_t* pages,
                             void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                             int d, float scale, attn_dtype_t dtype, hipStream_t stream) {
-  if (!o) return ATTN_ERR_NULL_POINTER;
-  const int st = check_paged(q, k_cache, v_cache, pages, B, Hq, Hkv, d, kDecodeChunk, scale, dtype, false, 1.f, 1.f);
-  if (st != ATTN_OK) return st;
-  if (!aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))) return ATTN_ERR_ALIGNMENT;
-  const attn_paged_kv_t& pk = *pages;
-  const int M = pk.max_blocks * pk.block_size;
-  if (!workspace || !aligned16(workspace) ||
-      workspace_bytes < attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d))
-    return ATTN_ERR_WORKSPACE;
-  return launch_status(attn::decode_paged_fused_dispatch(q, k_cache, v_cache, pk.block_table, pk.seq_lens,
-                                                         pk.num_blocks, pk.block_size, pk.max_blocks, pk.page_stride,
-                                                         pk.token_stride, pk.head_stride, o, lse, workspace,
-                                                         workspace_bytes, B, Hq, Hkv, d, dtype == ATTN_BF16, scale,
-                                                         stream));
+  return paged_fused(q, k_cache, v_cache, pages, o, lse, workspace, workspace_bytes, B, Hq, Hkv, d, scale, dtype,
+                     false, 1.f, 1.f, stream);
+}
+
+int attn_decode_paged_fp8kv_fused(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                                  float v_scale, const attn_paged_kv_t* pages, void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, int B, int Hq, int Hkv, int d, float scale,
+                                  attn_dtype_t dtype, hipStream_t stream) {
+  return paged_fused(q, k_cache, v_cache, pages, o, lse, workspace, workspace_bytes, B, Hq, Hkv, d, scale, dtype,
+                     true, k_scale, v_scale, stream);
 }
 
 int attn_decode_paged_fp8kv_splitkv(const void* q, const void* k_cache, const void* v_cache, float k_scale,

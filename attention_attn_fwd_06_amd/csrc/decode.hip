@@ -327,7 +327,6 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             const uint16_t* __restrict__ v, float* __restrict__ o_part,
                             float* __restrict__ lse_part, int Hq, int Hkv, int M, int C, int G,
                             int chunk, int n_items, float scale_log2, PagedKv pk, float v_scale, FusedOut fo) {
-  static_assert(!FUSED || !KV8, "the fused merge is built for 16-bit K/V");
   static_assert(!KV8 || D <= 128, "FP8 K/V: head dims up to 128");
   constexpr int kS = D / 32;                        // QK contraction steps
   constexpr int kWaves = kDecThreads / 64;
@@ -577,6 +576,15 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     if (tid == 0) __hip_atomic_store(fo.count + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
+  // Keys of item n: chunk n % C, or in fused mode segment n % C of the row's
+  // 128-key chunks; the end is nominal (not clamped to a sequence's length).
+  auto item_key0 = [&](int n) {
+    return FUSED ? (int)((int64_t)(n % C) * fo.n_chunks / C) * kChunk : (n % C) * chunk;
+  };
+  auto item_key_end = [&](int n) {
+    return FUSED ? (int)((int64_t)(n % C + 1) * fo.n_chunks / C) * kChunk : (n % C + 1) * chunk;
+  };
+
   // contiguous K/V: the item and first key of the K sub-chunk already
   // fetched ahead (-1: none)
   int pf_item = -1, pf_key0 = -1;
@@ -598,7 +606,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       seq = nx_item == item ? nx_seq : seq_len(b);
       seq = min(max(seq, 0), pk.max_blocks * pk.block_size);
       if constexpr (FUSED) {
-        if ((int)((int64_t)c * fo.n_chunks / C) * kChunk >= seq) {
+        if (item_key0(item) >= seq) {
           // a segment past the sequence's end still counts towards its row
           f32x4 zero[kDB];
 #pragma unroll
@@ -624,8 +632,8 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
       }
     }
     // keys of this item: chunk c, or (fused) segment c of the row's chunks
-    const int k_begin = FUSED ? (int)((int64_t)c * fo.n_chunks / C) * kChunk : c * chunk;
-    const int c_end = FUSED ? min(seq, (int)((int64_t)(c + 1) * fo.n_chunks / C) * kChunk) : min(seq, (c + 1) * chunk);
+    const int k_begin = item_key0(item);
+    const int c_end = min(seq, item_key_end(item));
     const int64_t slice = PAGED ? 0 : ((int64_t)b * Hkv + kvh) * M * D;
 
     // Q rows h0 .. h0 + 15 (once per item), then per 128-key sub-chunk its K
@@ -672,7 +680,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         } else if (item + (int)gridDim.x < n_items) {
           nt_item = item + (int)gridDim.x;
           const int bkv_n = nt_item / C / slices;
-          nt_key0 = (nt_item % C) * chunk;
+          nt_key0 = item_key0(nt_item);
           nt_b = bkv_n / Hkv;
           nt_kvh = bkv_n % Hkv;
         }
@@ -708,7 +716,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           put(k_lds, bad ? zero4 : kr8[p], u);
           put(v_lds, bad ? zero4 : vr8[p], u);
         }
-        if (key0 == c * chunk && tid < kGqaCols * kU)  // Q, before q8 is reloaded below
+        if (key0 == k_begin && tid < kGqaCols * kU)  // Q, before q8 is reloaded below
           *(lds_u32x4*)(uintptr_t)(q_lds + (uint32_t)tid * 16u) = (u32x4){q8.x, q8.y, q8.z, q8.w};
         // prefetch the next sub-chunk, or the next item's first one
         kv8_item = nt_item;
@@ -725,13 +733,13 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           if constexpr (PAGED) {
             // guess the fetch after it and look up its pages now
             pg_item = -1;
-            if (nt_key0 + kChunk < (nt_item % C + 1) * chunk) {
+            if (nt_key0 + kChunk < item_key_end(nt_item)) {
               pg_item = nt_item;
               pg_key0 = nt_key0 + kChunk;
               lookup8(nt_b, pg_key0);
             } else if (nt_item + (int)gridDim.x < n_items) {
               pg_item = nt_item + (int)gridDim.x;
-              pg_key0 = (pg_item % C) * chunk;
+              pg_key0 = item_key0(pg_item);
               lookup8(pg_item / C / slices / Hkv, pg_key0);
             }
           }
@@ -767,7 +775,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           if (n < n_items) {
             const int bn = n / C / slices / Hkv;
             nx_item = n;
-            nx_key0 = FUSED ? (int)((int64_t)(n % C) * fo.n_chunks / C) * kChunk : (n % C) * chunk;
+            nx_key0 = item_key0(n);
             nx_seq = seq_len(bn);
             load_pages(bn, nx_key0, pgv);
           }
@@ -886,6 +894,10 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) lt += red[1][w][j];
     if constexpr (FUSED) {
+      if constexpr (KV8) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) oacc[db] *= v_scale;  // V = v_scale * e4m3(v)
+      }
       fused_epilogue(rest, b, h0, c, lt, m_run, oacc);
       __syncthreads();  // Q, K, V, P, the sums and the merge states are refilled by the next item
       continue;
@@ -1080,28 +1092,37 @@ static int fused_segments(int64_t rows, int64_t chunks, int64_t grid, int cap) {
   return best;
 }
 
-hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
-                                 size_t ws_bytes, int B, int Hq, int Hkv, int M, int d, bool bf16, float scale,
-                                 hipStream_t stream) {
+// One fused launch: S segments per row chosen for the resident grid, the
+// workspace laid out for that S (the caller's buffer holds the largest S any
+// launch may pick).  scale_log2 carries k_scale and v_scale multiplies O for
+// FP8 K/V.
+template <int D, bool BF16, bool PAGED, bool KV8>
+hipError_t launch_fused(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                        int B, int Hq, int Hkv, int M, float scale_log2, float v_scale, const PagedKv& pk,
+                        hipStream_t stream) {
+  auto* kern = &decode_gqa_mfma_kernel<D, BF16, PAGED, KV8, true>;
   const int G = heads_per_item(Hq / Hkv);
   const int64_t rows = (int64_t)B * (Hq / G);
   const int chunks = (M + kChunk - 1) / kChunk;
-  const int cap = fused_segment_cap(B, Hq, Hkv, M);
+  const int resident = resident_grid<decode_gqa_mfma_kernel<D, BF16, PAGED, KV8, true>>(kDecThreads);
+  const int S = fused_segments(rows, chunks, std::min(resident, kFusedGridCap), fused_segment_cap(B, Hq, Hkv, M));
+  size_t off_lse = 0, off_o = 0;
+  if (fused_workspace_layout(B, Hq, Hkv, D, S, &off_lse, &off_o) > ws_bytes) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  const FusedOut fo{reinterpret_cast<float*>(base + off_o), reinterpret_cast<float*>(base + off_lse),
+                    reinterpret_cast<uint32_t*>(base), static_cast<uint16_t*>(o), lse, chunks};
+  const int n_items = (int)(rows * S);
+  return launch(kern, dim3(std::min(n_items, resident)), dim3(kDecThreads), stream, q, k, v, (float*)nullptr,
+                (float*)nullptr, Hq, Hkv, M, S, G, kChunk, n_items, scale_log2, pk, v_scale, fo);
+}
+
+hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, int B, int Hq, int Hkv, int M, int d, bool bf16, float scale,
+                                 hipStream_t stream) {
   const float sl2 = scale * kLog2e;
-#define ATTN_FUSED_CASE(DD, BB)                                                                              \
-  if (d == DD && bf16 == BB) {                                                                               \
-    auto* kern = &decode_gqa_mfma_kernel<DD, BB, false, false, true>;                                        \
-    const int resident = resident_grid<decode_gqa_mfma_kernel<DD, BB, false, false, true>>(kDecThreads);    \
-    const int S = fused_segments(rows, chunks, std::min(resident, kFusedGridCap), cap);                     \
-    size_t off_lse = 0, off_o = 0;                                                                           \
-    if (fused_workspace_layout(B, Hq, Hkv, DD, S, &off_lse, &off_o) > ws_bytes) return hipErrorInvalidValue; \
-    char* base = static_cast<char*>(ws);                                                                     \
-    const FusedOut fo{reinterpret_cast<float*>(base + off_o), reinterpret_cast<float*>(base + off_lse),      \
-                      reinterpret_cast<uint32_t*>(base), static_cast<uint16_t*>(o), lse, chunks};            \
-    const int n_items = (int)(rows * S);                                                                     \
-    return launch(kern, dim3(std::min(n_items, resident)), dim3(kDecThreads), stream, q, k, v,              \
-                  (float*)nullptr, (float*)nullptr, Hq, Hkv, M, S, G, kChunk, n_items, sl2, PagedKv{}, 1.f, fo); \
-  }
+#define ATTN_FUSED_CASE(DD, BB) \
+  if (d == DD && bf16 == BB)    \
+    return launch_fused<DD, BB, false, false>(q, k, v, o, lse, ws, ws_bytes, B, Hq, Hkv, M, sl2, 1.f, PagedKv{}, stream);
   ATTN_FUSED_CASE(32, false) ATTN_FUSED_CASE(32, true) ATTN_FUSED_CASE(64, false)
   ATTN_FUSED_CASE(64, true) ATTN_FUSED_CASE(128, false) ATTN_FUSED_CASE(128, true)
   ATTN_FUSED_CASE(256, false) ATTN_FUSED_CASE(256, true)
@@ -1109,38 +1130,43 @@ hipError_t decode_fused_dispatch(const void* q, const void* k, const void* v, vo
   return hipErrorInvalidValue;
 }
 
-// Fused decode over a paged cache: rows of the longest sequence the table can
-// describe (max_blocks * block_size keys) split into segments as in the
-// contiguous case; segments past a row's sequence end count as empty.
+// The fused decode with K and V as FP8 E4M3 codes (K = k_scale e4m3(k),
+// V = v_scale e4m3(v)).
+hipError_t decode_fp8kv_fused_dispatch(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                                       void* o, float* lse, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int M,
+                                       int d, bool bf16, float scale, hipStream_t stream) {
+  const float sl2 = scale * k_scale * kLog2e;
+#define ATTN_FUSED8_CASE(DD, BB) \
+  if (d == DD && bf16 == BB)     \
+    return launch_fused<DD, BB, false, true>(q, k, v, o, lse, ws, ws_bytes, B, Hq, Hkv, M, sl2, v_scale, PagedKv{}, stream);
+  ATTN_FUSED8_CASE(32, false) ATTN_FUSED8_CASE(32, true) ATTN_FUSED8_CASE(64, false)
+  ATTN_FUSED8_CASE(64, true) ATTN_FUSED8_CASE(128, false) ATTN_FUSED8_CASE(128, true)
+#undef ATTN_FUSED8_CASE
+  return hipErrorInvalidValue;
+}
+
+// Fused decode over a paged cache (16-bit, or FP8 codes with their scales):
+// rows of the longest sequence the table can describe (max_blocks *
+// block_size keys) split into segments as in the contiguous case; segments
+// past a row's sequence end count as empty.
 hipError_t decode_paged_fused_dispatch(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_table, const int32_t* seq_lens, int num_blocks,
                                        int block_size, int max_blocks, int64_t page_stride, int64_t token_stride,
                                        int64_t head_stride, void* o, float* lse, void* ws, size_t ws_bytes, int B,
-                                       int Hq, int Hkv, int d, bool bf16, float scale, hipStream_t stream) {
+                                       int Hq, int Hkv, int d, bool bf16, float scale, bool fp8, float k_scale,
+                                       float v_scale, hipStream_t stream) {
   const int M = max_blocks * block_size;
-  const int G = heads_per_item(Hq / Hkv);
-  const int64_t rows = (int64_t)B * (Hq / G);
-  const int chunks = (M + kChunk - 1) / kChunk;
-  const int cap = fused_segment_cap(B, Hq, Hkv, M);
-  const float sl2 = scale * kLog2e;
+  const float sl2 = scale * (fp8 ? k_scale : 1.f) * kLog2e;  // FP8: the scores carry k_scale
   const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
-#define ATTN_PFUSED_CASE(DD, BB)                                                                             \
-  if (d == DD && bf16 == BB) {                                                                               \
-    auto* kern = &decode_gqa_mfma_kernel<DD, BB, true, false, true>;                                         \
-    const int resident = resident_grid<decode_gqa_mfma_kernel<DD, BB, true, false, true>>(kDecThreads);     \
-    const int S = fused_segments(rows, chunks, std::min(resident, kFusedGridCap), cap);                     \
-    size_t off_lse = 0, off_o = 0;                                                                           \
-    if (fused_workspace_layout(B, Hq, Hkv, DD, S, &off_lse, &off_o) > ws_bytes) return hipErrorInvalidValue; \
-    char* base = static_cast<char*>(ws);                                                                     \
-    const FusedOut fo{reinterpret_cast<float*>(base + off_o), reinterpret_cast<float*>(base + off_lse),      \
-                      reinterpret_cast<uint32_t*>(base), static_cast<uint16_t*>(o), lse, chunks};            \
-    const int n_items = (int)(rows * S);                                                                     \
-    return launch(kern, dim3(std::min(n_items, resident)), dim3(kDecThreads), stream, q, k_cache, v_cache,  \
-                  (float*)nullptr, (float*)nullptr, Hq, Hkv, M, S, G, kChunk, n_items, sl2, pk, 1.f, fo);   \
-  }
-  ATTN_PFUSED_CASE(32, false) ATTN_PFUSED_CASE(32, true) ATTN_PFUSED_CASE(64, false)
-  ATTN_PFUSED_CASE(64, true) ATTN_PFUSED_CASE(128, false) ATTN_PFUSED_CASE(128, true)
-  ATTN_PFUSED_CASE(256, false) ATTN_PFUSED_CASE(256, true)
+#define ATTN_PFUSED_CASE(DD, BB, F8) \
+  if (d == DD && bf16 == BB && fp8 == F8) \
+    return launch_fused<DD, BB, true, F8>(q, k_cache, v_cache, o, lse, ws, ws_bytes, B, Hq, Hkv, M, sl2, \
+                                          F8 ? v_scale : 1.f, pk, stream);
+  ATTN_PFUSED_CASE(32, false, false) ATTN_PFUSED_CASE(32, true, false) ATTN_PFUSED_CASE(64, false, false)
+  ATTN_PFUSED_CASE(64, true, false) ATTN_PFUSED_CASE(128, false, false) ATTN_PFUSED_CASE(128, true, false)
+  ATTN_PFUSED_CASE(256, false, false) ATTN_PFUSED_CASE(256, true, false)
+  ATTN_PFUSED_CASE(32, false, true) ATTN_PFUSED_CASE(32, true, true) ATTN_PFUSED_CASE(64, false, true)
+  ATTN_PFUSED_CASE(64, true, true) ATTN_PFUSED_CASE(128, false, true) ATTN_PFUSED_CASE(128, true, true)
 #undef ATTN_PFUSED_CASE
   return hipErrorInvalidValue;
 }

@@ -344,9 +344,14 @@ def paged_and_fp8_rates(attn, w, args, dev):
                                                                w.chunk, w.scale, o_part=o_part, lse_part=lse_part),
                       args)
     nbytes8 = 2.0 * w.B * w.Hkv * w.M * w.d + w.B * w.Hq * w.d * 2
+    # the same FP8-KV decode in one launch (partials and merge fused)
+    ms8_f = _time_chunk(lambda i: attn.attn_decode_fp8kv_fused(q, sets8[i % 2][0], sets8[i % 2][1], 0.01, 0.01,
+                                                               w.scale, o=o, lse=lse, workspace=ws), args)
     out["decode_fp8kv"] = {"workload": w.desc + ", K/V as FP8 E4M3 codes",
                            "value": round(nbytes8 / (ms8 * 1e-3) / 1e9, 1), "unit": "GB/s",
                            "frac": round(nbytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "chunk_ms": round(ms8, 4),
+                           "fused_ms": round(ms8_f, 4), "fused_GBps": round(nbytes8 / (ms8_f * 1e-3) / 1e9, 1),
+                           "fused_frac": round(nbytes8 / (ms8_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                            "kernel": "decode_gqa_mfma_kernel<128,bf16,fp8kv>"}
     del sets8
     sets8p = []
@@ -358,10 +363,16 @@ def paged_and_fp8_rates(attn, w, args, dev):
     ms8p = _time_chunk(lambda i: attn.attn_decode_paged_splitkv(q, sets8p[i % 2][0], sets8p[i % 2][1], sets8p[i % 2][2],
                                                                 lens, w.chunk, w.scale, o_part=o_part,
                                                                 lse_part=lse_part, k_scale=0.01, v_scale=0.01), args)
+    ms8p_f = _time_chunk(lambda i: attn.attn_decode_paged_fused(q, sets8p[i % 2][0], sets8p[i % 2][1],
+                                                                sets8p[i % 2][2], lens, w.scale, o=o, lse=lse,
+                                                                workspace=ws, k_scale=0.01, v_scale=0.01), args)
     out["decode_paged_fp8kv"] = {"workload": w.desc + ", paged FP8 KV: 16-key token-major pages, shuffled",
                                  "value": round(nbytes8 / (ms8p * 1e-3) / 1e9, 1), "unit": "GB/s",
                                  "frac": round(nbytes8 / (ms8p * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                                 "chunk_ms": round(ms8p, 4), "kernel": "decode_gqa_mfma_kernel<128,bf16,paged,fp8kv>"}
+                                 "chunk_ms": round(ms8p, 4), "fused_ms": round(ms8p_f, 4),
+                                 "fused_GBps": round(nbytes8 / (ms8p_f * 1e-3) / 1e9, 1),
+                                 "fused_frac": round(nbytes8 / (ms8p_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                 "kernel": "decode_gqa_mfma_kernel<128,bf16,paged,fp8kv>"}
     return out
 
 

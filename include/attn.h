@@ -22,7 +22,9 @@
  *   attn_decode_paged_fp8kv_splitkv  both: a paged cache of FP8 codes.
  *   attn_decode_fused    both Flash-Decoding steps in one launch, the merge done by the
  *                        last workgroup of each row (a per-row counter in a caller-owned
- *                        workspace).
+ *                        workspace); attn_decode_paged_fused, attn_decode_fp8kv_fused and
+ *                        attn_decode_paged_fp8kv_fused do the same for the paged, FP8 and
+ *                        paged FP8 partials.
  *   lse_merge            Flash-Decoding step 2: O = sum_c w_c O_c with
  *                        w_c = exp(lse_c - logsumexp_c lse_c) ("CUDA Flash Decoding",
  *                        section 2.2, step 2, and section 6 "reduce kernel").
@@ -343,6 +345,43 @@ int attn_decode_fp8kv_splitkv(const void* q, const void* k, const void* v, float
                               float* o_part, float* lse_part,
                               int B, int Hq, int Hkv, int M, int d, int chunk_size, float scale,
                               attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_fp8kv_fused - attn_decode_fp8kv_splitkv at chunk size 128 and
+ * lse_merge in one launch (the FP8 counterpart of attn_decode_fused).
+ *
+ *   q    [B, Hq, d]     dtype (fp16 or bf16), read   o   [B, Hq, d] dtype, written
+ *   k, v [B, Hkv, M, d] FP8 E4M3 codes, read         lse [B, Hq]    fp32, written (may be NULL)
+ *
+ * K = k_scale * e4m3(k), V = v_scale * e4m3(v) as in attn_decode_fp8kv_splitkv;
+ * segments, merge and workspace (attn_decode_fused_workspace_bytes(B, Hq, Hkv,
+ * M, d) bytes, counters zero before the first call and left zero by every
+ * completed call, one workspace per concurrently running call) as in
+ * attn_decode_fused.  The result is that of attn_decode_fp8kv_splitkv +
+ * lse_merge up to rounding.  Requires the attn_decode_fp8kv_splitkv conditions
+ * at chunk size 128, a 16-byte aligned o, and ATTN_ERR_WORKSPACE for a NULL,
+ * misaligned or short workspace.
+ */
+int attn_decode_fp8kv_fused(const void* q, const void* k, const void* v, float k_scale, float v_scale,
+                            void* o, float* lse, void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int M, int d, float scale,
+                            attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_decode_paged_fp8kv_fused - attn_decode_paged_fp8kv_splitkv at chunk size
+ * 128 and lse_merge in one launch: attn_decode_paged_fused over a paged cache
+ * of FP8 E4M3 codes with per-tensor scales (byte strides, multiples of 16; d in
+ * {32, 64, 128}).  Segments past a sequence's end have no key and no weight;
+ * a sequence of 0 keys gets o = 0 and lse = -inf.  Requires the
+ * attn_decode_paged_fp8kv_splitkv conditions at chunk size 128, a 16-byte
+ * aligned o, and a workspace as for attn_decode_paged_fused (else
+ * ATTN_ERR_WORKSPACE).
+ */
+int attn_decode_paged_fp8kv_fused(const void* q, const void* k_cache, const void* v_cache,
+                                  float k_scale, float v_scale, const attn_paged_kv_t* pages,
+                                  void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                  int B, int Hq, int Hkv, int d, float scale,
+                                  attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * lse_merge - combine chunk partials into the decode output.

@@ -29,7 +29,8 @@ def test_header_declares_expected_api():
         ["attn_fwd", "attn_fwd_strided", "attn_decode_workspace_bytes", "attn_decode_splitkv",
          "attn_decode_paged_splitkv", "attn_decode_paged_fp8kv_splitkv", "attn_decode_fp8kv_splitkv", "lse_merge",
          "attn_status_string", "attn_decode_fused_workspace_bytes", "attn_decode_fused",
-         "attn_decode_fused_noalloc", "attn_fwd_fp8qk", "attn_decode_paged_fused"])
+         "attn_decode_fused_noalloc", "attn_fwd_fp8qk", "attn_decode_paged_fused", "attn_decode_fp8kv_fused",
+         "attn_decode_paged_fp8kv_fused"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -301,6 +302,48 @@ def test_decode_paged_fused_workspace_is_that_of_the_longest_sequence():
     lib = _lib.load()
     n = lib.attn_decode_fused_workspace_bytes(2, 8, 2, 32 * 16, 128)
     assert n > 0 and pfused(wsb=n - 1) == -13
+
+
+def fused8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.01, vs=2.0, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30, B=1, Hq=8, Hkv=2,
+             M=512, d=128, scale=0.088, dtype=1, stream=None)
+    a.update(kw)
+    return _lib.load().attn_decode_fp8kv_fused(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["lse"], a["ws"],
+                                               a["wsb"], a["B"], a["Hq"], a["Hkv"], a["M"], a["d"], a["scale"],
+                                               a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(o=None), -1), (dict(M=0), -2), (dict(d=48), -3), (dict(d=256), -3),
+    (dict(dtype=5), -4), (dict(Hq=6, Hkv=4), -5), (dict(ks=-1.0), -11), (dict(vs=float("inf")), -11),
+    (dict(scale=float("nan")), -11), (dict(B=70000, Hq=1, Hkv=1), -9), (dict(v=FAKE + 8), -10),
+    (dict(o=FAKE + 8), -10), (dict(lse=FAKE + 1), -10),
+    (dict(ws=None), -13), (dict(ws=FAKE + 8), -13), (dict(wsb=100), -13),
+])
+def test_fp8kv_decode_fused_rejects(kw, code):
+    assert fused8(**kw) == code
+
+
+def pfused8(**kw):
+    """attn_decode_paged_fp8kv_fused with a page table whose pointers are fake."""
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=0.01, vs=0.02, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30, B=2, Hq=8, Hkv=2,
+             d=128, scale=0.088, dtype=1, stream=None, bt=FAKE, sl=FAKE, nb=64, bs=16, mb=32, ps=16 * 2 * 128,
+             ts=2 * 128, hs=128)
+    a.update(kw)
+    pk = _lib.PagedKv(a["bt"], a["sl"], a["nb"], a["bs"], a["mb"], a["ps"], a["ts"], a["hs"])
+    return _lib.load().attn_decode_paged_fp8kv_fused(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], ctypes.byref(pk),
+                                                     a["o"], a["lse"], a["ws"], a["wsb"], a["B"], a["Hq"], a["Hkv"],
+                                                     a["d"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), -1), (dict(o=None), -1), (dict(bt=None), -1), (dict(mb=0), -2), (dict(d=80), -3),
+    (dict(d=256), -3), (dict(dtype=2), -4), (dict(ks=-0.5), -11), (dict(vs=float("nan")), -11),
+    (dict(hs=8), -12), (dict(ts=24), -12), (dict(bs=8), -12), (dict(vc=FAKE + 8), -10), (dict(o=FAKE + 8), -10),
+    (dict(ws=None), -13), (dict(ws=FAKE + 8), -13), (dict(wsb=100), -13),
+])
+def test_paged_fp8kv_decode_fused_rejects(kw, code):
+    assert pfused8(**kw) == code
 
 
 def noalloc(**kw):

@@ -84,6 +84,23 @@ def test_decode_fp8kv_rejects_mismatch():
         attn.attn_decode_fp8kv_splitkv(q, k8, k8, 1.0, 1.0)
 
 
+def test_decode_fp8kv_fused_rejects_mismatch():
+    q = t(1, 8, 64)
+    k8 = t(1, 2, 300, 64, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        attn.attn_decode_fp8kv_fused(q, t(1, 2, 300, 64), k8, 1.0, 1.0)
+    with pytest.raises(ValueError, match="v has shape"):
+        attn.attn_decode_fp8kv_fused(q, k8, t(1, 2, 301, 64, dtype=torch.uint8), 1.0, 1.0)
+    with pytest.raises(ValueError, match="o has dtype"):
+        attn.attn_decode_fp8kv_fused(q, k8, k8, 1.0, 1.0, o=t(1, 8, 64, dtype=BF16))
+    with pytest.raises(ValueError, match="lse has shape"):
+        attn.attn_decode_fp8kv_fused(q, k8, k8, 1.0, 1.0, lse=t(1, 4, dtype=F32))
+    with pytest.raises(ValueError, match="workspace holds"):
+        attn.attn_decode_fp8kv_fused(q, k8, k8, 1.0, 1.0, workspace=t(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        attn.attn_decode_fp8kv_fused(q, k8, k8, 1.0, 1.0)
+
+
 # ---- paged ------------------------------------------------------------------
 
 def paged_args(**kw):
@@ -119,6 +136,17 @@ def test_paged_rejects_mismatch(kw, msg):
 def test_paged_consistent_cpu_tensors_stop_at_device():
     with pytest.raises(ValueError, match="must be a GPU tensor"):
         call_paged(paged_args())
+
+
+def test_paged_fused_rejects_mismatch():
+    a = paged_args(kc=t(10, 16, 2, 64, dtype=torch.uint8), vc=t(10, 16, 2, 64, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="need k_scale"):
+        attn.attn_decode_paged_fused(a["q"], a["kc"], a["vc"], a["table"], a["lens"])
+    with pytest.raises(ValueError, match="o has shape"):
+        attn.attn_decode_paged_fused(a["q"], a["kc"], a["vc"], a["table"], a["lens"], o=t(2, 8, 32),
+                                     k_scale=1.0, v_scale=1.0)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        attn.attn_decode_paged_fused(a["q"], a["kc"], a["vc"], a["table"], a["lens"], k_scale=1.0, v_scale=1.0)
 
 
 # ---- lse_merge ----------------------------------------------------------------

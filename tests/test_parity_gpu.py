@@ -727,6 +727,110 @@ def test_decode_fp8kv(case):
     assert errs["lse"] <= TOL_LSE and errs["lse_part"] <= TOL_LSE, errs
 
 
+# the FP8-KV decode in one launch (partials of 128-key chunk runs and their
+# merge fused): the oracle is the two-step decode of the decoded values at
+# chunk 128
+FP8_FUSED_CASES = [
+    # B, Hq, Hkv, M, d, dtype
+    (2, 8, 2, 1000, 128, "bf16"),
+    (1, 4, 4, 777, 64, "f16"),
+    (8, 32, 8, 16384, 128, "bf16"),    # grouped-query decode workload
+    (2, 8, 8, 65536, 128, "f16"),      # long decode shape
+    (1, 16, 1, 300, 32, "bf16"),
+    (3, 24, 8, 4097, 128, "f16"),      # groups of 3 heads, a one-key tail chunk
+    (64, 32, 32, 1000, 64, "f16"),     # more rows than the grid: one segment per row
+    (1, 1, 1, 1, 128, "bf16"),         # a single key
+]
+
+
+@pytest.mark.parametrize("case", FP8_FUSED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_fp8kv_fused(case):
+    B, Hq, Hkv, M, d, dt = case
+    say(f"case fp8 kv fused decode {case}")
+    q, kc, vc, ks, vs = fp8kv_inputs(B, Hq, Hkv, M, d, dt, seed=M + d + 1)
+    scale = float(np.float32(d ** -0.5))
+    ws = torch.zeros(attn().attn_decode_fused_workspace_bytes(B, Hq, Hkv, M, d), dtype=torch.uint8, device=DEV)
+    Or, Lr, _, _ = oracle.decode_fp8kv_ref(q, kc.numpy(), vc.numpy(), ks, vs, scale, 128)
+    outs = []
+    for rep in range(2):       # the second call reuses the workspace (its counters reset themselves)
+        o, lse = attn().attn_decode_fp8kv_fused(q.to(DEV), kc.to(DEV), vc.to(DEV), ks, vs, scale, workspace=ws)
+        torch.cuda.synchronize()
+        eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+        say(f"  call {rep}: o={eo:.3e} lse={el:.3e}")
+        assert eo <= TOL_O[dt] and el <= TOL_LSE
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.count_nonzero(ws[:256]).item() == 0, "row counters left non-zero"
+
+
+PAGED_FP8_FUSED_CASES = [
+    # B, Hq, Hkv, lens, d, dtype, block size, head-major pages
+    (3, 8, 2, (1, 200, 1000), 128, "bf16", 16, False),
+    (2, 4, 4, (777, 64), 64, "f16", 64, True),
+    (2, 16, 1, (130, 16), 32, "bf16", 32, True),
+    (2, 32, 8, (5000, 4097), 128, "f16", 256, False),
+    (4, 16, 4, (0, 1, 4096, 700), 128, "bf16", 16, False),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_FP8_FUSED_CASES, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_decode_paged_fp8kv_fused(case):
+    """Paged cache of E4M3 codes in one launch; the unowned rows hold NaN
+    codes, an empty sequence gives o = 0 and lse = -inf."""
+    B, Hq, Hkv, lens, d, dt, bs, head_major = case
+    say(f"case paged fp8 kv fused decode {case}")
+    q, kc, vc, _, _, table, sl = paged_inputs(B, Hq, Hkv, list(lens), d, dt, bs, seed=sum(lens) + 2,
+                                              head_major=head_major)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(3.0 / 448.0))
+    kc8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    view = (lambda t: t.transpose(1, 2)) if head_major else (lambda t: t)
+    scale = float(np.float32(d ** -0.5))
+    ws = torch.zeros(attn().attn_decode_fused_workspace_bytes(B, Hq, Hkv, table.shape[1] * bs, d), dtype=torch.uint8,
+                     device=DEV)
+    kdeq = oracle.e4m3_decode(view(kc8).numpy()) * ks
+    vdeq = oracle.e4m3_decode(view(vc8).numpy()) * vs
+    Or, Lr, _, _ = oracle.paged_decode_ref(q, kdeq, vdeq, table.clamp(min=0), sl, scale, 128)
+    empty = np.asarray(lens) == 0
+    for rep in range(2):
+        o, lse = attn().attn_decode_paged_fused(q.to(DEV), view(kc8.to(DEV)), view(vc8.to(DEV)), table.to(DEV),
+                                                sl.to(DEV), scale, workspace=ws, k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        Og, Lg = f64(o), f64(lse)
+        assert np.all(Og[empty] == 0.0) and np.all(Lg[empty] == -np.inf), "empty sequence"
+        eo, el = maxerr(Og[~empty], Or[~empty]), maxerr(Lg[~empty], Lr[~empty])
+        say(f"  call {rep}: o={eo:.3e} lse={el:.3e}")
+        assert eo <= TOL_O[dt] and el <= TOL_LSE
+    assert torch.count_nonzero(ws[:256]).item() == 0, "row counters left non-zero"
+
+
+def test_decode_paged_fp8kv_fused_bad_page_id():
+    """A page id out of range inside a sequence reads as keys and values of
+    zeros, as in the two-launch paged FP8 decode."""
+    B, Hq, Hkv, d, bs = 3, 8, 2, 128, 16
+    lens = [5, 200, 1000]
+    say("case paged fp8 kv fused decode, bad page id")
+    q, kc, vc, _, _, table, sl = paged_inputs(B, Hq, Hkv, lens, d, "bf16", bs, seed=79, head_major=False)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(3.0 / 448.0))
+    kc8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    num_blocks = kc.shape[0]
+    table[2, 5] = num_blocks + 11
+    scale = float(np.float32(d ** -0.5))
+    o, lse = attn().attn_decode_paged_fused(q.to(DEV), kc8.to(DEV), vc8.to(DEV), table.to(DEV), sl.to(DEV), scale,
+                                            k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kref, vref = oracle.e4m3_decode(kc8.numpy()) * ks, oracle.e4m3_decode(vc8.numpy()) * vs
+    zero = np.zeros((1,) + kref.shape[1:])
+    kref, vref = np.concatenate([kref, zero]), np.concatenate([vref, zero])
+    tref = table.clone()
+    tref[2, 5] = num_blocks
+    Or, Lr, _, _ = oracle.paged_decode_ref(q, kref, vref, tref.clamp(min=0), sl, scale, 128)
+    eo, el = maxerr(f64(o), Or), maxerr(f64(lse), Lr)
+    say(f"  o={eo:.3e} lse={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_decode_fp8kv_every_code(dt):
     """Every E4M3 code through the kernel's conversion, exactly: one key per
