@@ -321,12 +321,7 @@ def attn_decode_fused_noalloc(q, k, v, scale: float | None = None, o=None, lse=N
     _dtype(v, "v", q.dtype)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _contig(t, n)
-    if o is not None:
-        _shape(o, "o", (B, Hq, d))
-        _dtype(o, "o", q.dtype)
-        _contig(o, "o")
-    if lse is not None:
-        _check_f32(lse, "lse", (B, Hq))
+    _fused_out_checks(q, o, lse, None, 0)
     _devices((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"))
     if scale is None:
         scale = d ** -0.5
