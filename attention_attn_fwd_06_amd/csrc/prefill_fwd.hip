@@ -560,8 +560,9 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
   // as an explicit software pipeline of kN slots, one MFMA each: the 2 kDT QK
   // MFMAs of S(j+1) = K(j+1) Q^T, then the 4 kDB PV MFMAs of O^T += V(j)^T P(j)
   // (k-step ks = 2 kb + st, d block db).  Slot i issues MFMA i, the LDS reads
-  // of MFMA i + kL, a share of the exp/pack work of tile j (each P k-step is
-  // complete before its first PV MFMA), in its first odd slots one of the
+  // of MFMA i + kL, a share of the exp/pack work of tile j (the first few
+  // exponentials come before slot 0; each P k-step is complete before its
+  // first PV MFMA), in its first odd slots one of the
   // step's tile fetches, and in the last slots the row max of S(j+1) (whose
   // MFMAs have finished by then), which the next step uses.  The slots are
   // separated by scheduling fences, so the order is the one written here.
@@ -636,6 +637,11 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kL; ++i) reads(i);
+    // the first exponentials go before the first MFMA, which waits for its K
+    // operand from LDS right after the step's barrier
+    constexpr int kPre = 4;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) exp_elem(k);
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -648,10 +654,10 @@ void prefill_fwd_kernel(const void* __restrict__ q, const void* __restrict__ k,
       }
       reads(i + kL);
       if ((i & 1) && (i >> 1) < kNF) fetch(i >> 1);
-      // elements k with floor(k * kExpEnd / 32) == i
+      // the other elements k: floor((k - kPre) * kExpEnd / (32 - kPre)) == i
 #pragma unroll
-      for (int k = 0; k < 32; ++k)
-        if (k * kExpEnd / 32 == i) exp_elem(k);
+      for (int k = kPre; k < 32; ++k)
+        if ((k - kPre) * kExpEnd / (32 - kPre) == i) exp_elem(k);
       if (kExact && i >= kExpEnd) {
         // row max of S(j+1), spread over the slots after the exp work
         constexpr int kMaxSlots = kN - kExpEnd;
