@@ -1,8 +1,10 @@
 """Seeded random shapes through the GPU path against the CPU oracle (needs an
 MI355X): prefill (MHA and GQA, causal and not, every head dim and dtype, N
 and M from 1 to a few hundred), the split-KV decode with its merge at
-several chunk sizes, the decode in one launch, and the FP8-KV decode in one
-launch.
+several chunk sizes, the decode in one launch, the FP8-KV decode in one
+launch, and the paged decode (16-bit and FP8 caches, both page layouts,
+random page sizes and sequence lengths including empty ones) in two
+launches and in one.
 
 The shapes come from a fixed seed, so every run tests the same cases.  V is
 the workloads' N(0, 1) draw times 0.25 (exact in fp16 and bf16): rows with
@@ -18,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+from tests.test_parity_gpu import paged_inputs
 from workloads import decode_inputs, prefill_inputs
 
 pytestmark = [pytest.mark.gpu,
@@ -64,9 +67,31 @@ def _decode_shapes(n, seed, dims):
     return out
 
 
+def _paged_shapes(n, seed, dims):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 5))
+        if B * Hkv * group > 64:
+            continue
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 4000, size=B)]
+        if max(lens) == 0:
+            lens[0] = int(rng.integers(1, 4000))
+        d = int(rng.choice(dims))
+        dt = str(rng.choice(["f16", "bf16"]))
+        bs = int(rng.choice([16, 32, 48, 64, 128, 256]))
+        chunk = int(rng.choice([128, 256, 512, 1024]))
+        out.append((B, Hkv * group, Hkv, tuple(lens), d, dt, bs, chunk, bool(rng.integers(0, 2))))
+    return out
+
+
 PREFILL_RANDOM = _prefill_shapes(24, 20261202)
 DECODE_RANDOM = _decode_shapes(16, 20261203, [32, 64, 128, 256])
 FP8_DECODE_RANDOM = _decode_shapes(10, 20261204, [32, 64, 128])
+PAGED_RANDOM = _paged_shapes(10, 20261205, [32, 64, 128, 256])
+PAGED_FP8_RANDOM = _paged_shapes(6, 20261206, [32, 64, 128])
 
 
 def attn():
@@ -143,3 +168,69 @@ def test_fp8kv_decode_random(shape):
     print("  " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()), flush=True)
     assert max(errs["o"], errs["o_fused"]) <= TOL_O[dt], errs
     assert max(errs["lse"], errs["lse_fused"]) <= TOL_LSE, errs
+
+
+def _paged_case(case, seed):
+    B, Hq, Hkv, lens, d, dt, bs, chunk, head_major = case
+    q, kc, vc, kv_k, kv_v, table, sl = paged_inputs(B, Hq, Hkv, list(lens), d, dt, bs, seed=seed,
+                                                    head_major=head_major)
+    vc.mul_(V_SCALE)  # (kv_v is a view of vc; the unowned rows stay NaN)
+    return q, kc, vc, kv_k, kv_v, table, sl
+
+
+def _check_paged(case, o, lse, op, lp, of, lf, Or, Lr, OPr, LPr, Orf, Lrf):
+    dt, lens = case[5], case[3]
+    empty = np.asarray(lens) == 0
+    OPg, LPg = f64(op), f64(lp)
+    full = np.isfinite(LPr)
+    assert np.array_equal(np.isfinite(LPg), full), "empty chunks must be exactly the chunks past each end"
+    Og, Lg, Ofg, Lfg = f64(o), f64(lse), f64(of), f64(lf)
+    assert np.all(Ofg[empty] == 0.0) and np.all(Lfg[empty] == -np.inf), "empty sequence (one launch)"
+    ne = ~empty
+    errs = dict(o=maxerr(Og[ne], Or[ne]), lse=maxerr(Lg[ne], Lr[ne]), o_part=maxerr(OPg[full], OPr[full]),
+                lse_part=maxerr(LPg[full], LPr[full]), o_fused=maxerr(Ofg[ne], Orf[ne]),
+                lse_fused=maxerr(Lfg[ne], Lrf[ne]))
+    print("  " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()), flush=True)
+    assert max(errs["o"], errs["o_part"], errs["o_fused"]) <= TOL_O[dt], errs
+    assert max(errs["lse"], errs["lse_part"], errs["lse_fused"]) <= TOL_LSE, errs
+
+
+@pytest.mark.parametrize("case", PAGED_RANDOM, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_paged_decode_random(case):
+    """16-bit paged cache: the two-launch decode at the case's chunk size
+    (partials compared too) and the one-launch decode (chunks of 128)."""
+    B, Hq, Hkv, lens, d, dt, bs, chunk, head_major = case
+    print(f"case random paged decode {case}", flush=True)
+    q, kc, vc, kv_k, kv_v, table, sl = _paged_case(case, seed=sum(lens) + bs)
+    view = (lambda t: t.transpose(1, 2)) if head_major else (lambda t: t)
+    scale = float(np.float32(d ** -0.5))
+    kd, vd, td, sd = view(kc.to(DEV)), view(vc.to(DEV)), table.to(DEV), sl.to(DEV)
+    o, lse, op, lp = attn().attn_decode_paged(q.to(DEV), kd, vd, td, sd, chunk, scale)
+    of, lf = attn().attn_decode_paged_fused(q.to(DEV), kd, vd, td, sd, scale)
+    torch.cuda.synchronize()
+    Or, Lr, OPr, LPr = oracle.paged_decode_ref(q, kv_k, kv_v, table.clamp(min=0), sl, scale, chunk)
+    Orf, Lrf, _, _ = oracle.paged_decode_ref(q, kv_k, kv_v, table.clamp(min=0), sl, scale, 128)
+    _check_paged(case, o, lse, op, lp, of, lf, Or, Lr, OPr, LPr, Orf, Lrf)
+
+
+@pytest.mark.parametrize("case", PAGED_FP8_RANDOM, ids=lambda c: "x".join(map(str, c)).replace(" ", ""))
+def test_paged_fp8kv_decode_random(case):
+    """Paged cache of E4M3 codes (per-tensor scales 4/448 and 1/448, the
+    unowned rows NaN codes): the two-launch and the one-launch decode."""
+    B, Hq, Hkv, lens, d, dt, bs, chunk, head_major = case
+    print(f"case random paged fp8 kv decode {case}", flush=True)
+    q, kc, vc, _, _, table, sl = _paged_case(case, seed=sum(lens) + bs + 1)
+    ks, vs = float(np.float32(4.0 / 448.0)), float(np.float32(1.0 / 448.0))
+    kc8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    view = (lambda t: t.transpose(1, 2)) if head_major else (lambda t: t)
+    scale = float(np.float32(d ** -0.5))
+    kd, vd, td, sd = view(kc8.to(DEV)), view(vc8.to(DEV)), table.to(DEV), sl.to(DEV)
+    o, lse, op, lp = attn().attn_decode_paged(q.to(DEV), kd, vd, td, sd, chunk, scale, k_scale=ks, v_scale=vs)
+    of, lf = attn().attn_decode_paged_fused(q.to(DEV), kd, vd, td, sd, scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kdeq = oracle.e4m3_decode(view(kc8).numpy()) * ks
+    vdeq = oracle.e4m3_decode(view(vc8).numpy()) * vs
+    Or, Lr, OPr, LPr = oracle.paged_decode_ref(q, kdeq, vdeq, table.clamp(min=0), sl, scale, chunk)
+    Orf, Lrf, _, _ = oracle.paged_decode_ref(q, kdeq, vdeq, table.clamp(min=0), sl, scale, 128)
+    _check_paged(case, o, lse, op, lp, of, lf, Or, Lr, OPr, LPr, Orf, Lrf)
