@@ -261,12 +261,30 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // Paged KV cache (device pointers and element strides; K and V share them).
 // Page p holds block_size consecutive keys of every KV head: key row r of kv
 // head h starts at p*page_stride + r*token_stride + h*head_stride.
+// A key's page (key / block_size) uses a multiplier and a shift worked out on
+// the host (round-up method of Granlund and Montgomery, exact for keys below
+// 2^31): three instructions instead of a division sequence per lane.
 struct PagedKv {
   const int32_t* block_table;  // [B, max_blocks]
   const int32_t* seq_lens;     // [B]
   int64_t page_stride, token_stride, head_stride;
   int num_blocks, block_size, max_blocks;
+  uint32_t bs_mul, bs_shift;   // key / block_size == (mulhi(key, bs_mul) + key) >> bs_shift
+  __device__ int page_of(int key) const {
+    return (int)((__umulhi((uint32_t)key, bs_mul) + (uint32_t)key) >> bs_shift);
+  }
+  __device__ int row_in_page(int key) const { return key - page_of(key) * block_size; }
 };
+
+static PagedKv make_paged_kv(const int32_t* block_table, const int32_t* seq_lens, int64_t page_stride,
+                             int64_t token_stride, int64_t head_stride, int num_blocks, int block_size,
+                             int max_blocks) {
+  uint32_t l = 0;
+  while ((1u << l) < (uint32_t)block_size) ++l;
+  const uint64_t mul = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - (uint32_t)block_size)) / (uint32_t)block_size + 1;
+  return PagedKv{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks,
+                 (uint32_t)mul, l};
+}
 // Fused decode (split-KV with the merge inside the chunk kernel): an item is
 // (row, segment), a row being (batch, kv head, head slice) and a segment a run
 // of consecutive 128-key chunks of that row.  Each item leaves its
@@ -409,7 +427,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
   int pgv = 0;  // lane i < kFetch: page id of fetch instruction i (current, then prefetched)
   auto load_pages = [&](int bb, int kk, int& pv) {
     const int i = min(lane, kFetch - 1);
-    const int e = min((kk + kRowsPerInst * i + wave_u * kWaveRows) / pk.block_size, pk.max_blocks - 1);
+    const int e = min(pk.page_of(kk + kRowsPerInst * i + wave_u * kWaveRows), pk.max_blocks - 1);
     pv = pk.block_table[(int64_t)bb * pk.max_blocks + e];
   };
 
@@ -441,7 +459,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int p = 0; p < kPieces8; ++p) {
       const int key = kk + piece_row(p * kDecThreads + tid);
-      const int e = min(key / pk.block_size, pk.max_blocks - 1);
+      const int e = min(pk.page_of(key), pk.max_blocks - 1);
       pg8[p] = pk.block_table[(int64_t)bb * pk.max_blocks + e];
     }
   };
@@ -457,7 +475,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         const int u = p * kDecThreads + tid, key = kk + piece_row(u);
         const bool ok = pg8[p] >= 0 && pg8[p] < pk.num_blocks;
         const int64_t off = ok ? (int64_t)pg8[p] * pk.page_stride + (int64_t)kvhh * pk.head_stride +
-                                     (int64_t)(key % pk.block_size) * pk.token_stride + 16 * (u % kPR8)
+                                     (int64_t)pk.row_in_page(key) * pk.token_stride + 16 * (u % kPR8)
                                : 0;
         kv8_ok |= (uint32_t)ok << p;
         kr8[p] = load_stream8(k8 + off);
@@ -756,7 +774,7 @@ void decode_gqa_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
           if (page < 0 || page >= pk.num_blocks) nv = 0;
           if (nv <= 0) page = 0;
           const int64_t off = (int64_t)page * pk.page_stride + (int64_t)kvh * pk.head_stride +
-                              (int64_t)(rg % pk.block_size) * pk.token_stride;
+                              (int64_t)pk.row_in_page(rg) * pk.token_stride;
           const uint32_t vo = (kOddRows && (i & 1)) ? voff_paged_odd : voff_paged;
           dma16<true>(make_desc_rows(k + off, pk.token_stride, max(nv, 0), D),
                       k_lds + (uint32_t)(i * kWaves + wave) * 1024u, vo);
@@ -1157,7 +1175,8 @@ hipError_t decode_paged_fused_dispatch(const void* q, const void* k_cache, const
                                        float v_scale, hipStream_t stream) {
   const int M = max_blocks * block_size;
   const float sl2 = scale * (fp8 ? k_scale : 1.f) * kLog2e;  // FP8: the scores carry k_scale
-  const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
+  const PagedKv pk = make_paged_kv(block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks,
+                                   block_size, max_blocks);
 #define ATTN_PFUSED_CASE(DD, BB, F8) \
   if (d == DD && bf16 == BB && fp8 == F8) \
     return launch_fused<DD, BB, true, F8>(q, k_cache, v_cache, o, lse, ws, ws_bytes, B, Hq, Hkv, M, sl2, \
@@ -1216,7 +1235,8 @@ hipError_t decode_paged_dispatch(const void* q, const void* k_cache, const void*
   int g = std::min(group, kGqaCols);
   while (group % g != 0) --g;
   const int n_items = B * (Hq / g) * C;
-  const PagedKv pk{block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks, block_size, max_blocks};
+  const PagedKv pk = make_paged_kv(block_table, seq_lens, page_stride, token_stride, head_stride, num_blocks,
+                                   block_size, max_blocks);
 #define ATTN_PAGED_CASE(DD, BB, F8)                                                                    \
   if (d == DD && bf16 == BB && fp8 == F8) {                                                            \
     const int grid = std::min(n_items, resident_grid<decode_gqa_mfma_kernel<DD, BB, true, F8>>(kDecThreads)); \
