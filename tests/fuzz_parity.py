@@ -3,9 +3,10 @@
     python tests/fuzz_parity.py SEED SECONDS
 
 draws prefill (MHA and GQA with groups up to 8, causal with N <= M or not,
-head dims 32-256, fp16 and bf16, N and M up to a few hundred), decode (chunks
-of 128-2048 keys, the two-launch and the one-launch paths) and paged decode
-(page sizes 16-256, both cache layouts) shapes from the seed, compares each
+head dims 32-256, fp16 and bf16, N and M up to a few hundred), FP8 Q/K
+prefill, decode (chunks of 128-2048 keys, the two-launch and the one-launch
+paths), FP8-KV decode and paged decode (page sizes 16-256, both cache
+layouts) shapes from the seed, compares each
 with the oracle at the fixed tolerances (V scaled by 0.25, as in
 test_parity_random.py) and exits non-zero if any case misses them.  Not
 collected by pytest (a time-bounded stress run, not a fixed test).
@@ -15,7 +16,7 @@ import pathlib
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 sys.path.insert(0, str(ROOT)); sys.path.insert(0, str(ROOT / 'tests'))
 import numpy as np, torch, oracle
-from workloads import prefill_inputs, decode_inputs
+from workloads import prefill_inputs, decode_inputs, prefill_fp8qk_inputs
 from tests.test_parity_gpu import paged_inputs
 import attention_attn_fwd_06_amd as A
 DEV = "cuda"; TOL_O = {"f16": 2e-3, "bf16": 8e-3}; TOL_L = 1e-3
@@ -25,7 +26,7 @@ rng = np.random.default_rng(int(sys.argv[1]) if len(sys.argv) > 1 else 7)
 budget = float(sys.argv[2]) if len(sys.argv) > 2 else 240
 t0 = time.time(); n = 0; bad = []
 while time.time() - t0 < budget:
-    kind = rng.choice(["prefill", "prefill", "decode", "paged"])
+    kind = rng.choice(["prefill", "prefill", "decode", "paged", "fp8qk", "fp8kv"])
     dt = str(rng.choice(["f16", "bf16"])); d = int(rng.choice([32, 64, 128, 256]))
     try:
         if kind == "prefill":
@@ -45,6 +46,31 @@ while time.time() - t0 < budget:
             o, l, _, _ = A.attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), chunk, sc)
             of, lf = A.attn_decode_fused(q.to(DEV), k.to(DEV), v.to(DEV), sc); torch.cuda.synchronize()
             Or, Lr, _, _ = oracle.decode_ref(q, k, v, sc, chunk)
+            eo = max(me(f64(o), Or), me(f64(of), Or)); el = max(me(f64(l), Lr), me(f64(lf), Lr))
+        elif kind == "fp8qk":
+            d = int(rng.choice([64, 128]))
+            Hkv = int(rng.choice([1, 2, 4])); g = int(rng.choice([1, 2, 4])); B = int(rng.integers(1, 3))
+            causal = bool(rng.integers(0, 2)); N = int(rng.integers(1, 300)); M = int(rng.integers(N if causal else 1, 520))
+            case = (kind, B, N, M, Hkv * g, Hkv, d, dt, causal); print(case, flush=True)
+            q8, k8, v, qs, ks = prefill_fp8qk_inputs(B, Hkv * g, Hkv, N, M, d, dt, seed=n); v = v * 0.25
+            sc = float(np.float32(d ** -0.5))
+            o, l = A.attn_fwd_fp8qk(q8.to(DEV), k8.to(DEV), v.to(DEV), qs, ks, causal=causal, scale=sc)
+            torch.cuda.synchronize()
+            Or, Lr = oracle.attn_fp8qk_ref(q8.numpy(), k8.numpy(), v, qs, ks, sc, causal)
+            eo, el = me(f64(o), Or), me(f64(l), Lr)
+        elif kind == "fp8kv":
+            d = int(rng.choice([32, 64, 128]))
+            Hkv = int(rng.choice([1, 2, 4, 8])); g = int(rng.choice([1, 2, 4, 8])); B = int(rng.integers(1, 3))
+            M = int(rng.integers(1, 5000)); chunk = int(rng.choice([128, 256, 512, 1024]))
+            case = (kind, B, Hkv * g, Hkv, M, d, dt, chunk); print(case, flush=True)
+            q, k, v = decode_inputs(B, Hkv * g, Hkv, M, d, dt, seed=n); v = v * 0.25
+            ks = float(np.float32(float(k.float().abs().max()) / 448.0)); vs = float(np.float32(float(v.float().abs().max()) / 448.0))
+            kc = (k.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+            vc = (v.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+            sc = float(np.float32(d ** -0.5))
+            o, l, _, _ = A.attn_decode_fp8kv(q.to(DEV), kc.to(DEV), vc.to(DEV), ks, vs, chunk, sc)
+            of, lf = A.attn_decode_fp8kv_fused(q.to(DEV), kc.to(DEV), vc.to(DEV), ks, vs, sc); torch.cuda.synchronize()
+            Or, Lr, _, _ = oracle.decode_fp8kv_ref(q, kc.numpy(), vc.numpy(), ks, vs, sc, chunk)
             eo = max(me(f64(o), Or), me(f64(of), Or)); el = max(me(f64(l), Lr), me(f64(lf), Lr))
         else:
             Hkv = int(rng.choice([1, 2, 4])); g = int(rng.choice([1, 2, 4, 8])); B = int(rng.integers(1, 4))
